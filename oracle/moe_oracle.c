@@ -1,0 +1,491 @@
+/*
+ * moe_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded CPU evaluation of the routed-expert MoE layer
+ * (top-k softmax routing, token->expert dispatch, 1x32 MX activation
+ * quantisation, GEMM1 against MXFP4 gate/up weights, SwiGLU, MX requantisation,
+ * GEMM2 against MXFP4 down weights, FP32 weighted top-k combine, BF16 output).
+ *
+ * Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this library.  The GPU library never links it, and the
+ * two share no source, header, table or helper.
+ *
+ * Sources of each step (the pages are pull-request descriptions):
+ *   - "add A4W4 and FP8 P2P transport support to MegaMoE" (ROCm/FlyDSL #972),
+ *     Technical Details: BF16 activations quantised to MXFP4 (or MXFP8) with
+ *     per-1x32 E8M0 scales before dispatch; GEMM1 consumes them; the SwiGLU
+ *     output is re-quantised ("emit FP4 A2 activations/scales"); GEMM2 runs on
+ *     it; weighted GEMM2 rows are combined with FP32 accumulation of the
+ *     top-k contributions.
+ *   - "feat(moe): FlyDSL MegaMoE fused EP-MoE integration" (ROCm/ATOM #1666),
+ *     summary bullets: interleaved gate/up contract (gate and up must be
+ *     paired for SwiGLU), experts stored explicitly.
+ *   - "[HIP] gfx950 A8W4 fused_moe configs for DSv4.1 TP-sharded experts"
+ *     (ROCm/aiter #6125), Motivation and Changes: A8W4 = MXFP8 activations on
+ *     MXFP4 experts; the top-k softmax routing kernel.
+ *   - The MX element/scale encodings follow the OCP Microscaling (MX) v1.0
+ *     convention named by the pages' "per-1x32 E8M0 scales": shared scale
+ *     exponent = floor(log2(amax)) - emax of the element type, elements
+ *     rounded to nearest-even on the element grid and saturated.
+ *
+ * Precision: routing weights are evaluated in double and rounded once to
+ * float.  The expert GEMMs, SwiGLU and the combine are FP32 (the pages fix
+ * FP32 accumulation of the top-k combine); an optional double-accumulation
+ * mode evaluates the same steps in double to bound the FP32 rounding error.
+ * Build with -ffp-contract=off so no FMA contraction changes the FP32 order.
+ *
+ * Parity pins: every function here is pinned by the CPU tests (codec grids
+ * and brute-force nearest search, worked examples, routing special cases,
+ * sort invariants against a library stable sort, dense brute force, token
+ * permutation invariance, the identity-expert construction, E=1/k=1
+ * reduction to a dense quantised SwiGLU MLP, the unquantised-FP32 error
+ * band).  GEMM/SwiGLU values at the large shapes are covered only by those
+ * invariants (parity otherwise unpinned at those sizes).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* Element formats                                                     */
+/* ------------------------------------------------------------------ */
+
+#define FMT_E4M3 0 /* MXFP8, OCP E4M3FN: bias 7, 3 mantissa bits, max 448 */
+#define FMT_E2M1 1 /* MXFP4, E2M1: bias 1, 1 mantissa bit, max 6          */
+
+typedef struct {
+    int mbits;   /* explicit mantissa bits            */
+    int emin;    /* exponent of the smallest normal   */
+    int emax;    /* exponent of the largest normal    */
+    int bias;    /* exponent bias of the code         */
+    double maxv; /* largest finite magnitude          */
+    int nbits;   /* code width including the sign bit */
+} fmt_desc;
+
+static fmt_desc describe(int fmt)
+{
+    fmt_desc d;
+    if (fmt == FMT_E4M3) {
+        d.mbits = 3; d.emin = -6; d.emax = 8; d.bias = 7; d.maxv = 448.0; d.nbits = 8;
+    } else {
+        d.mbits = 1; d.emin = 0; d.emax = 2; d.bias = 1; d.maxv = 6.0; d.nbits = 4;
+    }
+    return d;
+}
+
+/* Magnitude of a code (sign bit excluded), straight from its fields. */
+static double code_magnitude(int fmt, unsigned mag)
+{
+    fmt_desc d = describe(fmt);
+    unsigned efield = mag >> d.mbits;
+    unsigned mfield = mag & ((1u << d.mbits) - 1u);
+    if (efield == 0)
+        return ldexp((double)mfield, d.emin - d.mbits); /* subnormal */
+    return ldexp(1.0 + ldexp((double)mfield, -d.mbits), (int)efield - d.bias);
+}
+
+/* Round a non-negative double to the element grid: nearest, ties to the
+ * even code (nearbyint rounds half to even in the default FE_TONEAREST
+ * mode), values past the largest finite magnitude saturate. */
+static double round_to_grid(int fmt, double a)
+{
+    fmt_desc d = describe(fmt);
+    if (a >= d.maxv)
+        return d.maxv;
+    if (a == 0.0)
+        return 0.0;
+    int e2;
+    frexp(a, &e2);          /* a = f * 2^e2, f in [0.5, 1)  */
+    int ex = e2 - 1;        /* floor(log2(a))               */
+    if (ex < d.emin)
+        ex = d.emin;        /* subnormal spacing below emin */
+    double ulp = ldexp(1.0, ex - d.mbits);
+    double r = nearbyint(a / ulp) * ulp;
+    if (r > d.maxv)
+        r = d.maxv;
+    return r;
+}
+
+/* Code (magnitude bits) of an exactly representable grid value. */
+static unsigned encode_grid(int fmt, double r)
+{
+    fmt_desc d = describe(fmt);
+    if (r == 0.0)
+        return 0u;
+    int e2;
+    frexp(r, &e2);
+    int ex = e2 - 1;
+    if (ex < d.emin) /* subnormal: exponent field 0 */
+        return (unsigned)(r / ldexp(1.0, d.emin - d.mbits));
+    unsigned mfield = (unsigned)((r / ldexp(1.0, ex) - 1.0) * (double)(1 << d.mbits));
+    return ((unsigned)(ex + d.bias) << d.mbits) | mfield;
+}
+
+/* Shared block exponent X of one 1x32 block: floor(log2(amax)) - emax of the
+ * element type, clamped to the E8M0 range [-127, 127]; an all-zero block
+ * takes the smallest scale (byte 0). */
+static int block_exponent(int fmt, const double *v, int n)
+{
+    fmt_desc d = describe(fmt);
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i)
+        if (fabs(v[i]) > amax)
+            amax = fabs(v[i]);
+    if (amax == 0.0)
+        return -127;
+    int e2;
+    frexp(amax, &e2);
+    int X = (e2 - 1) - d.emax;
+    if (X < -127) X = -127;
+    if (X > 127) X = 127;
+    return X;
+}
+
+/* Quantise rows of K doubles (K % 32 == 0) into MX codes and E8M0 bytes.
+ * E4M3 codes take one byte each; E2M1 codes are packed two per byte with
+ * the even element in the low nibble.  Scales are row-major [rows][K/32]. */
+static void mx_quantize_rows_d(const double *v, long rows, int K, int fmt,
+                               uint8_t *codes, uint8_t *scales)
+{
+    fmt_desc d = describe(fmt);
+    long row_code_bytes = (fmt == FMT_E4M3) ? K : K / 2;
+    for (long r = 0; r < rows; ++r) {
+        const double *row = v + r * (long)K;
+        uint8_t *crow = codes + r * row_code_bytes;
+        if (fmt == FMT_E2M1)
+            memset(crow, 0, (size_t)row_code_bytes);
+        for (int b = 0; b < K / 32; ++b) {
+            int X = block_exponent(fmt, row + 32 * b, 32);
+            scales[r * (long)(K / 32) + b] = (uint8_t)(X + 127);
+            for (int i = 0; i < 32; ++i) {
+                int k = 32 * b + i;
+                double x = row[k];
+                double q = ldexp(fabs(x), -X); /* exact scaling by 2^-X */
+                unsigned mag = encode_grid(fmt, round_to_grid(fmt, q));
+                unsigned sign = signbit(x) ? (1u << (d.nbits - 1)) : 0u;
+                unsigned code = sign | mag;
+                if (fmt == FMT_E4M3)
+                    crow[k] = (uint8_t)code;
+                else
+                    crow[k / 2] |= (uint8_t)(code << ((k & 1) ? 4 : 0));
+            }
+        }
+    }
+}
+
+static double decode_code(int fmt, unsigned code)
+{
+    fmt_desc d = describe(fmt);
+    unsigned sign = code >> (d.nbits - 1);
+    double m = code_magnitude(fmt, code & ((1u << (d.nbits - 1)) - 1u));
+    return sign ? -m : m;
+}
+
+/* Decoded magnitudes of every code, filled once from decode_code(). */
+static double code_table[2][256];
+static int code_table_ready;
+
+static void init_tables(void)
+{
+    if (code_table_ready)
+        return;
+    for (unsigned c = 0; c < 256; ++c)
+        code_table[FMT_E4M3][c] = decode_code(FMT_E4M3, c);
+    for (unsigned c = 0; c < 16; ++c)
+        code_table[FMT_E2M1][c] = decode_code(FMT_E2M1, c);
+    code_table_ready = 1;
+}
+
+/* Dequantise one row of K MX elements: value(code) * 2^(scale - 127). */
+static void dequant_row(const uint8_t *crow, const uint8_t *srow, int K, int fmt, double *out)
+{
+    for (int b = 0; b < K / 32; ++b) {
+        double s = ldexp(1.0, (int)srow[b] - 127);
+        for (int i = 0; i < 32; ++i) {
+            int k = 32 * b + i;
+            unsigned code = (fmt == FMT_E4M3) ? crow[k] : ((crow[k / 2] >> ((k & 1) ? 4 : 0)) & 0xFu);
+            out[k] = code_table[fmt][code] * s;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* BF16                                                                */
+/* ------------------------------------------------------------------ */
+
+static float bf16_to_float(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round a finite float to the nearest bf16, ties to even. */
+static uint16_t float_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t lower = u & 0xFFFFu;
+    uint32_t upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1u;
+    return (uint16_t)upper;
+}
+
+/* ------------------------------------------------------------------ */
+/* Public helpers                                                      */
+/* ------------------------------------------------------------------ */
+
+/* fmt: 0 = E4M3, 1 = E2M1. */
+void oracle_mx_quantize(const float *v, long rows, int K, int fmt,
+                        uint8_t *codes, uint8_t *scales)
+{
+    double *tmp = (double *)malloc(sizeof(double) * (size_t)K);
+    long cb = (fmt == FMT_E4M3) ? K : K / 2;
+    for (long r = 0; r < rows; ++r) {
+        for (int k = 0; k < K; ++k)
+            tmp[k] = (double)v[r * (long)K + k];
+        mx_quantize_rows_d(tmp, 1, K, fmt, codes + r * cb, scales + r * (long)(K / 32));
+    }
+    free(tmp);
+}
+
+void oracle_mx_quantize_bf16(const uint16_t *x, long rows, int K, int fmt,
+                             uint8_t *codes, uint8_t *scales)
+{
+    double *tmp = (double *)malloc(sizeof(double) * (size_t)K);
+    long cb = (fmt == FMT_E4M3) ? K : K / 2;
+    for (long r = 0; r < rows; ++r) {
+        for (int k = 0; k < K; ++k)
+            tmp[k] = (double)bf16_to_float(x[r * (long)K + k]);
+        mx_quantize_rows_d(tmp, 1, K, fmt, codes + r * cb, scales + r * (long)(K / 32));
+    }
+    free(tmp);
+}
+
+void oracle_mx_dequantize(const uint8_t *codes, const uint8_t *scales, long rows, int K,
+                          int fmt, float *out)
+{
+    long cb = (fmt == FMT_E4M3) ? K : K / 2;
+    double *tmp = (double *)malloc(sizeof(double) * (size_t)K);
+    init_tables();
+    for (long r = 0; r < rows; ++r) {
+        dequant_row(codes + r * cb, scales + r * (long)(K / 32), K, fmt, tmp);
+        for (int k = 0; k < K; ++k)
+            out[r * (long)K + k] = (float)tmp[k];
+    }
+    free(tmp);
+}
+
+double oracle_code_value(int fmt, unsigned code) { return decode_code(fmt, code); }
+
+void oracle_float_to_bf16(const float *f, long n, uint16_t *out)
+{
+    for (long i = 0; i < n; ++i)
+        out[i] = float_to_bf16(f[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Routing: softmax over the E router logits, keep the top-k, renormalise */
+/* (aiter #6125 Changes: the top-k softmax kernel; the layer definition: */
+/* softmax then top-k with weights renormalised to sum to one).          */
+/* ------------------------------------------------------------------ */
+
+/* Selection is on the logits (softmax is monotone), larger first; equal
+ * logits keep the lower expert index first.  Slot j holds the j-th pick. */
+void oracle_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w)
+{
+    char *taken = (char *)malloc((size_t)E);
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    for (int t = 0; t < T; ++t) {
+        const float *l = logits + (long)t * E;
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < top_k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e; /* strict: ties keep lower index */
+            }
+            taken[best] = 1;
+            ids[(long)t * top_k + j] = best;
+        }
+        /* full softmax (max-subtracted), then renormalise over the picks */
+        double m = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > m) m = l[e];
+        double s = 0.0;
+        for (int e = 0; e < E; ++e) {
+            p[e] = exp((double)l[e] - m);
+            s += p[e];
+        }
+        for (int e = 0; e < E; ++e)
+            p[e] /= s;
+        double ssel = 0.0;
+        for (int j = 0; j < top_k; ++j)
+            ssel += p[ids[(long)t * top_k + j]];
+        for (int j = 0; j < top_k; ++j)
+            w[(long)t * top_k + j] = (float)(p[ids[(long)t * top_k + j]] / ssel);
+    }
+    free(p);
+    free(taken);
+}
+
+/* ------------------------------------------------------------------ */
+/* Dispatch on one GPU: group the N = T*top_k assignments a = t*top_k + j */
+/* by expert (FlyDSL #972 Technical Details: dispatch of the quantised  */
+/* payloads to their experts; on one device this is a permutation).     */
+/* ------------------------------------------------------------------ */
+
+/* counts[e] = #assignments to e; offsets = exclusive prefix sum (E+1
+ * entries); perm lists assignment ids grouped by ascending expert and
+ * ascending assignment id within an expert. */
+void oracle_sort(const int32_t *ids, int T, int E, int top_k,
+                 int32_t *counts, int32_t *offsets, int32_t *perm)
+{
+    long N = (long)T * top_k;
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (long a = 0; a < N; ++a)
+        counts[ids[a]] += 1;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *fill = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    for (int e = 0; e < E; ++e)
+        fill[e] = offsets[e];
+    for (long a = 0; a < N; ++a)
+        perm[fill[ids[a]]++] = (int32_t)a;
+    free(fill);
+}
+
+/* ------------------------------------------------------------------ */
+/* The layer                                                            */
+/* ------------------------------------------------------------------ */
+
+/*
+ * x        [T][H] bf16                  logits [T][E] fp32
+ * w13      [E][2I][H/2] E2M1 pairs      w13s   [E][2I][H/32] E8M0
+ *          rows [0,I) are gate rows, rows [I,2I) are up rows
+ * w2       [E][H][I/2]  E2M1 pairs      w2s    [E][H][I/32]  E8M0
+ * fmt      activation format: 0 = MXFP8 E4M3 (A8W4), 1 = MXFP4 E2M1 (A4W4)
+ * acc_double  0: FP32 evaluation (products and sums in float, ascending
+ *             K, no contraction); 1: the same steps in double.
+ * y        [T][H] bf16 (round to nearest even of the FP32 combine)
+ * y_f32    optional [T][H] fp32 combine before the bf16 rounding
+ * a2_codes / a2_scales  optional [T*top_k][I or I/2] / [T*top_k][I/32]
+ *             requantised SwiGLU activations, indexed by assignment.
+ * expert_map  optional [E]: when given, expert e's weights are the
+ *             expert_map[e]-th slab of w13/w13s/w2/w2s (a compact set holding
+ *             only the experts the tokens route to); NULL means slab e.
+ */
+void oracle_forward(const uint16_t *x, const float *logits, int T, int H, int I, int E,
+                    int top_k, int fmt,
+                    const uint8_t *w13, const uint8_t *w13s,
+                    const uint8_t *w2, const uint8_t *w2s,
+                    int acc_double, uint16_t *y, float *y_f32,
+                    uint8_t *a2_codes, uint8_t *a2_scales, const int32_t *expert_map)
+{
+    long a1_row = (fmt == FMT_E4M3) ? H : H / 2;
+    long a2_row = (fmt == FMT_E4M3) ? I : I / 2;
+    int KM = H > I ? H : I;
+    int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * ((size_t)T * top_k + 1));
+    float *wts = (float *)malloc(sizeof(float) * ((size_t)T * top_k + 1));
+    uint8_t *xa = (uint8_t *)malloc((size_t)a1_row + 1);
+    uint8_t *xs = (uint8_t *)malloc((size_t)H / 32 + 1);
+    double *xdq = (double *)malloc(sizeof(double) * (size_t)H);
+    double *wrow = (double *)malloc(sizeof(double) * (size_t)KM);
+    double *gu = (double *)malloc(sizeof(double) * 2 * (size_t)I); /* gate, then up */
+    double *hbuf = (double *)malloc(sizeof(double) * (size_t)I);
+    uint8_t *ha = (uint8_t *)malloc((size_t)a2_row + 1);
+    uint8_t *hs = (uint8_t *)malloc((size_t)I / 32 + 1);
+    double *hdq = (double *)malloc(sizeof(double) * (size_t)I);
+    float *cf = (float *)malloc(sizeof(float) * (size_t)H);
+    double *cd = (double *)malloc(sizeof(double) * (size_t)H);
+
+    init_tables();
+
+    /* step 1: routing */
+    oracle_route(logits, T, E, top_k, ids, wts);
+
+    for (int t = 0; t < T; ++t) {
+        /* step 2: quantise the token once, before dispatch */
+        oracle_mx_quantize_bf16(x + (long)t * H, 1, H, fmt, xa, xs);
+        dequant_row(xa, xs, H, fmt, xdq);
+        for (int h = 0; h < H; ++h) {
+            cf[h] = 0.0f;
+            cd[h] = 0.0;
+        }
+        for (int j = 0; j < top_k; ++j) {
+            long a = (long)t * top_k + j;
+            int e = ids[a];
+            float wj = wts[a];
+            long slab = expert_map ? (long)expert_map[e] : (long)e;
+            /* step 3: GEMM1, the token row against every gate and up row of e */
+            for (int n = 0; n < 2 * I; ++n) {
+                long row = slab * 2 * I + n;
+                dequant_row(w13 + row * (H / 2), w13s + row * (H / 32), H, FMT_E2M1, wrow);
+                if (acc_double) {
+                    double acc = 0.0;
+                    for (int k = 0; k < H; ++k)
+                        acc += xdq[k] * wrow[k];
+                    gu[n] = acc;
+                } else {
+                    float acc = 0.0f;
+                    for (int k = 0; k < H; ++k) {
+                        float prod = (float)xdq[k] * (float)wrow[k];
+                        acc = acc + prod;
+                    }
+                    gu[n] = (double)acc;
+                }
+            }
+            /* step 4: SwiGLU h = silu(gate) * up, silu(g) = g / (1 + exp(-g)) */
+            for (int i = 0; i < I; ++i) {
+                if (acc_double) {
+                    double g = gu[i], u = gu[I + i];
+                    hbuf[i] = g / (1.0 + exp(-g)) * u;
+                } else {
+                    float g = (float)gu[i], u = (float)gu[I + i];
+                    float s = g / (1.0f + expf(-g));
+                    hbuf[i] = (double)(s * u);
+                }
+            }
+            /* step 5: requantise h along I in 1x32 blocks */
+            mx_quantize_rows_d(hbuf, 1, I, fmt, ha, hs);
+            if (a2_codes)
+                memcpy(a2_codes + a * a2_row, ha, (size_t)a2_row);
+            if (a2_scales)
+                memcpy(a2_scales + a * (long)(I / 32), hs, (size_t)I / 32);
+            dequant_row(ha, hs, I, fmt, hdq);
+            /* step 6: GEMM2 and the weighted FP32 combine in slot order */
+            for (int hh = 0; hh < H; ++hh) {
+                long row = slab * H + hh;
+                dequant_row(w2 + row * (I / 2), w2s + row * (I / 32), I, FMT_E2M1, wrow);
+                if (acc_double) {
+                    double acc = 0.0;
+                    for (int i = 0; i < I; ++i)
+                        acc += hdq[i] * wrow[i];
+                    cd[hh] += (double)wj * acc;
+                } else {
+                    float acc = 0.0f;
+                    for (int i = 0; i < I; ++i) {
+                        float prod = (float)hdq[i] * (float)wrow[i];
+                        acc = acc + prod;
+                    }
+                    float contrib = wj * acc;
+                    cf[hh] = cf[hh] + contrib;
+                }
+            }
+        }
+        /* step 7: BF16 output */
+        for (int hh = 0; hh < H; ++hh) {
+            float c = acc_double ? (float)cd[hh] : cf[hh];
+            if (y_f32)
+                y_f32[(long)t * H + hh] = c;
+            y[(long)t * H + hh] = float_to_bf16(c);
+        }
+    }
+    free(ids); free(wts); free(xa); free(xs); free(xdq); free(wrow); free(gu);
+    free(hbuf); free(ha); free(hs); free(hdq); free(cf); free(cd);
+}
