@@ -1,0 +1,234 @@
+"""Benchmark of the MI355X MoE layer: one JSON line on stdout.
+
+A step is one moe_forward call (routing, expert sort, activation quant,
+GEMM1 + SwiGLU + requant, GEMM2 + weighted FP32 combine, BF16 finalize) on
+a batch of T synthetic tokens already resident in HBM.  The default workload
+is the DeepSeek-V4-Pro-shaped A8W4 decode layer (H=7168, I=3072, E=384,
+top_k=6, all experts resident) at T=64; the other decode sizes of that
+workload (T=1, 2, 8, 32) are timed too and reported under "sweep".
+
+Between steps the router logits rotate over 8 pre-drawn sets, so successive
+calls touch different experts (the touched weights of one call are larger
+than the MI355X last-level cache at T >= 8, and rotate through ~1.7 GB at
+T = 1).  Per-kernel times come from HIP events the library records around
+every kernel of the timed calls; the roofline entry is for the dominant
+kernel (GEMM1) against HBM bandwidth, with its algorithmic bytes per launch:
+touched experts x gate/up weight bytes (codes + E8M0 scales) + the quantised
+token rows read + the requantised rows written.
+
+cpu_baseline: the CPU oracle (test infrastructure, single-threaded C)
+timed on a bounded sample of the same workload: routing, sort and
+quantisation of all T tokens plus the expert FFN of a few sampled tokens.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="v4pro_decode")
+    p.add_argument("--T", type=int, default=None, help="headline token count")
+    p.add_argument("--act", type=int, default=None, help="0 = MXFP8 (A8W4), 1 = MXFP4 (A4W4)")
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=4, help="tokens the oracle FFN runs on")
+    return p.parse_args()
+
+
+def touched_experts(moe, layer, ws, T, top_k, act):
+    import numpy as np
+    offs = moe.moe_workspace_offsets(layer, T, top_k, act)
+    o = offs[moe.MOE_WS_COUNTS]
+    counts = ws[o:o + 4 * layer.E].cpu().numpy().view(np.int32)
+    return int((counts > 0).sum())
+
+
+def gemm1_bytes(layer, U, T, top_k, act):
+    H, I = layer.H, layer.I
+    a1 = (H if act == 0 else H // 2) + H // 32
+    a2 = (I if act == 0 else I // 2) + I // 32
+    return U * (I * H + 2 * I * H // 32) + T * a1 + T * top_k * a2
+
+
+def layer_weight_bytes(layer, U):
+    H, I = layer.H, layer.I
+    return U * (I * H + 2 * I * H // 32 + H * I // 2 + H * I // 32)
+
+
+def time_T(moe, torch, layer, wl, T, act, steps, warmup, profile):
+    x = torch.from_numpy(wl.x(T).view("int16")).cuda().view(torch.bfloat16)
+    lgs = [torch.from_numpy(wl.logits(T, r)).cuda() for r in range(8)]
+    ws = moe.alloc_workspace(layer, T, wl.top_k, act)
+    y = torch.empty((T, wl.H), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    Us = []
+    for r in range(8):
+        moe.moe_forward(layer, x, lgs[r], wl.top_k, act, y=y, ws=ws)
+        torch.cuda.synchronize()
+        Us.append(touched_experts(moe, layer, ws, T, wl.top_k, act))
+    for i in range(warmup):
+        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws)
+    if profile:
+        moe.moe_profile_enable(layer, True, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kern, ncalls = (moe.moe_profile_read(layer) if profile else ({}, 0))
+    if profile:
+        moe.moe_profile_enable(layer, False)
+    U_timed = [Us[i % 8] for i in range(steps)]
+    return dt, kern, ncalls, U_timed, x, lgs
+
+
+def cpu_baseline(moe, torch, layer_dev_weights, wl, T, act, rows):
+    """Oracle on a bounded sample: route/sort/quant of all T tokens + FFN of `rows` tokens."""
+    import numpy as np
+    import oracle
+    w13, w13s, w2, w2s = layer_dev_weights
+    x = wl.x(T)
+    lg = wl.logits(T, 0)
+    t0 = time.perf_counter()
+    ids, _ = oracle.route(lg, wl.top_k)
+    oracle.sort(ids, wl.E)
+    oracle.mx_quantize_bf16(x, act)
+    t_front = time.perf_counter() - t0
+    sample = np.linspace(0, T - 1, num=min(rows, T)).astype(np.int64)
+    cache = {}
+
+    def wfor(e):
+        if e not in cache:
+            cache[e] = tuple(a[e].cpu().numpy() for a in (w13, w13s, w2, w2s))
+        return cache[e]
+    sel, _ = oracle.route(lg[sample], wl.top_k)
+    for e in set(int(v) for v in sel.reshape(-1)):
+        wfor(e)  # fetch the sampled tokens' experts outside the timed part
+    t0 = time.perf_counter()
+    oracle.forward_rows(x, lg, sample, wfor, wl.top_k, act)
+    t_ffn = time.perf_counter() - t0
+    per_token = t_front / T + t_ffn / len(sample)
+    return {
+        "value": 1.0 / per_token,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": ("route+sort+quant of all %d tokens (%.3f s) + expert FFN of %d sampled tokens "
+                   "(%.2f s); value = 1 / (front time per token + FFN time per sampled token)"
+                   % (T, t_front, len(sample), t_ffn)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (the layer's "
+              "experts all fit one MI355X); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import quantized_moe_expert_softmax_amd as moe
+    from quantized_moe_expert_softmax_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    act = wl.act if args.act is None else args.act
+    T = args.T or max(wl.Ts)
+    torch.cuda.set_device(0)
+    log("building %s weights on the device (H=%d I=%d E=%d)" % (wl.name, wl.H, wl.I, wl.E))
+    t0 = time.perf_counter()
+    w = synth.device_weights(wl.H, wl.I, wl.E, wl.seed)
+    layer = moe.moe_prepare_weights(wl.E, wl.H, wl.I, *w)
+    torch.cuda.synchronize()
+    log("weights ready in %.1f s" % (time.perf_counter() - t0))
+
+    dt, kern, ncalls, Us, _, _ = time_T(moe, torch, layer, wl, T, act, args.steps, args.warmup,
+                                        profile=True)
+    ms_step = dt * 1e3 / args.steps
+    value = T * args.steps / dt
+    g1_ms = kern["gemm1"] / max(ncalls, 1)
+    U_mean = sum(Us[:ncalls]) / max(ncalls, 1)
+    g1_bytes = gemm1_bytes(layer, U_mean, T, wl.top_k, act)
+    achieved = g1_bytes / (g1_ms * 1e-3) / 1e9
+    kernels_us = {k: round(v / max(ncalls, 1) * 1e3, 2) for k, v in kern.items()}
+    layer_gbs = layer_weight_bytes(layer, U_mean) / (ms_step * 1e-3) / 1e9
+    log("T=%d: %.1f us/step, %.0f tokens/s, gemm1 %.1f us (%.0f GB/s), kernels %s"
+        % (T, ms_step * 1e3, value, g1_ms * 1e3, achieved, kernels_us))
+
+    sweep = {}
+    if not args.no_sweep:
+        for t in wl.Ts:
+            if t == T:
+                continue
+            d, kk, nc, us, _, _ = time_T(moe, torch, layer, wl, t, act, args.steps, args.warmup,
+                                         profile=True)
+            um = sum(us[:nc]) / max(nc, 1)
+            g1 = kk["gemm1"] / max(nc, 1)
+            sweep[str(t)] = {
+                "us_per_call": round(d * 1e6 / args.steps, 2),
+                "tokens_per_s": round(t * args.steps / d, 1),
+                "touched_experts": round(um, 1),
+                "layer_weight_GBps": round(layer_weight_bytes(layer, um) / (d / args.steps) / 1e9, 1),
+                "gemm1_us": round(g1 * 1e3, 2),
+                "gemm1_GBps": round(gemm1_bytes(layer, um, t, wl.top_k, act) / (g1 * 1e-3) / 1e9, 1),
+            }
+            log("T=%d: %s" % (t, sweep[str(t)]))
+    sweep[str(T)] = {"us_per_call": round(ms_step * 1e3, 2), "tokens_per_s": round(value, 1),
+                     "touched_experts": round(U_mean, 1), "layer_weight_GBps": round(layer_gbs, 1),
+                     "gemm1_us": round(g1_ms * 1e3, 2), "gemm1_GBps": round(achieved, 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(moe, torch, w, wl, T, act, args.cpu_rows)
+    dtype = "mxfp8xmxfp4" if act == 0 else "mxfp4xmxfp4"
+    line = {
+        "metric": "MoE layer tokens/s at T=%d (%s) on one MI355X; us/call vs T in sweep"
+                  % (T, "A8W4" if act == 0 else "A4W4"),
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s H=%d I=%d E=%d top_k=%d T=%d %s" % (
+            wl.name, wl.H, wl.I, wl.E, wl.top_k, T, "A8W4" if act == 0 else "A4W4"),
+            "global_batch": T, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": "gemm1", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": int(g1_bytes),
+                     "avg_launch_us": round(g1_ms * 1e3, 2)},
+        "kernels_us": kernels_us,
+        "sweep": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    layer.close()
+
+
+if __name__ == "__main__":
+    main()

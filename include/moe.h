@@ -1,0 +1,191 @@
+/*
+ * moe.h -- C-ABI of the MI355X (gfx950) routed-expert MoE layer.
+ *
+ * The layer (sources: "add A4W4 and FP8 P2P transport support to MegaMoE",
+ * ROCm/FlyDSL #972, Motivation and Technical Details; "feat(moe): FlyDSL
+ * MegaMoE fused EP-MoE integration", ROCm/ATOM #1666, summary bullets;
+ * "[HIP] gfx950 A8W4 fused_moe configs for DSv4.1 TP-sharded experts",
+ * ROCm/aiter #6125, Motivation and Changes):
+ *
+ *   1. top-k softmax routing of router logits [T, E];
+ *   2. dispatch: the T*top_k (token, slot) assignments grouped by expert
+ *      (one device holds every expert, so dispatch is a permutation);
+ *   3. BF16 activations quantised once per token to MXFP8 (E4M3, "A8W4") or
+ *      MXFP4 (E2M1, "A4W4") with one E8M0 scale per 1x32 block;
+ *   4. GEMM1 against the MXFP4 gate/up weights of each assignment's expert,
+ *      SwiGLU h = silu(gate) * up, h re-quantised to the activation format;
+ *   5. GEMM2 against the MXFP4 down weights, each row scaled by its routing
+ *      weight and accumulated over the top_k slots in FP32; output BF16.
+ *
+ * Conventions (all calls):
+ *   - Every pointer argument is a DEVICE pointer on the current HIP device
+ *     unless stated otherwise; the caller owns it.  Calls only enqueue work on
+ *     the given stream (0 = the legacy default stream) unless stated.
+ *   - Errors are returned as moe_status; nothing aborts.  Arguments are
+ *     validated before anything is enqueued; a failing call enqueues nothing
+ *     (HIP launch failures excepted: then MOE_ERR_HIP).  moe_last_error()
+ *     returns a thread-local description of the last failure.
+ *   - MX layouts at the ABI are canonical: E2M1 codes are packed two per byte,
+ *     the even element in the low nibble; E4M3 codes take one byte (OCP
+ *     E4M3FN); E8M0 scales are one byte per 1x32 block along the contraction
+ *     dimension, row-major, value 2^(byte - 127).
+ *   - Limits: 1 <= E <= 1024, 1 <= top_k <= min(E, 8), H and I positive
+ *     multiples of 128, 0 <= T <= 2^20; byte offsets are 64-bit throughout.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_layer *moe_layer_t;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* null pointer, size out of range, bad enum    */
+    MOE_ERR_UNSUPPORTED = -2, /* not a gfx950 device                           */
+    MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_workspace_bytes()  */
+    MOE_ERR_OOM = -4,         /* device allocation failed (prepare only)       */
+    MOE_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed     */
+} moe_status;
+
+/* Activation format of one forward call (chosen per call against the same
+ * MXFP4 weights; aiter #6125 Motivation: A8W4 vs A4W4). */
+typedef enum {
+    MOE_ACT_MXFP8_E4M3 = 0, /* A8W4 */
+    MOE_ACT_MXFP4_E2M1 = 1  /* A4W4 */
+} moe_act_dtype;
+
+/*
+ * Copy and repack one layer's canonical MXFP4 expert weights into memory the
+ * layer owns (ATOM #1666 summary: weights are shuffled once at build time; the
+ * expert count is stored explicitly, never inferred from shapes).
+ *
+ *   E, H, I    experts, hidden size, intermediate size (per expert)
+ *   w13        [E][2I][H/2] E2M1 pairs; rows [0, I) are the gate rows and
+ *              rows [I, 2I) the up rows of each expert (the gate/up pairing
+ *              that SwiGLU needs is kept by the repack)
+ *   w13_scale  [E][2I][H/32] E8M0
+ *   w2         [E][H][I/2]  E2M1 pairs (down projection, contraction over I)
+ *   w2_scale   [E][H][I/32] E8M0
+ *   s          stream for the repack; the call synchronises s before
+ *              returning, after which the canonical buffers may be freed
+ *   out        host pointer receiving the handle
+ *
+ * This is the only call that allocates device memory (about the canonical
+ * size: E*I*H*(3/2 + 3/32) bytes).  Returns MOE_ERR_OOM if that fails.
+ */
+moe_status moe_prepare_weights(int E, int H, int I, const void *w13, const void *w13_scale,
+                               const void *w2, const void *w2_scale, hipStream_t s,
+                               moe_layer_t *out);
+
+/* Release a handle and its device memory (synchronises the device first).
+ * NULL is ignored. */
+void moe_destroy(moe_layer_t layer);
+
+/* Bytes of workspace moe_forward needs for (T, top_k, act); 0 on invalid
+ * arguments (see moe_last_error). */
+size_t moe_workspace_bytes(moe_layer_t layer, int T, int top_k, moe_act_dtype act);
+
+/*
+ * One forward pass of the layer.
+ *
+ *   x        [T][H] bf16 tokens
+ *   logits   [T][E] fp32 router logits
+ *   top_k    experts per token
+ *   act      activation format
+ *   y        [T][H] bf16 output (may not alias x)
+ *   ws       device workspace of at least moe_workspace_bytes(layer, T,
+ *            top_k, act) bytes, 256-byte aligned; its contents need not be
+ *            initialised and are overwritten
+ *
+ * Only enqueues kernels on s: no allocation, no host synchronisation and no
+ * memcpy, so the call can be captured into a HIP graph.  T == 0 is a no-op.
+ * Calls sharing a workspace must be ordered (same stream); different
+ * workspaces may run concurrently against one handle.
+ */
+moe_status moe_forward(moe_layer_t layer, const void *x, const float *logits, int T, int top_k,
+                       moe_act_dtype act, void *y, void *ws, size_t ws_bytes, hipStream_t s);
+
+/* Regions of the forward workspace, for inspection after a call (all device
+ * pointers into ws; layouts as listed). */
+typedef enum {
+    MOE_WS_IDS = 0,     /* [T][top_k] int32 expert ids, slot order           */
+    MOE_WS_WEIGHTS,     /* [T][top_k] fp32 routing weights                   */
+    MOE_WS_COUNTS,      /* [E] int32 assignments per expert                  */
+    MOE_WS_OFFSETS,     /* [E+1] int32 exclusive prefix sum of counts        */
+    MOE_WS_PERM,        /* [T*top_k] int32 assignment ids t*top_k+j, grouped
+                           by expert, ascending within an expert             */
+    MOE_WS_A1_CODES,    /* [T][H] (E4M3) or [T][H/2] (E2M1) token codes      */
+    MOE_WS_A1_SCALES,   /* [T][H/32] E8M0                                    */
+    MOE_WS_A2_CODES,    /* [T*top_k][I] or [..][I/2] SwiGLU codes, row p is
+                           the assignment perm[p]                           */
+    MOE_WS_A2_SCALES,   /* [T*top_k][I/32] E8M0, same rows                   */
+    MOE_WS_COMBINE,     /* [T][H] fp32 weighted top-k sums                   */
+    MOE_WS_NUM
+} moe_ws_region;
+
+/* Byte offsets of each region inside the workspace (offs has MOE_WS_NUM
+ * entries, host memory). */
+moe_status moe_workspace_offsets(moe_layer_t layer, int T, int top_k, moe_act_dtype act,
+                                 size_t *offs);
+
+/* ---- stage entry points: the same kernels moe_forward launches ---------- */
+
+/* Step 1 (aiter #6125 Changes: the top-k softmax kernel).  For each token the
+ * top_k largest logits are taken, larger first, equal logits by lower expert
+ * index; w[t][j] = exp(l_j - m) / sum over the picks of exp(l - m), which is
+ * the softmax over all E renormalised over the picks.
+ *   logits [T][E] fp32 -> ids [T][top_k] int32, w [T][top_k] fp32. */
+moe_status moe_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w,
+                     hipStream_t s);
+
+/* Workspace bytes moe_sort needs for (T, E). */
+size_t moe_sort_workspace_bytes(int T, int E);
+
+/* Step 2 (FlyDSL #972 Technical Details: dispatch).  ids [T][top_k] int32 ->
+ * counts [E], offsets [E+1] (exclusive prefix sum), perm [T*top_k]: the flat
+ * assignment ids a = t*top_k + j grouped by ascending expert and ascending a
+ * within an expert (a deterministic, stable order).  Every id must lie in
+ * [0, E) and a token's top_k ids must be distinct (as routing produces). */
+moe_status moe_sort(const int32_t *ids, int T, int E, int top_k, int32_t *counts,
+                    int32_t *offsets, int32_t *perm, void *ws, size_t ws_bytes, hipStream_t s);
+
+/* Step 3 (FlyDSL #972 Technical Details: quantise BF16 activations with
+ * per-1x32 E8M0 scales).  x [T][H] bf16 -> codes [T][H] (E4M3) or [T][H/2]
+ * (E2M1), scales [T][H/32].  Block exponent floor(log2(amax)) - emax (8 for
+ * E4M3, 2 for E2M1) clamped to [-127, 127] (an all-zero block gets byte 0);
+ * elements rounded to nearest even and saturated, the sign of zero kept. */
+moe_status moe_quant_act(const void *x, int T, int H, moe_act_dtype act, uint8_t *codes,
+                         uint8_t *scales, hipStream_t s);
+
+/* ---- kernel timing for benchmarks (not thread-safe; mutates the handle) -- */
+
+/* Kernels moe_forward launches, in order. */
+typedef enum {
+    MOE_K_ROUTE = 0, MOE_K_SORT_HIST, MOE_K_SORT_SCAN, MOE_K_SORT_SCATTER, MOE_K_QUANT,
+    MOE_K_GEMM1, MOE_K_GEMM2, MOE_K_FINALIZE, MOE_K_NUM
+} moe_kernel_id;
+
+/* When enabled, each moe_forward records HIP events around every kernel on
+ * its stream (up to max_calls calls are kept; later calls are not timed).
+ * Enabling resets the record.  Events are created here, not in forward. */
+moe_status moe_profile_enable(moe_layer_t layer, int enable, int max_calls);
+
+/* Waits for the recorded events and writes, per moe_kernel_id, the summed
+ * milliseconds (ms[MOE_K_NUM], host) over *ncalls timed calls. */
+moe_status moe_profile_read(moe_layer_t layer, float *ms, int *ncalls);
+
+/* ---- errors --------------------------------------------------------------- */
+const char *moe_status_str(moe_status st);
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,244 @@
+"""MI355X (gfx950) routed-expert MoE layer with MXFP4 weights and MXFP8/MXFP4
+activations -- Python binding of the C-ABI in include/moe.h.
+
+The binding only marshals arguments: every step of the layer runs in the HIP
+kernels of libmoe_mi355x.so (built in-tree by ``build.py``).  If that library
+is missing, every call raises; there is no fallback.
+
+PyTorch is used for device memory and streams: tensors are passed by data
+pointer, the stream is torch's current stream unless one is given.
+
+Names mirror the C-ABI: moe_prepare_weights, moe_workspace_bytes,
+moe_forward, moe_destroy, moe_route, moe_sort, moe_quant_act, plus
+moe_workspace_offsets and the kernel-timing calls.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_OOM = -4
+MOE_ERR_HIP = -5
+
+MOE_ACT_MXFP8_E4M3 = 0  # A8W4
+MOE_ACT_MXFP4_E2M1 = 1  # A4W4
+
+(MOE_WS_IDS, MOE_WS_WEIGHTS, MOE_WS_COUNTS, MOE_WS_OFFSETS, MOE_WS_PERM, MOE_WS_A1_CODES,
+ MOE_WS_A1_SCALES, MOE_WS_A2_CODES, MOE_WS_A2_SCALES, MOE_WS_COMBINE, MOE_WS_NUM) = range(11)
+
+KERNELS = ("route", "sort_hist", "sort_scan", "sort_scatter", "quant", "gemm1", "gemm2",
+           "finalize")
+MOE_K_NUM = len(KERNELS)
+
+EXPORTS = ("moe_prepare_weights", "moe_destroy", "moe_workspace_bytes", "moe_forward",
+           "moe_workspace_offsets", "moe_route", "moe_sort_workspace_bytes", "moe_sort",
+           "moe_quant_act", "moe_profile_enable", "moe_profile_read", "moe_status_str",
+           "moe_last_error")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (status, msg))
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmoe_mi355x.so (raises if it was not built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError("HIP library %s is missing; run quantized_moe_expert_softmax_amd."
+                               "build.build() first (there is no CPU fallback)" % path)
+        import torch  # noqa: F401  (loads the HIP runtime the library links against)
+        lib = ctypes.CDLL(path)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        lib.moe_prepare_weights.argtypes = [I, I, I, P, P, P, P, P, ctypes.POINTER(P)]
+        lib.moe_destroy.argtypes = [P]
+        lib.moe_destroy.restype = None
+        lib.moe_workspace_bytes.argtypes = [P, I, I, I]
+        lib.moe_workspace_bytes.restype = Z
+        lib.moe_forward.argtypes = [P, P, P, I, I, I, P, P, Z, P]
+        lib.moe_workspace_offsets.argtypes = [P, I, I, I, P]
+        lib.moe_route.argtypes = [P, I, I, I, P, P, P]
+        lib.moe_sort_workspace_bytes.argtypes = [I, I]
+        lib.moe_sort_workspace_bytes.restype = Z
+        lib.moe_sort.argtypes = [P, I, I, I, P, P, P, P, Z, P]
+        lib.moe_quant_act.argtypes = [P, I, I, I, P, P, P]
+        lib.moe_profile_enable.argtypes = [P, I, I]
+        lib.moe_profile_read.argtypes = [P, P, P]
+        lib.moe_status_str.argtypes = [I]
+        lib.moe_status_str.restype = ctypes.c_char_p
+        lib.moe_last_error.argtypes = []
+        lib.moe_last_error.restype = ctypes.c_char_p
+        for name in ("moe_prepare_weights", "moe_forward", "moe_workspace_offsets", "moe_route",
+                     "moe_sort", "moe_quant_act", "moe_profile_enable", "moe_profile_read"):
+            getattr(lib, name).restype = I
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        lib = load_library()
+        raise MoeError(status, lib.moe_last_error().decode())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _require(t, dtype_bytes, shape, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.element_size() != dtype_bytes:
+        raise TypeError("%s must have %d-byte elements, got %s" % (name, dtype_bytes, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+class MoeLayer:
+    """Owner of a moe_layer_t handle (repacked weights of one layer)."""
+
+    def __init__(self, handle, E, H, I):
+        self.handle = handle
+        self.E, self.H, self.I = E, H, I
+
+    def __del__(self):
+        self.close()
+
+    def close(self):
+        if getattr(self, "handle", None):
+            load_library().moe_destroy(self.handle)
+            self.handle = None
+
+
+def moe_prepare_weights(E, H, I, w13, w13_scale, w2, w2_scale, stream=None) -> MoeLayer:
+    """Repack canonical MXFP4 weights (uint8 device tensors) into a layer handle.
+
+    w13 [E, 2I, H/2] (gate rows then up rows), w13_scale [E, 2I, H/32],
+    w2 [E, H, I/2], w2_scale [E, H, I/32].  Synchronises the stream.
+    """
+    lib = load_library()
+    _require(w13, 1, (E, 2 * I, H // 2), "w13")
+    _require(w13_scale, 1, (E, 2 * I, H // 32), "w13_scale")
+    _require(w2, 1, (E, H, I // 2), "w2")
+    _require(w2_scale, 1, (E, H, I // 32), "w2_scale")
+    h = ctypes.c_void_p()
+    _check(lib.moe_prepare_weights(E, H, I, _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+                                   _stream(stream), ctypes.byref(h)))
+    return MoeLayer(h, E, H, I)
+
+
+def moe_workspace_bytes(layer: MoeLayer, T: int, top_k: int, act: int) -> int:
+    n = load_library().moe_workspace_bytes(layer.handle, T, top_k, act)
+    if n == 0 and T >= 0:
+        _check(MOE_ERR_INVALID_ARG)
+    return n
+
+
+def alloc_workspace(layer: MoeLayer, T: int, top_k: int, act: int, device=None):
+    import torch
+    n = moe_workspace_bytes(layer, T, top_k, act)
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def moe_forward(layer: MoeLayer, x, logits, top_k: int, act: int, y=None, ws=None, stream=None):
+    """y [T, H] bf16 = MoE(x [T, H] bf16, logits [T, E] fp32); enqueue only."""
+    import torch
+    lib = load_library()
+    T = x.shape[0]
+    _require(x, 2, (T, layer.H), "x")
+    _require(logits, 4, (T, layer.E), "logits")
+    if y is None:
+        y = torch.empty((T, layer.H), dtype=torch.bfloat16, device=x.device)
+    _require(y, 2, (T, layer.H), "y")
+    if ws is None:
+        ws = alloc_workspace(layer, T, top_k, act, x.device)
+    _check(lib.moe_forward(layer.handle, _ptr(x), _ptr(logits), T, top_k, act, _ptr(y), _ptr(ws),
+                           ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_workspace_offsets(layer: MoeLayer, T: int, top_k: int, act: int):
+    lib = load_library()
+    arr = (ctypes.c_size_t * MOE_WS_NUM)()
+    _check(lib.moe_workspace_offsets(layer.handle, T, top_k, act, arr))
+    return list(arr)
+
+
+def moe_route(logits, top_k: int, stream=None):
+    """ids [T, k] int32 and weights [T, k] fp32 from logits [T, E] fp32."""
+    import torch
+    lib = load_library()
+    T, E = logits.shape
+    _require(logits, 4, (T, E), "logits")
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    _check(lib.moe_route(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(w), _stream(stream)))
+    return ids, w
+
+
+def moe_sort(ids, E: int, stream=None):
+    """counts [E], offsets [E+1], perm [T*k] (int32) from ids [T, k] int32."""
+    import torch
+    lib = load_library()
+    T, k = ids.shape
+    _require(ids, 4, (T, k), "ids")
+    dev = ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    n = lib.moe_sort_workspace_bytes(T, E)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    _check(lib.moe_sort(_ptr(ids), T, E, k, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(ws),
+                        ws.numel(), _stream(stream)))
+    return counts, offsets, perm
+
+
+def moe_quant_act(x, act: int, stream=None):
+    """codes [T, H] (E4M3) or [T, H/2] (E2M1 pairs) and scales [T, H/32] uint8."""
+    import torch
+    lib = load_library()
+    T, H = x.shape
+    _require(x, 2, (T, H), "x")
+    codes = torch.empty((T, H if act == MOE_ACT_MXFP8_E4M3 else H // 2), dtype=torch.uint8,
+                        device=x.device)
+    scales = torch.empty((T, H // 32), dtype=torch.uint8, device=x.device)
+    _check(lib.moe_quant_act(_ptr(x), T, H, act, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def moe_profile_enable(layer: MoeLayer, enable: bool = True, max_calls: int = 1024):
+    _check(load_library().moe_profile_enable(layer.handle, int(bool(enable)), max_calls))
+
+
+def moe_profile_read(layer: MoeLayer):
+    """{kernel name: summed ms}, number of timed calls."""
+    lib = load_library()
+    ms = (ctypes.c_float * MOE_K_NUM)()
+    n = ctypes.c_int()
+    _check(lib.moe_profile_read(layer.handle, ms, ctypes.byref(n)))
+    return dict(zip(KERNELS, list(ms))), n.value

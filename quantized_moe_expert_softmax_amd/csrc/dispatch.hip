@@ -1,0 +1,404 @@
+// dispatch.hip -- routing, expert sort, activation quantisation, weight
+// repack and the BF16 finalize of the MoE layer (gfx950).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+#include "mx_device.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Step 1: top-k softmax routing ("[HIP] gfx950 A8W4 fused_moe configs for
+// DSv4.1 TP-sharded experts", Changes: the top-k softmax kernel).  One wave
+// per token: each lane holds E/64 logits in registers; top_k rounds of a
+// wave-wide arg-max (larger logit first, equal logits by lower index) pick
+// the experts; the weights are exp(l_j - max) normalised over the picks,
+// which equals the full softmax renormalised over the picks (the softmax
+// denominator over all E cancels).  The wave also
+// zeroes the token's FP32 combine row, which GEMM2 accumulates into.
+// ---------------------------------------------------------------------------
+template <int NV>
+__global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ logits, int T, int E,
+                                                    int top_k, int32_t *__restrict__ ids,
+                                                    float *__restrict__ wts,
+                                                    float *__restrict__ comb, int H) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long t = (long)blockIdx.x * 4 + wave;
+  if (t >= T) return;  // wave-uniform; no barriers below
+  const float *row = logits + t * E;
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : 0.0f;
+  }
+  if (comb) {
+    float4 *c = reinterpret_cast<float4 *>(comb + t * (long)H);
+    for (int i = lane; i < H / 4; i += 64) c[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  uint32_t taken = 0;
+  float selv[8];
+  int seli[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < top_k) {
+      float bv = 0.0f;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = lane + 64 * i;
+        // indices grow with i, so a strict compare keeps the lower index on ties
+        if (e < E && !((taken >> i) & 1u) && (bi == 0x7fffffff || v[i] > bv)) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        const bool better = oi != 0x7fffffff &&
+                            (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
+        if (better) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      selv[j] = bv;
+      seli[j] = bi;
+    }
+  }
+  // weights: exp(l_j - l_0) / sum_j' exp(l_j' - l_0); l_0 is the largest logit.
+  // Evaluated in double (the difference of two floats is exact there), then
+  // rounded once to float: at most top_k exponentials per token.
+  double ex[8];
+  double sum = 0.0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ex[j] = j < top_k ? exp((double)selv[j] - (double)selv[0]) : 0.0;
+    sum += ex[j];
+  }
+  if (lane < top_k) {
+    int id = 0;
+    double e = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j == lane) {
+        id = seli[j];
+        e = ex[j];
+      }
+    ids[t * top_k + lane] = id;
+    wts[t * top_k + lane] = (float)(e / sum);
+  }
+}
+
+hipError_t launch_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w,
+                        float *comb, int H, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(T, 4)), block(256);
+  const int nv = ceil_div(E, 64);
+#define ROUTE_CASE(NV_)                                                                   \
+  case NV_:                                                                               \
+    route_kernel<NV_><<<grid, block, 0, s>>>(logits, T, E, top_k, ids, w, comb, H);       \
+    break;
+  switch (nv) {
+    ROUTE_CASE(1) ROUTE_CASE(2) ROUTE_CASE(3) ROUTE_CASE(4) ROUTE_CASE(5) ROUTE_CASE(6)
+    ROUTE_CASE(7) ROUTE_CASE(8) ROUTE_CASE(9) ROUTE_CASE(10) ROUTE_CASE(11) ROUTE_CASE(12)
+    ROUTE_CASE(13) ROUTE_CASE(14) ROUTE_CASE(15) ROUTE_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef ROUTE_CASE
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Step 2: dispatch as an on-device, deterministic counting sort of the
+// assignments a = t*top_k + j by expert ("add A4W4 and FP8 P2P transport
+// support to MegaMoE", Technical Details: dispatch of the quantised payloads;
+// on one device the experts all live here, so dispatch is a permutation).
+//   hist:    per 256-token block, the number of assignments of each expert
+//   scan:    per expert, exclusive prefix over blocks -> block bases; counts,
+//            offsets (exclusive prefix over experts) and the prefix of
+//            16-row m-tiles per expert that the GEMMs schedule from
+//   scatter: within a block, the rank of a token among the tokens routed to
+//            the same expert comes from 64-bit per-wave masks (LDS atomic
+//            OR is order-free; popcount of the lanes below gives the rank),
+//            so the order within an expert is ascending token, i.e.
+//            ascending a (a token's top_k experts are distinct).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restrict__ ids, int T,
+                                                        int E, int top_k,
+                                                        int32_t *__restrict__ hist) {
+  extern __shared__ int32_t lhist[];
+  for (int e = threadIdx.x; e < E; e += 256) lhist[e] = 0;
+  __syncthreads();
+  const long t = (long)blockIdx.x * kSortBlock + threadIdx.x;
+  if (t < T) {
+    for (int j = 0; j < top_k; ++j) {
+      const uint32_t e = (uint32_t)ids[t * top_k + j];
+      if (e < (uint32_t)E) atomicAdd(&lhist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[(long)blockIdx.x * E + e] = lhist[e];
+}
+
+__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ hist, int nb, int E,
+                                                         int32_t *__restrict__ counts,
+                                                         int32_t *__restrict__ offsets,
+                                                         int32_t *__restrict__ mtoff) {
+  __shared__ int32_t sc[1024];
+  __shared__ int32_t sm[1024];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      const int v = hist[(long)b * E + e];
+      hist[(long)b * E + e] = run;
+      run += v;
+    }
+    counts[e] = run;
+  }
+  const int c = e < E ? run : 0;
+  const int m = e < E ? (run + kMTile - 1) / kMTile : 0;
+  sc[e] = c;
+  sm[e] = m;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int ac = e >= d ? sc[e - d] : 0;
+    const int am = e >= d ? sm[e - d] : 0;
+    __syncthreads();
+    sc[e] += ac;
+    sm[e] += am;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int base = sc[e] - c;
+    offsets[e] = base;
+    mtoff[e] = sm[e] - m;
+    if (e == E - 1) {
+      offsets[E] = sc[e];
+      mtoff[E] = sm[e];
+    }
+    for (int b = 0; b < nb; ++b) hist[(long)b * E + e] += base;
+  }
+}
+
+__global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__restrict__ ids, int T,
+                                                           int E, int top_k,
+                                                           const int32_t *__restrict__ base,
+                                                           int32_t *__restrict__ perm) {
+  extern __shared__ unsigned long long masks[];  // [4 waves][E]
+  for (int i = threadIdx.x; i < 4 * E; i += 256) masks[i] = 0ull;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long t = (long)blockIdx.x * kSortBlock + threadIdx.x;
+  const unsigned long long bit = 1ull << lane;
+  if (t < T) {
+    for (int j = 0; j < top_k; ++j) {
+      const uint32_t e = (uint32_t)ids[t * top_k + j];
+      if (e < (uint32_t)E) atomicOr(&masks[wave * E + e], bit);
+    }
+  }
+  __syncthreads();
+  if (t < T) {
+    for (int j = 0; j < top_k; ++j) {
+      const uint32_t e = (uint32_t)ids[t * top_k + j];
+      if (e >= (uint32_t)E) continue;
+      int r = __popcll(masks[wave * E + e] & (bit - 1ull));
+      for (int w = 0; w < wave; ++w) r += __popcll(masks[w * E + e]);
+      perm[base[(long)blockIdx.x * E + e] + r] = (int32_t)(t * top_k + j);
+    }
+  }
+}
+
+hipError_t launch_sort_hist(const int32_t *ids, int T, int E, int top_k, int32_t *hist, int nb,
+                            hipStream_t s) {
+  sort_hist_kernel<<<nb, 256, (size_t)E * 4, s>>>(ids, T, E, top_k, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_scan(int32_t *hist, int nb, int E, int32_t *counts, int32_t *offsets,
+                            int32_t *mtoff, hipStream_t s) {
+  sort_scan_kernel<<<1, 1024, 0, s>>>(hist, nb, E, counts, offsets, mtoff);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, const int32_t *hist,
+                               int32_t *perm, hipStream_t s) {
+  const int nb = ceil_div(T, kSortBlock);
+  sort_scatter_kernel<<<nb, 256, (size_t)E * 4 * 8, s>>>(ids, T, E, top_k, hist, perm);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Step 3: 1x32 MX quantisation of BF16 rows (FlyDSL #972 Technical Details:
+// BF16 activations to MXFP4 -- or MXFP8 on the A8W4 path -- with per-1x32
+// E8M0 scales, once per token before dispatch).  One thread per 32-element
+// block: amax over the bit patterns, block exponent, integer RNE encode.
+// ---------------------------------------------------------------------------
+template <class F>
+__global__ __launch_bounds__(256) void quant_kernel(const uint16_t *__restrict__ x, long nblocks,
+                                                    uint8_t *__restrict__ codes,
+                                                    uint8_t *__restrict__ scales) {
+  const long b = (long)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const uint4 *src = reinterpret_cast<const uint4 *>(x + b * 32);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 q = src[i];
+    w[4 * i + 0] = q.x;
+    w[4 * i + 1] = q.y;
+    w[4 * i + 2] = q.z;
+    w[4 * i + 3] = q.w;
+  }
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t lo = (w[i] << 16) & 0x7fffffffu, hi = w[i] & 0x7fff0000u;
+    amax = max(amax, max(lo, hi));
+  }
+  const int X = block_exponent<F>(amax);
+  if (F::kBits == 8) {
+    uint32_t out[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c0 = encode_element<F>(w[2 * i] << 16, X);
+      const uint32_t c1 = encode_element<F>(w[2 * i] & 0xffff0000u, X);
+      const uint32_t c2 = encode_element<F>(w[2 * i + 1] << 16, X);
+      const uint32_t c3 = encode_element<F>(w[2 * i + 1] & 0xffff0000u, X);
+      out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(codes + b * 32);
+    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  } else {
+    uint32_t out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t d = 0;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t word = w[4 * i + h];
+        const uint32_t c0 = encode_element<F>(word << 16, X);
+        const uint32_t c1 = encode_element<F>(word & 0xffff0000u, X);
+        d |= (c0 | (c1 << 4)) << (8 * h);
+      }
+      out[i] = d;
+    }
+    *reinterpret_cast<uint4 *>(codes + b * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+  scales[b] = (uint8_t)(X + 127);
+}
+
+hipError_t launch_quant(const uint16_t *x, long rows, int K, int act, uint8_t *codes,
+                        uint8_t *scales, hipStream_t s) {
+  const long nblocks = rows * (K / 32);
+  if (nblocks == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((nblocks + 255) / 256);
+  if (act == MOE_ACT_MXFP8_E4M3)
+    quant_kernel<E4M3><<<grid, 256, 0, s>>>(x, nblocks, codes, scales);
+  else
+    quant_kernel<E2M1><<<grid, 256, 0, s>>>(x, nblocks, codes, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Weight repack (load time; "feat(moe): FlyDSL MegaMoE fused EP-MoE
+// integration", summary bullets: gate/up weights are shuffled into the
+// interleaved layout the fused SwiGLU needs).  Canonical MXFP4 rows become
+// 1 KiB scaled-MFMA B fragments (see PackDims); for the gate/up matrix the
+// 16-row tiles are ordered gate[32j, +16), gate[32j+16, +16), up[32j, +16),
+// up[32j+16, +16) so that one GEMM1 work unit holds the gate and up columns
+// of one 32-wide requantisation block of h.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ long packed_row(int tile, int c, int half_rows, bool gate_up) {
+  if (!gate_up) return (long)tile * 16 + c;
+  const int j = tile >> 2, q = tile & 3;
+  return (long)((q >> 1) ? half_rows : 0) + 32 * j + 16 * (q & 1) + c;
+}
+
+__global__ __launch_bounds__(256) void prepack_codes_kernel(const uint8_t *__restrict__ src,
+                                                            long total, int R, int K, bool gate_up,
+                                                            uint8_t *__restrict__ dst) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int steps = K / 128, ntile = R / 16;
+  const int lane = (int)(idx & 63);
+  const long rest = idx >> 6;
+  const int s = (int)(rest % steps);
+  const long rest2 = rest / steps;
+  const int tile = (int)(rest2 % ntile);
+  const long e = rest2 / ntile;
+  const long row = packed_row(tile, lane & 15, R / 2, gate_up);
+  const uint8_t *p = src + (e * R + row) * (long)(K / 2) + 64 * s + 16 * (lane >> 4);
+  *reinterpret_cast<uint4 *>(dst + idx * 16) = *reinterpret_cast<const uint4 *>(p);
+}
+
+__global__ __launch_bounds__(256) void prepack_scales_kernel(const uint8_t *__restrict__ src,
+                                                             long total, int R, int K,
+                                                             bool gate_up,
+                                                             uint32_t *__restrict__ dst) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int steps = K / 128, groups = (steps + 3) / 4, ntile = R / 16;
+  const int lane = (int)(idx & 63);
+  const long rest = idx >> 6;
+  const int gq = (int)(rest % groups);
+  const long rest2 = rest / groups;
+  const int tile = (int)(rest2 % ntile);
+  const long e = rest2 / ntile;
+  const long row = packed_row(tile, lane & 15, R / 2, gate_up);
+  const uint8_t *p = src + (e * R + row) * (long)(K / 32);
+  uint32_t d = 0;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int s = 4 * gq + jj;
+    const uint32_t byte = s < steps ? p[4 * s + (lane >> 4)] : 127u;
+    d |= byte << (8 * jj);
+  }
+  dst[idx] = d;
+}
+
+hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int E, int R, int K,
+                          bool gate_up, uint8_t *pcodes, uint8_t *pscales, hipStream_t s) {
+  const PackDims d = pack_dims(R, K);
+  const long nc = (long)E * (R / 16) * d.steps * 64;
+  const long ns = (long)E * (R / 16) * d.groups * 64;
+  prepack_codes_kernel<<<(unsigned)((nc + 255) / 256), 256, 0, s>>>(codes, nc, R, K, gate_up,
+                                                                   pcodes);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  prepack_scales_kernel<<<(unsigned)((ns + 255) / 256), 256, 0, s>>>(
+      scales, ns, R, K, gate_up, reinterpret_cast<uint32_t *>(pscales));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Finalize: y = bf16(combine), round to nearest even; 8 elements per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__ comb, long n8,
+                                                       uint16_t *__restrict__ y) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const float4 a = reinterpret_cast<const float4 *>(comb)[2 * i];
+  const float4 b = reinterpret_cast<const float4 *>(comb)[2 * i + 1];
+  uint4 o;
+  o.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
+  o.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
+  o.z = (uint32_t)f32_to_bf16(b.x) | ((uint32_t)f32_to_bf16(b.y) << 16);
+  o.w = (uint32_t)f32_to_bf16(b.z) | ((uint32_t)f32_to_bf16(b.w) << 16);
+  reinterpret_cast<uint4 *>(y)[i] = o;
+}
+
+hipError_t launch_finalize(const float *comb, long n, uint16_t *y, hipStream_t s) {
+  const long n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  finalize_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(comb, n8, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,104 @@
+// internal.h -- host-side plan shared by the C-ABI and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kSortBlock = 256;  // tokens per sort workgroup
+constexpr int kMTile = 16;       // rows per MFMA m-tile
+constexpr int kUnit = 32;        // h columns per GEMM1 work unit (one requant block)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+// Prepacked weight layout of one matrix of R rows and K columns (R % 16 == 0,
+// K % 128 == 0): codes [R/16 n-tiles][K/128 steps][64 lanes][16 B], scales
+// [R/16][ceil(K/512) groups][64 lanes][4 B].  Lane l = 16*g + c holds row
+// 16*tile + c, columns [128*step + 32*g, +32) (the gfx950 scaled-MFMA B
+// operand of one 16x16x128 step); its scale dword holds the E8M0 bytes of
+// blocks 4*step + g for the four steps of a group.
+struct PackDims {
+  int R, K, steps, groups;
+  size_t code_bytes_per_tile() const { return (size_t)steps * 1024; }
+  size_t scale_bytes_per_tile() const { return (size_t)groups * 256; }
+  size_t code_bytes() const { return (size_t)(R / 16) * code_bytes_per_tile(); }
+  size_t scale_bytes() const { return (size_t)(R / 16) * scale_bytes_per_tile(); }
+};
+inline PackDims pack_dims(int R, int K) { return PackDims{R, K, K / 128, (K / 128 + 3) / 4}; }
+
+struct WsLayout {
+  size_t off[MOE_WS_NUM];
+  size_t hist;    // [nb][E] int32 per-sort-block histograms, then bases
+  size_t mtoff;   // [E+1] int32 prefix sum of m-tiles per expert
+  size_t total;
+  int nb;
+};
+
+inline WsLayout ws_layout(int T, int top_k, int E, int H, int I, int act) {
+  WsLayout L{};
+  const size_t N = (size_t)T * top_k;
+  const size_t a1row = act == MOE_ACT_MXFP8_E4M3 ? (size_t)H : (size_t)H / 2;
+  const size_t a2row = act == MOE_ACT_MXFP8_E4M3 ? (size_t)I : (size_t)I / 2;
+  L.nb = ceil_div(T, kSortBlock);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
+  L.off[MOE_WS_IDS] = take(N * 4);
+  L.off[MOE_WS_WEIGHTS] = take(N * 4);
+  L.off[MOE_WS_COUNTS] = take((size_t)E * 4);
+  L.off[MOE_WS_OFFSETS] = take((size_t)(E + 1) * 4);
+  L.mtoff = take((size_t)(E + 1) * 4);
+  L.hist = take((size_t)L.nb * E * 4);
+  L.off[MOE_WS_PERM] = take(N * 4);
+  L.off[MOE_WS_A1_CODES] = take((size_t)T * a1row);
+  L.off[MOE_WS_A1_SCALES] = take((size_t)T * (H / 32));
+  L.off[MOE_WS_A2_CODES] = take(N * a2row);
+  L.off[MOE_WS_A2_SCALES] = take(N * (size_t)(I / 32));
+  L.off[MOE_WS_COMBINE] = take((size_t)T * H * 4);
+  L.total = o;
+  return L;
+}
+
+// Sort-only workspace (moe_sort): histograms and m-tile prefix.
+inline size_t sort_ws_bytes(int T, int E, size_t *hist_off, size_t *mtoff_off) {
+  size_t o = 0;
+  *mtoff_off = o;
+  o = align_up(o + (size_t)(E + 1) * 4, 256);
+  *hist_off = o;
+  o = align_up(o + (size_t)ceil_div(T, kSortBlock) * E * 4, 256);
+  return o;
+}
+
+// ---- launchers (kernels.hip) -----------------------------------------------
+hipError_t launch_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w,
+                        float *comb, int H, hipStream_t s);
+hipError_t launch_sort_hist(const int32_t *ids, int T, int E, int top_k, int32_t *hist, int nb,
+                            hipStream_t s);
+hipError_t launch_sort_scan(int32_t *hist, int nb, int E, int32_t *counts, int32_t *offsets,
+                            int32_t *mtoff, hipStream_t s);
+hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, const int32_t *hist,
+                               int32_t *perm, hipStream_t s);
+hipError_t launch_quant(const uint16_t *x, long rows, int K, int act, uint8_t *codes,
+                        uint8_t *scales, hipStream_t s);
+hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int E, int R, int K,
+                          bool interleave_gate_up, uint8_t *pcodes, uint8_t *pscales,
+                          hipStream_t s);
+struct GemmArgs {
+  int T, top_k, E, H, I, act;
+  long max_mtiles;  // host upper bound of m-tiles (N/16 + E)
+  int num_cus;
+  const uint8_t *a1c, *a1s;
+  uint8_t *a2c, *a2s;
+  const int32_t *perm, *offsets, *mtoff;
+  const float *wts;
+  const uint8_t *w13p, *w13sp, *w2p, *w2sp;
+  float *comb;
+};
+hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s);
+hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s);
+hipError_t launch_finalize(const float *comb, long n, uint16_t *y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,341 @@
+// moe_api.cpp -- the C-ABI of the MoE layer: validation, the handle, the
+// workspace plan and the launch sequence of one forward call.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using namespace moe;
+
+struct moe_layer {
+  int E, H, I;
+  int device;
+  int num_cus;
+  uint8_t *w13p, *w13sp, *w2p, *w2sp;
+  // kernel timing (benchmarks only)
+  bool profiling;
+  int prof_max, prof_calls;
+  std::vector<hipEvent_t> events;  // [prof_max][MOE_K_NUM + 1]
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status hip_fail(hipError_t e, const char *what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool bad_dims(int E, int H, int I, std::string *why) {
+  char b[160];
+  if (E < 1 || E > 1024) { snprintf(b, sizeof b, "E=%d outside [1, 1024]", E); *why = b; return true; }
+  if (H <= 0 || H % 128) { snprintf(b, sizeof b, "H=%d is not a positive multiple of 128", H); *why = b; return true; }
+  if (I <= 0 || I % 128) { snprintf(b, sizeof b, "I=%d is not a positive multiple of 128", I); *why = b; return true; }
+  if (H > (1 << 16) || I > (1 << 16)) { snprintf(b, sizeof b, "H=%d or I=%d above 65536", H, I); *why = b; return true; }
+  return false;
+}
+
+bool misaligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+moe_status check_call(moe_layer_t L, int T, int top_k, int act) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "null layer handle");
+  if (T < 0 || T > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, 2^20]", T);
+  const int kmax = L->E < 8 ? L->E : 8;
+  if (top_k < 1 || top_k > kmax)
+    return fail(MOE_ERR_INVALID_ARG, "top_k=%d outside [1, %d]", top_k, kmax);
+  if (act != MOE_ACT_MXFP8_E4M3 && act != MOE_ACT_MXFP4_E2M1)
+    return fail(MOE_ERR_INVALID_ARG, "unknown activation dtype %d", act);
+  return MOE_OK;
+}
+
+// Device in use must be gfx950 and must be the handle's device.
+moe_status check_device(int *dev_out, int *cus_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  if (dev_out) *dev_out = dev;
+  if (cus_out) *cus_out = prop.multiProcessorCount;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_OOM: return "MOE_ERR_OOM";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_prepare_weights(int E, int H, int I, const void *w13, const void *w13_scale,
+                               const void *w2, const void *w2_scale, hipStream_t s,
+                               moe_layer_t *out) {
+  std::string why;
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "null output handle pointer");
+  *out = nullptr;
+  if (bad_dims(E, H, I, &why)) return fail(MOE_ERR_INVALID_ARG, "%s", why.c_str());
+  if (!w13 || !w13_scale || !w2 || !w2_scale) return fail(MOE_ERR_INVALID_ARG, "null weight pointer");
+  if (misaligned(w13, 16) || misaligned(w2, 16))
+    return fail(MOE_ERR_INVALID_ARG, "weight code buffers must be 16-byte aligned");
+  int dev = 0, cus = 0;
+  moe_status st = check_device(&dev, &cus);
+  if (st != MOE_OK) return st;
+
+  const PackDims d13 = pack_dims(2 * I, H), d2 = pack_dims(H, I);
+  moe_layer *L = new moe_layer();
+  L->E = E; L->H = H; L->I = I; L->device = dev; L->num_cus = cus;
+  L->profiling = false; L->prof_max = 0; L->prof_calls = 0;
+  const size_t b13 = (size_t)E * d13.code_bytes(), s13 = (size_t)E * d13.scale_bytes();
+  const size_t b2 = (size_t)E * d2.code_bytes(), s2 = (size_t)E * d2.scale_bytes();
+  hipError_t e = hipMalloc(&L->w13p, b13);
+  if (e == hipSuccess) e = hipMalloc(&L->w13sp, s13);
+  if (e == hipSuccess) e = hipMalloc(&L->w2p, b2);
+  if (e == hipSuccess) e = hipMalloc(&L->w2sp, s2);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    moe_destroy(L);
+    return fail(MOE_ERR_OOM, "hipMalloc of %zu bytes of packed weights failed",
+                b13 + s13 + b2 + s2);
+  }
+  e = launch_prepack(static_cast<const uint8_t *>(w13), static_cast<const uint8_t *>(w13_scale),
+                     E, 2 * I, H, true, L->w13p, L->w13sp, s);
+  if (e == hipSuccess)
+    e = launch_prepack(static_cast<const uint8_t *>(w2), static_cast<const uint8_t *>(w2_scale),
+                       E, H, I, false, L->w2p, L->w2sp, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    moe_destroy(L);
+    return hip_fail(e, "weight repack");
+  }
+  *out = L;
+  return MOE_OK;
+}
+
+void moe_destroy(moe_layer_t L) {
+  if (!L) return;
+  (void)hipDeviceSynchronize();
+  for (hipEvent_t ev : L->events) (void)hipEventDestroy(ev);
+  if (L->w13p) (void)hipFree(L->w13p);
+  if (L->w13sp) (void)hipFree(L->w13sp);
+  if (L->w2p) (void)hipFree(L->w2p);
+  if (L->w2sp) (void)hipFree(L->w2sp);
+  delete L;
+}
+
+size_t moe_workspace_bytes(moe_layer_t L, int T, int top_k, moe_act_dtype act) {
+  if (check_call(L, T, top_k, act) != MOE_OK) return 0;
+  return ws_layout(T, top_k, L->E, L->H, L->I, act).total;
+}
+
+moe_status moe_workspace_offsets(moe_layer_t L, int T, int top_k, moe_act_dtype act,
+                                 size_t *offs) {
+  moe_status st = check_call(L, T, top_k, act);
+  if (st != MOE_OK) return st;
+  if (!offs) return fail(MOE_ERR_INVALID_ARG, "null offsets array");
+  const WsLayout W = ws_layout(T, top_k, L->E, L->H, L->I, act);
+  for (int i = 0; i < MOE_WS_NUM; ++i) offs[i] = W.off[i];
+  return MOE_OK;
+}
+
+moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T, int top_k,
+                       moe_act_dtype act, void *y, void *ws, size_t ws_bytes, hipStream_t s) {
+  moe_status st = check_call(L, T, top_k, act);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !logits || !y || !ws) return fail(MOE_ERR_INVALID_ARG, "null data pointer");
+  if (misaligned(x, 16) || misaligned(y, 16) || misaligned(logits, 4))
+    return fail(MOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned, logits 4-byte aligned");
+  if (misaligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (x == y) return fail(MOE_ERR_INVALID_ARG, "y must not alias x");
+  const WsLayout W = ws_layout(T, top_k, L->E, L->H, L->I, act);
+  if (ws_bytes < W.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
+
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  int32_t *ids = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_IDS]);
+  float *wts = reinterpret_cast<float *>(base + W.off[MOE_WS_WEIGHTS]);
+  int32_t *counts = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_COUNTS]);
+  int32_t *offsets = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_OFFSETS]);
+  int32_t *mtoff = reinterpret_cast<int32_t *>(base + W.mtoff);
+  int32_t *hist = reinterpret_cast<int32_t *>(base + W.hist);
+  int32_t *perm = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_PERM]);
+  uint8_t *a1c = base + W.off[MOE_WS_A1_CODES];
+  uint8_t *a1s = base + W.off[MOE_WS_A1_SCALES];
+  uint8_t *a2c = base + W.off[MOE_WS_A2_CODES];
+  uint8_t *a2s = base + W.off[MOE_WS_A2_SCALES];
+  float *comb = reinterpret_cast<float *>(base + W.off[MOE_WS_COMBINE]);
+
+  GemmArgs g{};
+  g.T = T; g.top_k = top_k; g.E = L->E; g.H = L->H; g.I = L->I; g.act = act;
+  g.max_mtiles = ((long)T * top_k + kMTile - 1) / kMTile + L->E;
+  g.num_cus = L->num_cus;
+  g.a1c = a1c; g.a1s = a1s; g.a2c = a2c; g.a2s = a2s;
+  g.perm = perm; g.offsets = offsets; g.mtoff = mtoff; g.wts = wts;
+  g.w13p = L->w13p; g.w13sp = L->w13sp; g.w2p = L->w2p; g.w2sp = L->w2sp;
+  g.comb = comb;
+
+  const bool prof = L->profiling && L->prof_calls < L->prof_max;
+  hipEvent_t *ev = prof ? &L->events[(size_t)L->prof_calls * (MOE_K_NUM + 1)] : nullptr;
+  int stage = 0;
+  hipError_t e = hipSuccess;
+  auto mark = [&]() {
+    if (prof && e == hipSuccess) e = hipEventRecord(ev[stage], s);
+    ++stage;
+  };
+  mark();
+  if (e == hipSuccess) e = launch_route(logits, T, L->E, top_k, ids, wts, comb, L->H, s);
+  mark();
+  if (e == hipSuccess) e = launch_sort_hist(ids, T, L->E, top_k, hist, W.nb, s);
+  mark();
+  if (e == hipSuccess) e = launch_sort_scan(hist, W.nb, L->E, counts, offsets, mtoff, s);
+  mark();
+  if (e == hipSuccess) e = launch_sort_scatter(ids, T, L->E, top_k, hist, perm, s);
+  mark();
+  if (e == hipSuccess)
+    e = launch_quant(static_cast<const uint16_t *>(x), T, L->H, act, a1c, a1s, s);
+  mark();
+  if (e == hipSuccess) e = launch_gemm1(g, s);
+  mark();
+  if (e == hipSuccess) e = launch_gemm2(g, s);
+  mark();
+  if (e == hipSuccess) e = launch_finalize(comb, (long)T * L->H, static_cast<uint16_t *>(y), s);
+  mark();
+  if (e != hipSuccess) return hip_fail(e, "moe_forward launch");
+  if (prof) ++L->prof_calls;
+  return MOE_OK;
+}
+
+moe_status moe_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w,
+                     hipStream_t s) {
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "E=%d outside [1, 1024]", E);
+  const int kmax = E < 8 ? E : 8;
+  if (top_k < 1 || top_k > kmax) return fail(MOE_ERR_INVALID_ARG, "top_k=%d outside [1, %d]", top_k, kmax);
+  if (T < 0 || T > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, 2^20]", T);
+  if (T == 0) return MOE_OK;
+  if (!logits || !ids || !w) return fail(MOE_ERR_INVALID_ARG, "null data pointer");
+  moe_status st = check_device(nullptr, nullptr);
+  if (st != MOE_OK) return st;
+  hipError_t e = launch_route(logits, T, E, top_k, ids, w, nullptr, 0, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "route launch");
+}
+
+size_t moe_sort_workspace_bytes(int T, int E) {
+  if (T < 0 || T > (1 << 20) || E < 1 || E > 1024) return 0;
+  size_t h, m;
+  return sort_ws_bytes(T, E, &h, &m);
+}
+
+moe_status moe_sort(const int32_t *ids, int T, int E, int top_k, int32_t *counts,
+                    int32_t *offsets, int32_t *perm, void *ws, size_t ws_bytes, hipStream_t s) {
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID_ARG, "E=%d outside [1, 1024]", E);
+  const int kmax = E < 8 ? E : 8;
+  if (top_k < 1 || top_k > kmax) return fail(MOE_ERR_INVALID_ARG, "top_k=%d outside [1, %d]", top_k, kmax);
+  if (T < 0 || T > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, 2^20]", T);
+  if (!ids || !counts || !offsets || !perm || !ws) return fail(MOE_ERR_INVALID_ARG, "null data pointer");
+  if (misaligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  size_t hist_off, mtoff_off;
+  const size_t need = sort_ws_bytes(T, E, &hist_off, &mtoff_off);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  moe_status st = check_device(nullptr, nullptr);
+  if (st != MOE_OK) return st;
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  int32_t *hist = reinterpret_cast<int32_t *>(base + hist_off);
+  int32_t *mtoff = reinterpret_cast<int32_t *>(base + mtoff_off);
+  const int nb = ceil_div(T, kSortBlock);
+  hipError_t e = hipSuccess;
+  if (nb > 0) e = launch_sort_hist(ids, T, E, top_k, hist, nb, s);
+  if (e == hipSuccess) e = launch_sort_scan(hist, nb, E, counts, offsets, mtoff, s);
+  if (e == hipSuccess && nb > 0) e = launch_sort_scatter(ids, T, E, top_k, hist, perm, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "sort launch");
+}
+
+moe_status moe_quant_act(const void *x, int T, int H, moe_act_dtype act, uint8_t *codes,
+                         uint8_t *scales, hipStream_t s) {
+  if (T < 0 || T > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, 2^20]", T);
+  if (H <= 0 || H % 128) return fail(MOE_ERR_INVALID_ARG, "H=%d is not a positive multiple of 128", H);
+  if (act != MOE_ACT_MXFP8_E4M3 && act != MOE_ACT_MXFP4_E2M1)
+    return fail(MOE_ERR_INVALID_ARG, "unknown activation dtype %d", act);
+  if (T == 0) return MOE_OK;
+  if (!x || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "null data pointer");
+  if (misaligned(x, 16) || misaligned(codes, 16))
+    return fail(MOE_ERR_INVALID_ARG, "x and codes must be 16-byte aligned");
+  moe_status st = check_device(nullptr, nullptr);
+  if (st != MOE_OK) return st;
+  hipError_t e = launch_quant(static_cast<const uint16_t *>(x), T, H, act, codes, scales, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "quant launch");
+}
+
+moe_status moe_profile_enable(moe_layer_t L, int enable, int max_calls) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "null layer handle");
+  if (enable && (max_calls < 1 || max_calls > 100000))
+    return fail(MOE_ERR_INVALID_ARG, "max_calls=%d outside [1, 100000]", max_calls);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  for (hipEvent_t ev : L->events) (void)hipEventDestroy(ev);
+  L->events.clear();
+  L->profiling = false;
+  L->prof_calls = 0;
+  L->prof_max = 0;
+  if (!enable) return MOE_OK;
+  L->events.resize((size_t)max_calls * (MOE_K_NUM + 1));
+  for (size_t i = 0; i < L->events.size(); ++i) {
+    e = hipEventCreate(&L->events[i]);
+    if (e != hipSuccess) {
+      for (size_t k = 0; k < i; ++k) (void)hipEventDestroy(L->events[k]);
+      L->events.clear();
+      return hip_fail(e, "hipEventCreate");
+    }
+  }
+  L->prof_max = max_calls;
+  L->profiling = true;
+  return MOE_OK;
+}
+
+moe_status moe_profile_read(moe_layer_t L, float *ms, int *ncalls) {
+  if (!L || !ms || !ncalls) return fail(MOE_ERR_INVALID_ARG, "null argument");
+  for (int k = 0; k < MOE_K_NUM; ++k) ms[k] = 0.0f;
+  *ncalls = L->prof_calls;
+  for (int c = 0; c < L->prof_calls; ++c) {
+    hipEvent_t *ev = &L->events[(size_t)c * (MOE_K_NUM + 1)];
+    hipError_t e = hipEventSynchronize(ev[MOE_K_NUM]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    for (int k = 0; k < MOE_K_NUM; ++k) {
+      float t = 0.0f;
+      e = hipEventElapsedTime(&t, ev[k], ev[k + 1]);
+      if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+      ms[k] += t;
+    }
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

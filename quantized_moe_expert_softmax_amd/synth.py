@@ -160,3 +160,37 @@ for _I in (640, 1152):
     for _E, _k in ((384, 6), (128, 3)):
         _n = "v41flash_i%d_e%d" % (_I, _E)
         WORKLOADS[_n] = Workload(_n, 5120, _I, _E, _k, MXFP8, _FLASH_TS, seed=5)
+
+
+def device_weights(H: int, I: int, E: int, seed: int = 0, device="cuda", chunk: int = 8):
+    """Canonical MXFP4 weights of a whole (H, I, E) expert set, drawn on the GPU.
+
+    Same code and scale distributions as expert_weights(), drawn with torch's
+    seeded device generator (much faster for the 13.5 GB expert sets; the
+    values differ from the numpy path).  Returns uint8 device tensors
+    w13 [E, 2I, H/2], w13s [E, 2I, H/32], w2 [E, H, I/2], w2s [E, H, I/32].
+    """
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((0x3E7 * 1000003 + H * 7919 + I * 104729 + E * 1299709 + seed) % (2 ** 62))
+    pair = torch.from_numpy(_PAIR).to(device)
+    s13 = torch.from_numpy(_scale_table(H)).to(device)
+    s2 = torch.from_numpy(_scale_table(I)).to(device)
+    w13 = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=device)
+    w13s = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=device)
+    w2 = torch.empty((E, H, I // 2), dtype=torch.uint8, device=device)
+    w2s = torch.empty((E, H, I // 32), dtype=torch.uint8, device=device)
+
+    def fill(dst, table, hi):
+        flat = dst.view(-1)
+        per = dst[0].numel()
+        for e0 in range(0, E, chunk):
+            n = min(chunk, E - e0) * per
+            raw = torch.randint(0, hi, (n,), generator=g, device=device, dtype=torch.int64)
+            flat[e0 * per:e0 * per + n] = table[raw]
+
+    fill(w13, pair, 65536)
+    fill(w13s, s13, 256)
+    fill(w2, pair, 65536)
+    fill(w2s, s2, 256)
+    return w13, w13s, w2, w2s
