@@ -1,0 +1,110 @@
+"""GPU parity at the benchmarked full sizes, in the launch configuration the
+benchmark times (one moe_forward call over the whole batch).
+
+On every row: routing ids, counts/offsets and the expert permutation, and the
+first-stage codes and scales are compared bit-exact with the oracle.  The
+BF16 output is compared on sampled rows (the oracle evaluates one token in
+about a second at 7168/3072): the first and last token, the first and last
+token routed to the most loaded expert, a token of the least loaded
+non-empty expert and a few random tokens.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_moe_expert_softmax_amd as moe
+from quantized_moe_expert_softmax_amd import synth
+from tests.gpu_util import (ROUTE_ULP_TOL, assert_output_close, bf16_dev, bf16_host_bits, dev,
+                            ulp_diff, ws_view)
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def _shape(wl):
+    key = (wl.H, wl.I, wl.E, wl.seed)
+    if key not in _cache:
+        import torch
+        for k in list(_cache):  # keep one expert set resident at a time
+            _cache.pop(k)[1].close()
+        torch.cuda.empty_cache()
+        w = synth.device_weights(wl.H, wl.I, wl.E, wl.seed)
+        layer = moe.moe_prepare_weights(wl.E, wl.H, wl.I, *w)
+        _cache[key] = (w, layer)
+    return _cache[key]
+
+
+def sample_rows(ids, E, n_random=2, seed=0):
+    T = ids.shape[0]
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    hot = int(np.argmax(counts))
+    nz = np.where(counts > 0)[0]
+    cold = int(nz[np.argmin(counts[nz])])
+    hot_tokens = np.where((ids == hot).any(axis=1))[0]
+    cold_tokens = np.where((ids == cold).any(axis=1))[0]
+    rows = [0, T - 1, hot_tokens[0], hot_tokens[-1], cold_tokens[0]]
+    rows += list(np.random.default_rng(seed).integers(0, T, n_random))
+    return sorted(set(int(r) for r in rows))
+
+
+def run_case(name, T, act=None, n_random=2):
+    import torch
+    wl = synth.WORKLOADS[name]
+    act = wl.act if act is None else act
+    w, layer = _shape(wl)
+    x = wl.x(T)
+    lg = wl.logits(T)
+    ws = moe.alloc_workspace(layer, T, wl.top_k, act)
+    y = moe.moe_forward(layer, bf16_dev(x), dev(lg), wl.top_k, act, ws=ws)
+    torch.cuda.synchronize()
+    yb = bf16_host_bits(y)
+    N = T * wl.top_k
+    offs = moe.moe_workspace_offsets(layer, T, wl.top_k, act)
+    rid, rw = oracle.route(lg, wl.top_k)
+    assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_IDS, N * 4, np.int32), rid.reshape(-1))
+    assert ulp_diff(ws_view(ws, offs, moe.MOE_WS_WEIGHTS, N * 4, np.float32),
+                    rw.reshape(-1)).max() <= ROUTE_ULP_TOL
+    rc, ro, rp = oracle.sort(rid, wl.E)
+    assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_COUNTS, wl.E * 4, np.int32), rc)
+    assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_OFFSETS, (wl.E + 1) * 4, np.int32), ro)
+    assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_PERM, N * 4, np.int32), rp)
+    a1row = wl.H if act == 0 else wl.H // 2
+    xc, xs = oracle.mx_quantize_bf16(x, act)
+    assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_A1_CODES, T * a1row).reshape(T, -1), xc)
+    assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_A1_SCALES, T * (wl.H // 32)).reshape(T, -1),
+                          xs)
+    rows = sample_rows(rid, wl.E, n_random=n_random, seed=T)
+    wcache = {}
+
+    def wfor(e):
+        if e not in wcache:
+            wcache[e] = tuple(a[e].cpu().numpy() for a in w)
+        return wcache[e]
+    ref = oracle.forward_rows(x, lg, rows, wfor, wl.top_k, act)
+    rel, row = assert_output_close(yb[rows], ref, "%s T=%d act=%d rows=%s" % (name, T, act, rows))
+    print("%s T=%d act=%d rows=%d rel=%.2e max_row=%.2e" % (name, T, act, len(rows), rel, row))
+
+
+@pytest.mark.parametrize("T", [1, 2, 8, 64])
+def test_v4pro_decode(T):
+    run_case("v4pro_decode", T)
+
+
+@pytest.mark.parametrize("name,T", [("v4pro_prefill", 512), ("v4pro_prefill", 8192),
+                                    ("v4pro_prefill_skewed", 4096),
+                                    ("v4pro_prefill_skewed", 8192)])
+def test_v4pro_prefill(name, T):
+    run_case(name, T)
+
+
+@pytest.mark.parametrize("T", [1, 64, 1024, 16384])
+def test_v4pro_a4w4(T):
+    run_case("v4pro_a4w4", T, n_random=1)
+
+
+@pytest.mark.parametrize("name,T", [("v41flash_i640_e384", 1), ("v41flash_i640_e384", 4096),
+                                    ("v41flash_i1152_e384", 32768), ("v41flash_i640_e128", 256),
+                                    ("v41flash_i1152_e128", 32768), ("v41flash_i1152_e128", 2)])
+def test_v41flash(name, T):
+    run_case(name, T, n_random=3)
