@@ -15,7 +15,8 @@
  *   4. GEMM1 against the MXFP4 gate/up weights of each assignment's expert,
  *      SwiGLU h = silu(gate) * up, h re-quantised to the activation format;
  *   5. GEMM2 against the MXFP4 down weights, each row scaled by its routing
- *      weight and accumulated over the top_k slots in FP32; output BF16.
+ *      weight; the top_k rows of a token summed in FP32 in slot order and
+ *      rounded once to BF16.
  *
  * Conventions (all calls):
  *   - Every pointer argument is a DEVICE pointer on the current HIP device
@@ -126,7 +127,9 @@ typedef enum {
     MOE_WS_A2_CODES,    /* [T*top_k][I] or [..][I/2] SwiGLU codes, row p is
                            the assignment perm[p]                           */
     MOE_WS_A2_SCALES,   /* [T*top_k][I/32] E8M0, same rows                   */
-    MOE_WS_COMBINE,     /* [T][H] fp32 weighted top-k sums                   */
+    MOE_WS_ROWS,        /* [T*top_k][H] fp32 GEMM2 rows times their routing
+                           weight, row p is the assignment perm[p]         */
+    MOE_WS_SLOT,        /* [T*top_k] int32: row of assignment a in perm    */
     MOE_WS_NUM
 } moe_ws_region;
 
@@ -145,8 +148,8 @@ moe_status moe_workspace_offsets(moe_layer_t layer, int T, int top_k, moe_act_dt
 moe_status moe_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w,
                      hipStream_t s);
 
-/* Workspace bytes moe_sort needs for (T, E). */
-size_t moe_sort_workspace_bytes(int T, int E);
+/* Workspace bytes moe_sort needs for (T, E, top_k). */
+size_t moe_sort_workspace_bytes(int T, int E, int top_k);
 
 /* Step 2 (FlyDSL #972 Technical Details: dispatch).  ids [T][top_k] int32 ->
  * counts [E], offsets [E+1] (exclusive prefix sum), perm [T*top_k]: the flat
@@ -169,7 +172,7 @@ moe_status moe_quant_act(const void *x, int T, int H, moe_act_dtype act, uint8_t
 /* Kernels moe_forward launches, in order. */
 typedef enum {
     MOE_K_ROUTE = 0, MOE_K_SORT_HIST, MOE_K_SORT_SCAN, MOE_K_SORT_SCATTER, MOE_K_QUANT,
-    MOE_K_GEMM1, MOE_K_GEMM2, MOE_K_FINALIZE, MOE_K_NUM
+    MOE_K_GEMM1, MOE_K_GEMM2, MOE_K_COMBINE, MOE_K_NUM
 } moe_kernel_id;
 
 /* When enabled, each moe_forward records HIP events around every kernel on

@@ -32,10 +32,11 @@ MOE_ACT_MXFP8_E4M3 = 0  # A8W4
 MOE_ACT_MXFP4_E2M1 = 1  # A4W4
 
 (MOE_WS_IDS, MOE_WS_WEIGHTS, MOE_WS_COUNTS, MOE_WS_OFFSETS, MOE_WS_PERM, MOE_WS_A1_CODES,
- MOE_WS_A1_SCALES, MOE_WS_A2_CODES, MOE_WS_A2_SCALES, MOE_WS_COMBINE, MOE_WS_NUM) = range(11)
+ MOE_WS_A1_SCALES, MOE_WS_A2_CODES, MOE_WS_A2_SCALES, MOE_WS_ROWS, MOE_WS_SLOT,
+ MOE_WS_NUM) = range(12)
 
 KERNELS = ("route", "sort_hist", "sort_scan", "sort_scatter", "quant", "gemm1", "gemm2",
-           "finalize")
+           "combine")
 MOE_K_NUM = len(KERNELS)
 
 EXPORTS = ("moe_prepare_weights", "moe_destroy", "moe_workspace_bytes", "moe_forward",
@@ -73,7 +74,7 @@ def load_library(path: str = LIB_PATH):
         lib.moe_forward.argtypes = [P, P, P, I, I, I, P, P, Z, P]
         lib.moe_workspace_offsets.argtypes = [P, I, I, I, P]
         lib.moe_route.argtypes = [P, I, I, I, P, P, P]
-        lib.moe_sort_workspace_bytes.argtypes = [I, I]
+        lib.moe_sort_workspace_bytes.argtypes = [I, I, I]
         lib.moe_sort_workspace_bytes.restype = Z
         lib.moe_sort.argtypes = [P, I, I, I, P, P, P, P, Z, P]
         lib.moe_quant_act.argtypes = [P, I, I, I, P, P, P]
@@ -130,9 +131,10 @@ class MoeLayer:
         self.close()
 
     def close(self):
-        if getattr(self, "handle", None):
-            load_library().moe_destroy(self.handle)
-            self.handle = None
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            _lib.moe_destroy(h)
+        self.handle = None
 
 
 def moe_prepare_weights(E, H, I, w13, w13_scale, w2, w2_scale, stream=None) -> MoeLayer:
@@ -211,7 +213,7 @@ def moe_sort(ids, E: int, stream=None):
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
-    n = lib.moe_sort_workspace_bytes(T, E)
+    n = lib.moe_sort_workspace_bytes(T, E, k)
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
     _check(lib.moe_sort(_ptr(ids), T, E, k, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(ws),
                         ws.numel(), _stream(stream)))

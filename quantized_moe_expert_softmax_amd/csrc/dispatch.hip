@@ -15,14 +15,12 @@ namespace moe {
 // wave-wide arg-max (larger logit first, equal logits by lower index) pick
 // the experts; the weights are exp(l_j - max) normalised over the picks,
 // which equals the full softmax renormalised over the picks (the softmax
-// denominator over all E cancels).  The wave also
-// zeroes the token's FP32 combine row, which GEMM2 accumulates into.
+// denominator over all E cancels).
 // ---------------------------------------------------------------------------
 template <int NV>
 __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ logits, int T, int E,
                                                     int top_k, int32_t *__restrict__ ids,
-                                                    float *__restrict__ wts,
-                                                    float *__restrict__ comb, int H) {
+                                                    float *__restrict__ wts) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long t = (long)blockIdx.x * 4 + wave;
   if (t >= T) return;  // wave-uniform; no barriers below
@@ -32,10 +30,6 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ lo
   for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
     v[i] = e < E ? row[e] : 0.0f;
-  }
-  if (comb) {
-    float4 *c = reinterpret_cast<float4 *>(comb + t * (long)H);
-    for (int i = lane; i < H / 4; i += 64) c[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   uint32_t taken = 0;
   float selv[8];
@@ -95,13 +89,13 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ lo
 }
 
 hipError_t launch_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w,
-                        float *comb, int H, hipStream_t s) {
+                        hipStream_t s) {
   if (T == 0) return hipSuccess;
   const dim3 grid((unsigned)ceil_div(T, 4)), block(256);
   const int nv = ceil_div(E, 64);
 #define ROUTE_CASE(NV_)                                                                   \
   case NV_:                                                                               \
-    route_kernel<NV_><<<grid, block, 0, s>>>(logits, T, E, top_k, ids, w, comb, H);       \
+    route_kernel<NV_><<<grid, block, 0, s>>>(logits, T, E, top_k, ids, w);                \
     break;
   switch (nv) {
     ROUTE_CASE(1) ROUTE_CASE(2) ROUTE_CASE(3) ROUTE_CASE(4) ROUTE_CASE(5) ROUTE_CASE(6)
@@ -120,8 +114,9 @@ hipError_t launch_route(const float *logits, int T, int E, int top_k, int32_t *i
 // on one device the experts all live here, so dispatch is a permutation).
 //   hist:    per 256-token block, the number of assignments of each expert
 //   scan:    per expert, exclusive prefix over blocks -> block bases; counts,
-//            offsets (exclusive prefix over experts) and the prefix of
-//            16-row m-tiles per expert that the GEMMs schedule from
+//            offsets (exclusive prefix over experts), the prefix of bm-row
+//            m-blocks per expert and the expert of every m-block, which the
+//            GEMMs schedule from
 //   scatter: within a block, the rank of a token among the tokens routed to
 //            the same expert comes from 64-bit per-wave masks (LDS atomic
 //            OR is order-free; popcount of the lanes below gives the rank),
@@ -148,7 +143,8 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restric
 __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ hist, int nb, int E,
                                                          int32_t *__restrict__ counts,
                                                          int32_t *__restrict__ offsets,
-                                                         int32_t *__restrict__ mtoff) {
+                                                         int32_t *__restrict__ mtoff,
+                                                         int32_t *__restrict__ mbexp, int bm) {
   __shared__ int32_t sc[1024];
   __shared__ int32_t sm[1024];
   const int e = threadIdx.x;
@@ -162,7 +158,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ h
     counts[e] = run;
   }
   const int c = e < E ? run : 0;
-  const int m = e < E ? (run + kMTile - 1) / kMTile : 0;
+  const int m = e < E ? (run + bm - 1) / bm : 0;
   sc[e] = c;
   sm[e] = m;
   __syncthreads();
@@ -183,13 +179,16 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ h
       mtoff[E] = sm[e];
     }
     for (int b = 0; b < nb; ++b) hist[(long)b * E + e] += base;
+    const int mb0 = sm[e] - m;
+    for (int i = 0; i < m; ++i) mbexp[mb0 + i] = e;
   }
 }
 
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__restrict__ ids, int T,
                                                            int E, int top_k,
                                                            const int32_t *__restrict__ base,
-                                                           int32_t *__restrict__ perm) {
+                                                           int32_t *__restrict__ perm,
+                                                           int32_t *__restrict__ inv) {
   extern __shared__ unsigned long long masks[];  // [4 waves][E]
   for (int i = threadIdx.x; i < 4 * E; i += 256) masks[i] = 0ull;
   __syncthreads();
@@ -209,7 +208,9 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
       if (e >= (uint32_t)E) continue;
       int r = __popcll(masks[wave * E + e] & (bit - 1ull));
       for (int w = 0; w < wave; ++w) r += __popcll(masks[w * E + e]);
-      perm[base[(long)blockIdx.x * E + e] + r] = (int32_t)(t * top_k + j);
+      const int32_t pos = base[(long)blockIdx.x * E + e] + r;
+      perm[pos] = (int32_t)(t * top_k + j);
+      inv[t * top_k + j] = pos;
     }
   }
 }
@@ -221,15 +222,15 @@ hipError_t launch_sort_hist(const int32_t *ids, int T, int E, int top_k, int32_t
 }
 
 hipError_t launch_sort_scan(int32_t *hist, int nb, int E, int32_t *counts, int32_t *offsets,
-                            int32_t *mtoff, hipStream_t s) {
-  sort_scan_kernel<<<1, 1024, 0, s>>>(hist, nb, E, counts, offsets, mtoff);
+                            int32_t *mtoff, int32_t *mbexp, int bm, hipStream_t s) {
+  sort_scan_kernel<<<1, 1024, 0, s>>>(hist, nb, E, counts, offsets, mtoff, mbexp, bm);
   return hipGetLastError();
 }
 
 hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, const int32_t *hist,
-                               int32_t *perm, hipStream_t s) {
+                               int32_t *perm, int32_t *inv, hipStream_t s) {
   const int nb = ceil_div(T, kSortBlock);
-  sort_scatter_kernel<<<nb, 256, (size_t)E * 4 * 8, s>>>(ids, T, E, top_k, hist, perm);
+  sort_scatter_kernel<<<nb, 256, (size_t)E * 4 * 8, s>>>(ids, T, E, top_k, hist, perm, inv);
   return hipGetLastError();
 }
 
@@ -378,26 +379,41 @@ hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int E, in
 }
 
 // ---------------------------------------------------------------------------
-// Finalize: y = bf16(combine), round to nearest even; 8 elements per thread.
+// Combine ("add A4W4 and FP8 P2P transport support to MegaMoE", Technical
+// Details: accumulate the top-k contributions in FP32): y[t] = bf16 of the
+// FP32 sum, in slot order j = 0..top_k-1, of the weighted GEMM2 rows of the
+// token's assignments (row inv[t*top_k + j]), rounded once to nearest even.
+// One thread per 8 outputs.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__ comb, long n8,
-                                                       uint16_t *__restrict__ y) {
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ rows,
+                                                      const int32_t *__restrict__ inv, long n8,
+                                                      int H, int top_k,
+                                                      uint16_t *__restrict__ y) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
-  const float4 a = reinterpret_cast<const float4 *>(comb)[2 * i];
-  const float4 b = reinterpret_cast<const float4 *>(comb)[2 * i + 1];
+  const long t = i / (H / 8);
+  const int h = (int)(i % (H / 8)) * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < top_k; ++j) {
+    const float *r = rows + (size_t)inv[t * top_k + j] * H + h;
+    const float4 a = reinterpret_cast<const float4 *>(r)[0];
+    const float4 b = reinterpret_cast<const float4 *>(r)[1];
+    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  }
   uint4 o;
-  o.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
-  o.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
-  o.z = (uint32_t)f32_to_bf16(b.x) | ((uint32_t)f32_to_bf16(b.y) << 16);
-  o.w = (uint32_t)f32_to_bf16(b.z) | ((uint32_t)f32_to_bf16(b.w) << 16);
+  o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+  o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+  o.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+  o.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
   reinterpret_cast<uint4 *>(y)[i] = o;
 }
 
-hipError_t launch_finalize(const float *comb, long n, uint16_t *y, hipStream_t s) {
-  const long n8 = n / 8;
+hipError_t launch_combine(const float *rows, const int32_t *inv, int T, int H, int top_k,
+                          uint16_t *y, hipStream_t s) {
+  const long n8 = (long)T * H / 8;
   if (n8 == 0) return hipSuccess;
-  finalize_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(comb, n8, y);
+  combine_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(rows, inv, n8, H, top_k, y);
   return hipGetLastError();
 }
 

@@ -9,8 +9,8 @@
 //
 // GEMM2 (same page: FP4xFP4 GEMM2, weighted rows, FP32 accumulation of the
 // top-k contributions): per expert, the A2 rows times the MXFP4 down rows,
-// each output row scaled by its routing weight and added atomically into the
-// FP32 combine buffer of its token.
+// each output row scaled by its routing weight and stored as an FP32 row in
+// sorted order; the combine kernel sums a token's top-k rows.
 //
 // Both use the gfx950 block-scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4
 // (A = activations, E4M3 or E2M1; B = weights, E2M1; one E8M0 scale per lane
@@ -21,12 +21,16 @@
 //   scale:        lane l gives the scale of row l%16, K block l/16
 //   result:       lane l, register r holds row 4*(l/16) + r, column l%16
 //
-// Work is scheduled persistently: a work item is one 16-row m-tile of one
-// expert (from the sort's m-tile prefix) times one 64-row weight block; the
-// four waves of a workgroup split the K steps and reduce in LDS.  Padded rows
-// of a partial m-tile load a valid row and never store (padding guard).
+// Two variants, chosen per call from the rows per expert.  Stream (decode):
+// a work item is one 16-row m-tile of one expert times one 64-row weight
+// block; the four waves of a workgroup split the K steps and reduce in LDS.
+// Tiled (prefill): see below.  Both schedule persistently from the sort's
+// m-block table; padded rows of a partial m-block load a valid row and never
+// store (padding guard).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "internal.h"
 #include "mx_device.h"
@@ -35,30 +39,21 @@ namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct KArgs {
   int T, top_k, E, H, I;
   const uint8_t *a1c, *a1s;
   uint8_t *a2c, *a2s;
-  const int32_t *perm, *offsets, *mtoff;
+  const int32_t *perm, *offsets, *mtoff, *mbexp;
   const float *wts;
   const uint8_t *wp;
   const uint32_t *wsp;
-  float *comb;
+  float *rows;  // [N][H] weighted GEMM2 rows (sorted order)
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Expert owning global m-tile mt: the largest e with mtoff[e] <= mt.
-__device__ __forceinline__ int find_expert(const int32_t *__restrict__ mtoff, int E, int mt) {
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (uniform(mtoff[mid]) <= mt) lo = mid;
-    else hi = mid;
-  }
-  return lo;
-}
 
 // A operand of K step s for lane group g from a row-major code row.
 template <int FMT>
@@ -111,7 +106,55 @@ __device__ __forceinline__ void mma_4tiles(v4f acc[4], const uint8_t *__restrict
   }
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + exp(-g)) with the hardware exp2 and reciprocal; for very
+// negative g the exponential overflows to inf and silu goes to (-)0.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// Cross-lane moves within 16-lane rows (DPP, no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+// maximum over the 16 lanes of a row: quad_perm [1,0,3,2], [2,3,0,1], then
+// row_half_mirror and row_mirror
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, dpp<0xB1>(v));
+  v = max(v, dpp<0x4E>(v));
+  v = max(v, dpp<0x141>(v));
+  v = max(v, dpp<0x140>(v));
+  return v;
+}
+
+// GEMM1 epilogue for one accumulator register r: lane c = l%16 of row group
+// l/16 holds gate/up columns 32j + c (lo) and 32j + 16 + c (hi) of one token
+// row; h = silu(gate) * up; the 32 h values of the row form one 1x32 block
+// (amax over the 16 lanes), requantised and stored to the A2 row (all lanes
+// must call; only `valid` rows store).
+template <class F, int FMT>
+__device__ __forceinline__ void swiglu_requant(float glo, float ghi, float ulo, float uhi,
+                                               bool valid, uint8_t *__restrict__ a2row,
+                                               uint8_t *__restrict__ a2srow, int j, int c) {
+  const float hlo = silu(glo) * ulo;
+  const float hhi = silu(ghi) * uhi;
+  const uint32_t am = row16_max(max(f32_bits(hlo) & 0x7fffffffu, f32_bits(hhi) & 0x7fffffffu));
+  const int X = block_exponent<F>(am);
+  const uint32_t clo = encode_element<F>(f32_bits(hlo), X);
+  const uint32_t chi = encode_element<F>(f32_bits(hhi), X);
+  const uint32_t plo = dpp<0xB1>(clo);  // code of lane c ^ 1
+  const uint32_t phi = dpp<0xB1>(chi);
+  if (valid) {
+    if (FMT == 0) {
+      a2row[32 * j + c] = (uint8_t)clo;
+      a2row[32 * j + 16 + c] = (uint8_t)chi;
+    } else if ((c & 1) == 0) {
+      a2row[16 * j + c / 2] = (uint8_t)(clo | (plo << 4));
+      a2row[16 * j + 8 + c / 2] = (uint8_t)(chi | (phi << 4));
+    }
+    if (c == 0) a2srow[j] = (uint8_t)(X + 127);
+  }
+}
 
 template <int FMT>
 struct ActFmt;
@@ -136,7 +179,7 @@ __global__ __launch_bounds__(256) void gemm1_kernel(KArgs p) {
   const size_t tile_bytes = (size_t)S * 1024, tile_dwords = (size_t)G * 64;
   for (long w = blockIdx.x; w < total; w += gridDim.x) {
     const int j = (int)(w / n_mt), mt = (int)(w % n_mt);
-    const int e = find_expert(p.mtoff, p.E, mt);
+    const int e = uniform(p.mbexp[mt]);
     const int row0 = uniform(p.offsets[e]) + kMTile * (mt - uniform(p.mtoff[e]));
     const int nrows = min(kMTile, uniform(p.offsets[e + 1]) - row0);
     const int pr = row0 + min(lane & 15, nrows - 1);
@@ -163,29 +206,10 @@ __global__ __launch_bounds__(256) void gemm1_kernel(KArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // tiles: 0 = gate cols [32j, +16), 1 = gate [32j+16, +16), 2/3 = up
-        const float hlo = silu(v[0 * 4 + r]) * v[2 * 4 + r];
-        const float hhi = silu(v[1 * 4 + r]) * v[3 * 4 + r];
-        uint32_t am = max(f32_bits(hlo) & 0x7fffffffu, f32_bits(hhi) & 0x7fffffffu);
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) am = max(am, (uint32_t)__shfl_xor((int)am, off));
-        const int X = block_exponent<F>(am);
-        const uint32_t clo = encode_element<F>(f32_bits(hlo), X);
-        const uint32_t chi = encode_element<F>(f32_bits(hhi), X);
-        const uint32_t plo = (uint32_t)__shfl_xor((int)clo, 1);
-        const uint32_t phi = (uint32_t)__shfl_xor((int)chi, 1);
         const int m = 4 * (lane >> 4) + r;
-        if (m < nrows) {
-          const size_t prow = (size_t)(row0 + m);
-          uint8_t *dst = p.a2c + prow * a2row;
-          if (FMT == 0) {
-            dst[32 * j + c] = (uint8_t)clo;
-            dst[32 * j + 16 + c] = (uint8_t)chi;
-          } else if ((c & 1) == 0) {
-            dst[16 * j + c / 2] = (uint8_t)(clo | (plo << 4));
-            dst[16 * j + 8 + c / 2] = (uint8_t)(chi | (phi << 4));
-          }
-          if (c == 0) p.a2s[prow * (p.I / 32) + j] = (uint8_t)(X + 127);
-        }
+        const size_t prow = (size_t)(row0 + min(m, nrows - 1));
+        swiglu_requant<F, FMT>(v[0 * 4 + r], v[1 * 4 + r], v[2 * 4 + r], v[3 * 4 + r], m < nrows,
+                               p.a2c + prow * a2row, p.a2s + prow * (p.I / 32), j, c);
       }
     }
     __syncthreads();
@@ -206,7 +230,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(KArgs p) {
   const size_t tile_bytes = (size_t)S * 1024, tile_dwords = (size_t)G * 64;
   for (long w = blockIdx.x; w < total; w += gridDim.x) {
     const int nb = (int)(w / n_mt), mt = (int)(w % n_mt);
-    const int e = find_expert(p.mtoff, p.E, mt);
+    const int e = uniform(p.mbexp[mt]);
     const int row0 = uniform(p.offsets[e]) + kMTile * (mt - uniform(p.mtoff[e]));
     const int nrows = min(kMTile, uniform(p.offsets[e + 1]) - row0);
     const size_t pr = (size_t)(row0 + min(lane & 15, nrows - 1));
@@ -229,15 +253,13 @@ __global__ __launch_bounds__(256) void gemm2_kernel(KArgs p) {
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * (lane >> 4) + r;
         if (m < nrows) {
-          const int a = p.perm[row0 + m];
-          const long t = a / p.top_k;
-          const float wt_a = p.wts[a];
-          float *dst = p.comb + t * (long)p.H + 64 * nb + c;
+          const float wt_a = p.wts[p.perm[row0 + m]];
+          float *dst = p.rows + (size_t)(row0 + m) * p.H + 64 * nb + c;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int i = 4 * q + r;
             const float o = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
-            unsafeAtomicAdd(dst + 16 * q, wt_a * o);
+            dst[16 * q] = wt_a * o;
           }
         }
       }
@@ -246,14 +268,272 @@ __global__ __launch_bounds__(256) void gemm2_kernel(KArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tiled variant (prefill): a work item is (expert e, 256 weight rows, BM =
+// 16*MT token rows).  Wave w owns 64 weight rows (GEMM1: one gate/up unit)
+// and MT x 4 accumulator tiles, so every weight fragment is read from HBM
+// once per item and feeds MT MFMAs; the activation tile of a K step is
+// shared by the four waves.  Every operand of a K step -- the BM activation
+// rows (16-byte chunks XOR-swizzled by row), their E8M0 scales, each wave's
+// four 1 KiB weight fragments and their scale dwords -- is copied from
+// global memory straight into LDS with global_load_lds (no register
+// staging), NS steps deep; the waits count those copies exactly (they are
+// the only vector-memory instructions in the loop and issue in program
+// order).  Items run expert by expert with the m-blocks innermost (the
+// m-blocks of one (expert, weight block) reuse its weights from L2), and the
+// logical workgroup index is remapped so consecutive items share an XCD.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef __attribute__((address_space(1))) void *glb_ptr_t;
+
+// lane i of the wave copies 16 (4) bytes from its own address g to
+// lds_base + 16*i (4*i); lds_base must be wave-uniform
+__device__ __forceinline__ void copy16_to_lds(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void copy4_to_lds(const void *g, void *lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(N), expcnt and lgkmcnt left free (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier for the copy pipeline: LDS reads of this wave done, no
+// wait on the copies still in flight (a __syncthreads would wait for all of
+// them, since they write LDS).
+__device__ __forceinline__ void barrier_keep_copies() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
+  __builtin_amdgcn_s_barrier();
+}
+template <int FMT, int MT>
+struct TileShape {
+  static constexpr int BM = 16 * MT;
+  static constexpr int ROWB = FMT == 0 ? 128 : 64;   // activation bytes per row per K step
+  static constexpr int CH = ROWB / 16;               // 16-byte chunks per row
+  static constexpr int A_BYTES = BM * ROWB;
+  static constexpr int A_COPIES = A_BYTES / 4096;    // 1 KiB copies per wave per stage
+  static constexpr int RPW = BM / 4;                 // scale rows copied per wave
+  static constexpr int C = A_COPIES + 1 + 8;         // copies per wave per stage
+  static constexpr int OFF_AS = A_BYTES;             // [4 waves][64 slots] dwords
+  static constexpr int OFF_B = OFF_AS + 1024;
+  static constexpr int OFF_BS = OFF_B + 4 * 4096;
+  static constexpr int STAGE = OFF_BS + 4 * 1024;
+  static_assert(A_BYTES % 4096 == 0, "activation tile must fill whole copies");
+  static_assert(RPW <= 64, "scale rows per wave");
+  // LDS slot of row r's scale dword
+  static __device__ __forceinline__ int sslot(int r) { return (r / RPW) * 64 + (r % RPW); }
+};
+
+template <int FMT, int MT, bool SECOND>
+__global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
+  using F = typename ActFmt<FMT>::F;
+  using TS = TileShape<FMT, MT>;
+  constexpr int NS = 4;  // K steps in flight
+  constexpr int BM = TS::BM, ROWB = TS::ROWB, CH = TS::CH;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * TS::STAGE];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int K = SECOND ? p.I : p.H;
+  const int S = K / 128;
+  const int ntiles = (SECOND ? p.H : 2 * p.I) / 16;
+  const int NB = (ntiles + 15) / 16;
+  const int n_mb = uniform(p.mtoff[p.E]);
+  const long total = (long)n_mb * NB;
+  const size_t arow = FMT == 0 ? (size_t)K : (size_t)K / 2;
+  const size_t srow = (size_t)K / 32;
+  const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
+  const size_t tile_bytes = (size_t)S * 1024, tile_dwords = (size_t)((S + 3) / 4) * 64;
+  const uint8_t *__restrict__ A = SECOND ? p.a2c : p.a1c;
+  const uint8_t *__restrict__ As = SECOND ? p.a2s : p.a1s;
+  const int G = gridDim.x;
+  const int L = (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8);
+  // per-lane constant LDS offsets of the swizzled activation fragments
+  const int swz = (FMT == 0) ? (r16 & 7) : (r16 & 3);
+  const int aoff_lo = r16 * ROWB + 16 * (g ^ swz);
+  const int aoff_hi = r16 * ROWB + 16 * ((4 + g) ^ swz);
+
+  for (long w = L; w < total; w += G) {
+    const int gmb = (int)(w / NB), nb = (int)(w % NB);
+    const int e = uniform(p.mbexp[gmb]);
+    const int mb = gmb - uniform(p.mtoff[e]);
+    const int row0 = uniform(p.offsets[e]) + BM * mb;
+    const int nrows = min(BM, uniform(p.offsets[e + 1]) - row0);
+
+    // global sources of this lane's copies (the K-step offset is added later)
+    const uint8_t *asrc[TS::A_COPIES];
+#pragma unroll
+    for (int i = 0; i < TS::A_COPIES; ++i) {
+      const int ci = (wave * TS::A_COPIES + i) * 64 + lane;  // LDS chunk this lane fills
+      const int row = ci / CH, slot = ci % CH;
+      const int rr = min(row, nrows - 1);
+      const size_t ridx = SECOND ? (size_t)(row0 + rr) : (size_t)(p.perm[row0 + rr] / p.top_k);
+      asrc[i] = A + ridx * arow + 16 * (slot ^ (row & (CH - 1)));
+    }
+    const uint8_t *ssrc;
+    {
+      const int row = wave * TS::RPW + (lane % TS::RPW);
+      const int rr = min(row, nrows - 1);
+      const size_t ridx = SECOND ? (size_t)(row0 + rr) : (size_t)(p.perm[row0 + rr] / p.top_k);
+      ssrc = As + ridx * srow;
+    }
+    const int tile0 = 16 * nb + 4 * wave;
+    const bool active = tile0 < ntiles;
+    const size_t tbase = (size_t)e * ntiles + (active ? tile0 : 0);
+    const uint8_t *wsrc = p.wp + tbase * tile_bytes + (size_t)lane * 16;
+    const uint32_t *wssrc = p.wsp + tbase * tile_dwords + lane;
+
+    // Copies of K step s into stage buffer s % NS.  Past the last step the
+    // same number of copies is issued from one fixed address (every lane
+    // reads the same 16 bytes) into a buffer no step reads any more, so each
+    // loop iteration issues exactly C copies and one wait count fits all.
+    const uint8_t *dummy = p.wp + tbase * tile_bytes;
+    auto issue = [&](int s) __attribute__((always_inline)) {
+      const bool real = s < S;
+      uint8_t *st = lds + (s % NS) * TS::STAGE;
+#pragma unroll
+      for (int i = 0; i < TS::A_COPIES; ++i)
+        copy16_to_lds(real ? asrc[i] + (size_t)ROWB * s : dummy,
+                      st + (wave * TS::A_COPIES + i) * 1024);
+      copy4_to_lds(real ? ssrc + 4 * s : dummy, st + TS::OFF_AS + wave * 256);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        copy16_to_lds(real ? wsrc + q * tile_bytes + (size_t)s * 1024 : dummy,
+                      st + TS::OFF_B + wave * 4096 + q * 1024);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        copy4_to_lds(real ? (const void *)(wssrc + q * tile_dwords + (size_t)(s >> 2) * 64)
+                          : (const void *)dummy,
+                     st + TS::OFF_BS + wave * 1024 + q * 256);
+    };
+
+    v4f acc[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[m][q] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    auto read_a = [&](const uint8_t *st, int m) __attribute__((always_inline)) {
+      v8i a;
+      const uint8_t *base = st + m * 16 * ROWB;
+      const u32x4 lo = *reinterpret_cast<const u32x4 *>(base + aoff_lo);
+      a[0] = (int)lo[0]; a[1] = (int)lo[1]; a[2] = (int)lo[2]; a[3] = (int)lo[3];
+      if (FMT == 0) {
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(base + aoff_hi);
+        a[4] = (int)hi[0]; a[5] = (int)hi[1]; a[6] = (int)hi[2]; a[7] = (int)hi[3];
+      } else {
+        a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
+      }
+      return a;
+    };
+    auto read_sa = [&](const uint8_t *st, int m) __attribute__((always_inline)) {
+      const uint32_t d = *reinterpret_cast<const uint32_t *>(st + TS::OFF_AS +
+                                                             4 * TS::sslot(16 * m + r16));
+      return (int)((d >> (8 * g)) & 0xffu);
+    };
+
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(s);
+    wait_vm<(NS - 2) * TS::C>();  // step 0 has landed
+    __syncthreads();
+
+    for (int s = 0; s < S; ++s) {
+      issue(s + NS - 1);
+      {  // inactive waves (past the last weight tile) compute on valid data and never store
+        const uint8_t *st = lds + (s % NS) * TS::STAGE;
+        v8i b[4];
+        int sb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(st + TS::OFF_B + wave * 4096 +
+                                                          q * 1024 + lane * 16);
+          b[q][0] = (int)v[0]; b[q][1] = (int)v[1]; b[q][2] = (int)v[2]; b[q][3] = (int)v[3];
+          b[q][4] = 0; b[q][5] = 0; b[q][6] = 0; b[q][7] = 0;
+          const uint32_t d = *reinterpret_cast<const uint32_t *>(st + TS::OFF_BS + wave * 1024 +
+                                                                 q * 256 + lane * 4);
+          sb[q] = (int)((d >> (8 * (s & 3))) & 0xffu);
+        }
+        // activation fragment m+1 is read from LDS while the MFMAs of m run
+        v8i acur = read_a(st, 0);
+        int sacur = read_sa(st, 0);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          v8i anext = acur;
+          int sanext = sacur;
+          if (m + 1 < MT) {
+            anext = read_a(st, m + 1);
+            sanext = read_sa(st, m + 1);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[m][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(acur, b[q], acc[m][q],
+                                                                         FMT, 4, 0, sacur, 0, sb[q]);
+          __builtin_amdgcn_sched_barrier(0);
+          acur = anext;
+          sacur = sanext;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<(NS - 2) * TS::C>();  // step s+1 has landed
+      barrier_keep_copies();
+    }
+
+    if (active) {
+      if (!SECOND) {
+        const int j = tile0 / 4;  // unit: h columns [32j, 32j + 32)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int mrow = 16 * m + 4 * g + r;
+            const size_t prow = (size_t)(row0 + min(mrow, nrows - 1));
+            swiglu_requant<F, FMT>(acc[m][0][r], acc[m][1][r], acc[m][2][r], acc[m][3][r],
+                                   mrow < nrows, p.a2c + prow * a2row,
+                                   p.a2s + prow * (p.I / 32), j, r16);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int mrow = 16 * m + 4 * g + r;
+            if (mrow < nrows) {
+              const float wa = p.wts[p.perm[row0 + mrow]];
+              float *d = p.rows + (size_t)(row0 + mrow) * p.H + 16 * (size_t)tile0 + r16;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) d[16 * q] = wa * acc[m][q][r];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+GemmPlan choose_plan(int T, int top_k, int E, int act) {
+  // average rows per expert decides between weight streaming (few rows) and
+  // the pipelined tiled kernel, and that kernel's rows per item (an MXFP4
+  // activation tile needs at least 64 rows to fill whole 4 KiB copies)
+  const long N = (long)T * top_k;
+  const double avg = (double)N / E;
+  if (avg < 6.0) return GemmPlan{false, 1};
+  if (avg < 24.0) return GemmPlan{true, act == MOE_ACT_MXFP8_E4M3 ? 2 : 4};
+  if (avg < 56.0) return GemmPlan{true, 4};
+  return GemmPlan{true, 8};
+}
+
 static KArgs make_args(const GemmArgs &a, bool second) {
   KArgs k{};
   k.T = a.T; k.top_k = a.top_k; k.E = a.E; k.H = a.H; k.I = a.I;
   k.a1c = a.a1c; k.a1s = a.a1s; k.a2c = a.a2c; k.a2s = a.a2s;
-  k.perm = a.perm; k.offsets = a.offsets; k.mtoff = a.mtoff; k.wts = a.wts;
+  k.perm = a.perm; k.offsets = a.offsets; k.mtoff = a.mtoff; k.mbexp = a.mbexp; k.wts = a.wts;
   k.wp = second ? a.w2p : a.w13p;
   k.wsp = reinterpret_cast<const uint32_t *>(second ? a.w2sp : a.w13sp);
-  k.comb = a.comb;
+  k.rows = a.rows;
   return k;
 }
 
@@ -262,8 +542,30 @@ static unsigned persistent_grid(long items_upper, int num_cus) {
   return (unsigned)(items_upper < cap ? items_upper : cap);
 }
 
+template <bool SECOND>
+static hipError_t launch_tiled(const GemmArgs &a, const KArgs &k, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.num_cus / 8 * 8);  // one workgroup per CU
+  const bool f8 = a.act == MOE_ACT_MXFP8_E4M3;
+  if (f8) {
+    switch (a.plan.mt) {
+      case 2: tiled_kernel<0, 2, SECOND><<<grid, 256, 0, s>>>(k); break;
+      case 4: tiled_kernel<0, 4, SECOND><<<grid, 256, 0, s>>>(k); break;
+      case 8: tiled_kernel<0, 8, SECOND><<<grid, 256, 0, s>>>(k); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.plan.mt) {
+      case 4: tiled_kernel<4, 4, SECOND><<<grid, 256, 0, s>>>(k); break;
+      case 8: tiled_kernel<4, 8, SECOND><<<grid, 256, 0, s>>>(k); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s) {
   const KArgs k = make_args(a, false);
+  if (a.plan.tiled) return launch_tiled<false>(a, k, s);
   const unsigned grid = persistent_grid(a.max_mtiles * (a.I / 32), a.num_cus);
   if (a.act == MOE_ACT_MXFP8_E4M3) gemm1_kernel<0><<<grid, 256, 0, s>>>(k);
   else gemm1_kernel<4><<<grid, 256, 0, s>>>(k);
@@ -272,6 +574,7 @@ hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s) {
 
 hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s) {
   const KArgs k = make_args(a, true);
+  if (a.plan.tiled) return launch_tiled<true>(a, k, s);
   const unsigned grid = persistent_grid(a.max_mtiles * (a.H / 64), a.num_cus);
   if (a.act == MOE_ACT_MXFP8_E4M3) gemm2_kernel<0><<<grid, 256, 0, s>>>(k);
   else gemm2_kernel<4><<<grid, 256, 0, s>>>(k);

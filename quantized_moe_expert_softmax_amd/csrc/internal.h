@@ -33,7 +33,8 @@ inline PackDims pack_dims(int R, int K) { return PackDims{R, K, K / 128, (K / 12
 struct WsLayout {
   size_t off[MOE_WS_NUM];
   size_t hist;    // [nb][E] int32 per-sort-block histograms, then bases
-  size_t mtoff;   // [E+1] int32 prefix sum of m-tiles per expert
+  size_t mtoff;   // [E+1] int32 prefix sum of m-blocks per expert
+  size_t mbexp;   // [N/16 + E] int32 expert of each m-block
   size_t total;
   int nb;
 };
@@ -51,54 +52,78 @@ inline WsLayout ws_layout(int T, int top_k, int E, int H, int I, int act) {
   L.off[MOE_WS_COUNTS] = take((size_t)E * 4);
   L.off[MOE_WS_OFFSETS] = take((size_t)(E + 1) * 4);
   L.mtoff = take((size_t)(E + 1) * 4);
+  L.mbexp = take((N / kMTile + E + 1) * 4);
   L.hist = take((size_t)L.nb * E * 4);
   L.off[MOE_WS_PERM] = take(N * 4);
   L.off[MOE_WS_A1_CODES] = take((size_t)T * a1row);
   L.off[MOE_WS_A1_SCALES] = take((size_t)T * (H / 32));
   L.off[MOE_WS_A2_CODES] = take(N * a2row);
   L.off[MOE_WS_A2_SCALES] = take(N * (size_t)(I / 32));
-  L.off[MOE_WS_COMBINE] = take((size_t)T * H * 4);
+  L.off[MOE_WS_ROWS] = take(N * (size_t)H * 4);
+  L.off[MOE_WS_SLOT] = take(N * 4);
   L.total = o;
   return L;
 }
 
-// Sort-only workspace (moe_sort): histograms and m-tile prefix.
-inline size_t sort_ws_bytes(int T, int E, size_t *hist_off, size_t *mtoff_off) {
+// Sort-only workspace (moe_sort): histograms, m-block prefix and table,
+// inverse permutation.
+struct SortWs {
+  size_t mtoff, hist, mbexp, inv, total;
+};
+inline SortWs sort_ws_layout(int T, int E, int top_k) {
+  SortWs w{};
   size_t o = 0;
-  *mtoff_off = o;
-  o = align_up(o + (size_t)(E + 1) * 4, 256);
-  *hist_off = o;
-  o = align_up(o + (size_t)ceil_div(T, kSortBlock) * E * 4, 256);
-  return o;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
+  const size_t N = (size_t)T * top_k;
+  w.mtoff = take((size_t)(E + 1) * 4);
+  w.hist = take((size_t)ceil_div(T, kSortBlock) * E * 4);
+  w.mbexp = take((N / kMTile + E + 1) * 4);
+  w.inv = take(N * 4);
+  w.total = o;
+  return w;
 }
 
 // ---- launchers (kernels.hip) -----------------------------------------------
 hipError_t launch_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w,
-                        float *comb, int H, hipStream_t s);
+                        hipStream_t s);
 hipError_t launch_sort_hist(const int32_t *ids, int T, int E, int top_k, int32_t *hist, int nb,
                             hipStream_t s);
 hipError_t launch_sort_scan(int32_t *hist, int nb, int E, int32_t *counts, int32_t *offsets,
-                            int32_t *mtoff, hipStream_t s);
+                            int32_t *mtoff, int32_t *mbexp, int bm, hipStream_t s);
 hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, const int32_t *hist,
-                               int32_t *perm, hipStream_t s);
+                               int32_t *perm, int32_t *inv, hipStream_t s);
 hipError_t launch_quant(const uint16_t *x, long rows, int K, int act, uint8_t *codes,
                         uint8_t *scales, hipStream_t s);
 hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int E, int R, int K,
                           bool interleave_gate_up, uint8_t *pcodes, uint8_t *pscales,
                           hipStream_t s);
+// GEMM variant of one forward call (chosen on the host from the token count).
+//   stream: 16-row m-tiles, the four waves of a workgroup split K, weights
+//           go straight from HBM to VGPRs (decode: few rows per expert)
+//   tiled:  bm = 16*MT rows per work item staged in LDS and shared by the
+//           waves, each wave owning 64 weight rows (prefill)
+struct GemmPlan {
+  bool tiled;
+  int mt;  // 16-row MFMA tiles per work item (1 for stream)
+  int bm() const { return 16 * mt; }
+};
+GemmPlan choose_plan(int T, int top_k, int E, int act);
+
 struct GemmArgs {
   int T, top_k, E, H, I, act;
-  long max_mtiles;  // host upper bound of m-tiles (N/16 + E)
+  GemmPlan plan;
+  long max_mtiles;  // host upper bound of m-blocks (N/bm + E)
   int num_cus;
   const uint8_t *a1c, *a1s;
   uint8_t *a2c, *a2s;
-  const int32_t *perm, *offsets, *mtoff;
+  const int32_t *perm, *offsets, *mtoff, *mbexp;
   const float *wts;
   const uint8_t *w13p, *w13sp, *w2p, *w2sp;
-  float *comb;
+  float *rows;  // [N][H] weighted GEMM2 rows
 };
 hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s);
-hipError_t launch_finalize(const float *comb, long n, uint16_t *y, hipStream_t s);
+hipError_t launch_combine(const float *rows, const int32_t *inv, int T, int H, int top_k,
+                          uint16_t *y, hipStream_t s);
 
 }  // namespace moe

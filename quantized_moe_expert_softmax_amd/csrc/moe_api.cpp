@@ -186,22 +186,25 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
   int32_t *counts = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_COUNTS]);
   int32_t *offsets = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_OFFSETS]);
   int32_t *mtoff = reinterpret_cast<int32_t *>(base + W.mtoff);
+  int32_t *mbexp = reinterpret_cast<int32_t *>(base + W.mbexp);
   int32_t *hist = reinterpret_cast<int32_t *>(base + W.hist);
   int32_t *perm = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_PERM]);
   uint8_t *a1c = base + W.off[MOE_WS_A1_CODES];
   uint8_t *a1s = base + W.off[MOE_WS_A1_SCALES];
   uint8_t *a2c = base + W.off[MOE_WS_A2_CODES];
   uint8_t *a2s = base + W.off[MOE_WS_A2_SCALES];
-  float *comb = reinterpret_cast<float *>(base + W.off[MOE_WS_COMBINE]);
+  float *rows = reinterpret_cast<float *>(base + W.off[MOE_WS_ROWS]);
+  int32_t *inv = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_SLOT]);
 
   GemmArgs g{};
   g.T = T; g.top_k = top_k; g.E = L->E; g.H = L->H; g.I = L->I; g.act = act;
-  g.max_mtiles = ((long)T * top_k + kMTile - 1) / kMTile + L->E;
+  g.plan = choose_plan(T, top_k, L->E, act);
+  g.max_mtiles = ((long)T * top_k + g.plan.bm() - 1) / g.plan.bm() + L->E;
   g.num_cus = L->num_cus;
   g.a1c = a1c; g.a1s = a1s; g.a2c = a2c; g.a2s = a2s;
-  g.perm = perm; g.offsets = offsets; g.mtoff = mtoff; g.wts = wts;
+  g.perm = perm; g.offsets = offsets; g.mtoff = mtoff; g.mbexp = mbexp; g.wts = wts;
   g.w13p = L->w13p; g.w13sp = L->w13sp; g.w2p = L->w2p; g.w2sp = L->w2sp;
-  g.comb = comb;
+  g.rows = rows;
 
   const bool prof = L->profiling && L->prof_calls < L->prof_max;
   hipEvent_t *ev = prof ? &L->events[(size_t)L->prof_calls * (MOE_K_NUM + 1)] : nullptr;
@@ -212,13 +215,14 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
     ++stage;
   };
   mark();
-  if (e == hipSuccess) e = launch_route(logits, T, L->E, top_k, ids, wts, comb, L->H, s);
+  if (e == hipSuccess) e = launch_route(logits, T, L->E, top_k, ids, wts, s);
   mark();
   if (e == hipSuccess) e = launch_sort_hist(ids, T, L->E, top_k, hist, W.nb, s);
   mark();
-  if (e == hipSuccess) e = launch_sort_scan(hist, W.nb, L->E, counts, offsets, mtoff, s);
+  if (e == hipSuccess)
+    e = launch_sort_scan(hist, W.nb, L->E, counts, offsets, mtoff, mbexp, g.plan.bm(), s);
   mark();
-  if (e == hipSuccess) e = launch_sort_scatter(ids, T, L->E, top_k, hist, perm, s);
+  if (e == hipSuccess) e = launch_sort_scatter(ids, T, L->E, top_k, hist, perm, inv, s);
   mark();
   if (e == hipSuccess)
     e = launch_quant(static_cast<const uint16_t *>(x), T, L->H, act, a1c, a1s, s);
@@ -227,7 +231,8 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
   mark();
   if (e == hipSuccess) e = launch_gemm2(g, s);
   mark();
-  if (e == hipSuccess) e = launch_finalize(comb, (long)T * L->H, static_cast<uint16_t *>(y), s);
+  if (e == hipSuccess)
+    e = launch_combine(rows, inv, T, L->H, top_k, static_cast<uint16_t *>(y), s);
   mark();
   if (e != hipSuccess) return hip_fail(e, "moe_forward launch");
   if (prof) ++L->prof_calls;
@@ -244,14 +249,13 @@ moe_status moe_route(const float *logits, int T, int E, int top_k, int32_t *ids,
   if (!logits || !ids || !w) return fail(MOE_ERR_INVALID_ARG, "null data pointer");
   moe_status st = check_device(nullptr, nullptr);
   if (st != MOE_OK) return st;
-  hipError_t e = launch_route(logits, T, E, top_k, ids, w, nullptr, 0, s);
+  hipError_t e = launch_route(logits, T, E, top_k, ids, w, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "route launch");
 }
 
-size_t moe_sort_workspace_bytes(int T, int E) {
-  if (T < 0 || T > (1 << 20) || E < 1 || E > 1024) return 0;
-  size_t h, m;
-  return sort_ws_bytes(T, E, &h, &m);
+size_t moe_sort_workspace_bytes(int T, int E, int top_k) {
+  if (T < 0 || T > (1 << 20) || E < 1 || E > 1024 || top_k < 1 || top_k > 8) return 0;
+  return sort_ws_layout(T, E, top_k).total;
 }
 
 moe_status moe_sort(const int32_t *ids, int T, int E, int top_k, int32_t *counts,
@@ -262,19 +266,20 @@ moe_status moe_sort(const int32_t *ids, int T, int E, int top_k, int32_t *counts
   if (T < 0 || T > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, 2^20]", T);
   if (!ids || !counts || !offsets || !perm || !ws) return fail(MOE_ERR_INVALID_ARG, "null data pointer");
   if (misaligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  size_t hist_off, mtoff_off;
-  const size_t need = sort_ws_bytes(T, E, &hist_off, &mtoff_off);
-  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  const SortWs W = sort_ws_layout(T, E, top_k);
+  if (ws_bytes < W.total) return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
   moe_status st = check_device(nullptr, nullptr);
   if (st != MOE_OK) return st;
   uint8_t *base = static_cast<uint8_t *>(ws);
-  int32_t *hist = reinterpret_cast<int32_t *>(base + hist_off);
-  int32_t *mtoff = reinterpret_cast<int32_t *>(base + mtoff_off);
+  int32_t *hist = reinterpret_cast<int32_t *>(base + W.hist);
+  int32_t *mtoff = reinterpret_cast<int32_t *>(base + W.mtoff);
+  int32_t *mbexp = reinterpret_cast<int32_t *>(base + W.mbexp);
+  int32_t *inv = reinterpret_cast<int32_t *>(base + W.inv);
   const int nb = ceil_div(T, kSortBlock);
   hipError_t e = hipSuccess;
   if (nb > 0) e = launch_sort_hist(ids, T, E, top_k, hist, nb, s);
-  if (e == hipSuccess) e = launch_sort_scan(hist, nb, E, counts, offsets, mtoff, s);
-  if (e == hipSuccess && nb > 0) e = launch_sort_scatter(ids, T, E, top_k, hist, perm, s);
+  if (e == hipSuccess) e = launch_sort_scan(hist, nb, E, counts, offsets, mtoff, mbexp, kMTile, s);
+  if (e == hipSuccess && nb > 0) e = launch_sort_scatter(ids, T, E, top_k, hist, perm, inv, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "sort launch");
 }
 

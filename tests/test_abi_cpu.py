@@ -90,10 +90,15 @@ def test_stage_calls_validate(lib):
 
 
 def test_sort_workspace_size(lib):
-    # [E+1] m-tile prefix and [ceil(T/256)][E] block histograms, 256-byte aligned
-    assert lib.moe_sort_workspace_bytes(1, 8) == 256 + 256
-    assert lib.moe_sort_workspace_bytes(32768, 384) == 1792 + 128 * 384 * 4
-    assert lib.moe_sort_workspace_bytes(4, 0) == 0
+    # [E+1] m-block prefix, [ceil(T/256)][E] block histograms, [N/16 + E + 1]
+    # m-block experts, [N] inverse permutation; each region 256-byte aligned
+    al = lambda n: -(-n // 256) * 256
+    for T, E, k in ((1, 8, 2), (32768, 384, 6), (1000, 128, 3)):
+        N = T * k
+        want = al((E + 1) * 4) + al(-(-T // 256) * E * 4) + al((N // 16 + E + 1) * 4) + al(N * 4)
+        assert lib.moe_sort_workspace_bytes(T, E, k) == want
+    assert lib.moe_sort_workspace_bytes(4, 0, 1) == 0
+    assert lib.moe_sort_workspace_bytes(4, 8, 9) == 0
 
 
 def test_profile_calls_validate(lib):

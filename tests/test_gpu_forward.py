@@ -46,6 +46,8 @@ def _check_workspace(layer, ws, x, lg, k, act, ref_a2=None):
     assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_OFFSETS, (E + 1) * 4, np.int32), ro)
     perm = ws_view(ws, offs, moe.MOE_WS_PERM, N * 4, np.int32)
     assert np.array_equal(perm, rp)
+    slot = ws_view(ws, offs, moe.MOE_WS_SLOT, N * 4, np.int32)
+    assert np.array_equal(slot[rp], np.arange(N))
     a1row = H if act == 0 else H // 2
     xc, xs = oracle.mx_quantize_bf16(x, act)
     assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_A1_CODES, T * a1row).reshape(T, a1row), xc)
