@@ -52,7 +52,21 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4, help="tokens the oracle FFN runs on")
+    p.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB three times (the "
+                        "known-size kernel that scales the HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(torch, mib, reps=3):
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "reps": reps}), flush=True)
 
 
 def touched_experts(moe, layer, ws, T, top_k, act):
@@ -147,6 +161,9 @@ def main():
               "experts all fit one MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibrate:
+        copy_calibration(torch, args.copy_calibrate)
+        return
     import quantized_moe_expert_softmax_amd as moe
     from quantized_moe_expert_softmax_amd import synth
 

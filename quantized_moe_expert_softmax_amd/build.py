@@ -35,13 +35,19 @@ CFLAGS = [
 ]
 
 
+# Per-file extra flags.  The expert GEMMs keep their MFMA accumulators in
+# ordinary VGPRs: with the accumulation-register form the register allocator
+# shuffles accumulators between register files on every K step.
+FILE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the packed-fp32 feature name; that warning is harmless
     out = "\n".join(l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l)

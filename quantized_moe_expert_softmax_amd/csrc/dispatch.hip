@@ -345,21 +345,18 @@ __global__ __launch_bounds__(256) void prepack_scales_kernel(const uint8_t *__re
                                                              uint32_t *__restrict__ dst) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
-  const int steps = K / 128, groups = (steps + 3) / 4, ntile = R / 16;
+  const int steps = K / 128, nquad = R / 64;
   const int lane = (int)(idx & 63);
   const long rest = idx >> 6;
-  const int gq = (int)(rest % groups);
-  const long rest2 = rest / groups;
-  const int tile = (int)(rest2 % ntile);
-  const long e = rest2 / ntile;
-  const long row = packed_row(tile, lane & 15, R / 2, gate_up);
-  const uint8_t *p = src + (e * R + row) * (long)(K / 32);
+  const int s = (int)(rest % steps);
+  const long rest2 = rest / steps;
+  const int u = (int)(rest2 % nquad);
+  const long e = rest2 / nquad;
   uint32_t d = 0;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int s = 4 * gq + jj;
-    const uint32_t byte = s < steps ? p[4 * s + (lane >> 4)] : 127u;
-    d |= byte << (8 * jj);
+  for (int q = 0; q < 4; ++q) {
+    const long row = packed_row(4 * u + q, lane & 15, R / 2, gate_up);
+    d |= (uint32_t)src[(e * R + row) * (long)(K / 32) + 4 * s + (lane >> 4)] << (8 * q);
   }
   dst[idx] = d;
 }
@@ -368,7 +365,7 @@ hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int E, in
                           bool gate_up, uint8_t *pcodes, uint8_t *pscales, hipStream_t s) {
   const PackDims d = pack_dims(R, K);
   const long nc = (long)E * (R / 16) * d.steps * 64;
-  const long ns = (long)E * (R / 16) * d.groups * 64;
+  const long ns = (long)E * (R / 64) * d.steps * 64;
   prepack_codes_kernel<<<(unsigned)((nc + 255) / 256), 256, 0, s>>>(codes, nc, R, K, gate_up,
                                                                    pcodes);
   hipError_t err = hipGetLastError();

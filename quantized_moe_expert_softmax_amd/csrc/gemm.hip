@@ -28,6 +28,7 @@
 // m-block table; padded rows of a partial m-block load a valid row and never
 // store (padding guard).
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include <type_traits>
@@ -55,6 +56,18 @@ struct KArgs {
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 
+// One scaled MFMA with the weight scale taken from byte q of sb (q is a
+// compile-time constant after unrolling: the byte is the MFMA's op_sel).
+template <int FMT>
+__device__ __forceinline__ v4f mfma_q(int q, v8i a, v8i b, v4f c, int sa, int sb) {
+  switch (q) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, 4, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, 4, 0, sa, 1, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, 4, 0, sa, 2, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, 4, 0, sa, 3, sb);
+  }
+}
+
 // A operand of K step s for lane group g from a row-major code row.
 template <int FMT>
 __device__ __forceinline__ v8i load_a(const uint8_t *__restrict__ row, int s, int g) {
@@ -72,36 +85,27 @@ __device__ __forceinline__ v8i load_a(const uint8_t *__restrict__ row, int s, in
   return a;
 }
 
-// acc[q] += A(rows of this lane's m-tile) x B(prepacked tile q) over the K
-// groups [g0, g1) of 4 steps each.
+// acc[q] += A(rows of this lane's m-tile) x B(prepacked tile q of one quad)
+// over the K steps [s0, s1).
 template <int FMT>
 __device__ __forceinline__ void mma_4tiles(v4f acc[4], const uint8_t *__restrict__ arow,
                                            const uint8_t *__restrict__ asrow,
                                            const uint8_t *__restrict__ wt,
-                                           const uint32_t *__restrict__ wst, size_t tile_bytes,
-                                           size_t tile_dwords, int S, int g0, int g1, int lane) {
+                                           const uint32_t *__restrict__ wsq, size_t tile_bytes,
+                                           int s0, int s1, int lane) {
   const int g = lane >> 4;
-  for (int gq = g0; gq < g1; ++gq) {
-    uint32_t bs[4];
+  for (int s = s0; s < s1; ++s) {
+    const v8i a = load_a<FMT>(arow, s, g);
+    const int sa = asrow[4 * s + g];
+    const int sb = (int)wsq[(size_t)s * 64 + lane];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bs[q] = wst[q * tile_dwords + (size_t)gq * 64 + lane];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int s = 4 * gq + jj;
-      if (s < S) {
-        const v8i a = load_a<FMT>(arow, s, g);
-        const int sa = asrow[4 * s + g];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 bq = *reinterpret_cast<const uint4 *>(wt + q * tile_bytes +
-                                                           ((size_t)s * 64 + lane) * 16);
-          v8i b;
-          b[0] = (int)bq.x; b[1] = (int)bq.y; b[2] = (int)bq.z; b[3] = (int)bq.w;
-          b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
-          acc[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              a, b, acc[q], FMT, 4, 0, sa, 0, (int)((bs[q] >> (8 * jj)) & 0xffu));
-        }
-      }
+    for (int q = 0; q < 4; ++q) {
+      const uint4 bq = *reinterpret_cast<const uint4 *>(wt + q * tile_bytes +
+                                                       ((size_t)s * 64 + lane) * 16);
+      v8i b;
+      b[0] = (int)bq.x; b[1] = (int)bq.y; b[2] = (int)bq.z; b[3] = (int)bq.w;
+      b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
+      acc[q] = mfma_q<FMT>(q, a, b, acc[q], sa, sb);
     }
   }
 }
@@ -171,12 +175,12 @@ __global__ __launch_bounds__(256) void gemm1_kernel(KArgs p) {
   const int NU = p.I / 32;
   const int n_mt = uniform(p.mtoff[p.E]);
   const long total = (long)n_mt * NU;
-  const int S = p.H / 128, G = (S + 3) / 4;
-  const int g0 = wave * G / 4, g1 = (wave + 1) * G / 4;
+  const int S = p.H / 128;
+  const int s0 = wave * S / 4, s1 = (wave + 1) * S / 4;
   const size_t a1row = FMT == 0 ? (size_t)p.H : (size_t)p.H / 2;
   const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
   const size_t ntiles = (size_t)(2 * p.I) / 16;
-  const size_t tile_bytes = (size_t)S * 1024, tile_dwords = (size_t)G * 64;
+  const size_t tile_bytes = (size_t)S * 1024;
   for (long w = blockIdx.x; w < total; w += gridDim.x) {
     const int j = (int)(w / n_mt), mt = (int)(w % n_mt);
     const int e = uniform(p.mbexp[mt]);
@@ -187,11 +191,11 @@ __global__ __launch_bounds__(256) void gemm1_kernel(KArgs p) {
     const uint8_t *arow = p.a1c + (size_t)tok * a1row;
     const uint8_t *asrow = p.a1s + (size_t)tok * (p.H / 32);
     const uint8_t *wt = p.wp + ((size_t)e * ntiles + 4 * (size_t)j) * tile_bytes;
-    const uint32_t *wst = p.wsp + ((size_t)e * ntiles + 4 * (size_t)j) * tile_dwords;
+    const uint32_t *wsq = p.wsp + ((size_t)e * (ntiles / 4) + j) * (size_t)S * 64;
     v4f acc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
-    mma_4tiles<FMT>(acc, arow, asrow, wt, wst, tile_bytes, tile_dwords, S, g0, g1, lane);
+    mma_4tiles<FMT>(acc, arow, asrow, wt, wsq, tile_bytes, s0, s1, lane);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -223,11 +227,11 @@ __global__ __launch_bounds__(256) void gemm2_kernel(KArgs p) {
   const int NB = p.H / 64;
   const int n_mt = uniform(p.mtoff[p.E]);
   const long total = (long)n_mt * NB;
-  const int S = p.I / 128, G = (S + 3) / 4;
-  const int g0 = wave * G / 4, g1 = (wave + 1) * G / 4;
+  const int S = p.I / 128;
+  const int s0 = wave * S / 4, s1 = (wave + 1) * S / 4;
   const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
   const size_t ntiles = (size_t)p.H / 16;
-  const size_t tile_bytes = (size_t)S * 1024, tile_dwords = (size_t)G * 64;
+  const size_t tile_bytes = (size_t)S * 1024;
   for (long w = blockIdx.x; w < total; w += gridDim.x) {
     const int nb = (int)(w / n_mt), mt = (int)(w % n_mt);
     const int e = uniform(p.mbexp[mt]);
@@ -237,11 +241,11 @@ __global__ __launch_bounds__(256) void gemm2_kernel(KArgs p) {
     const uint8_t *arow = p.a2c + pr * a2row;
     const uint8_t *asrow = p.a2s + pr * (p.I / 32);
     const uint8_t *wt = p.wp + ((size_t)e * ntiles + 4 * (size_t)nb) * tile_bytes;
-    const uint32_t *wst = p.wsp + ((size_t)e * ntiles + 4 * (size_t)nb) * tile_dwords;
+    const uint32_t *wsq = p.wsp + ((size_t)e * (ntiles / 4) + nb) * (size_t)S * 64;
     v4f acc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
-    mma_4tiles<FMT>(acc, arow, asrow, wt, wst, tile_bytes, tile_dwords, S, g0, g1, lane);
+    mma_4tiles<FMT>(acc, arow, asrow, wt, wsq, tile_bytes, s0, s1, lane);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -275,13 +279,14 @@ __global__ __launch_bounds__(256) void gemm2_kernel(KArgs p) {
 // once per item and feeds MT MFMAs; the activation tile of a K step is
 // shared by the four waves.  Every operand of a K step -- the BM activation
 // rows (16-byte chunks XOR-swizzled by row), their E8M0 scales, each wave's
-// four 1 KiB weight fragments and their scale dwords -- is copied from
+// four 1 KiB weight fragments and their scale dword -- is copied from
 // global memory straight into LDS with global_load_lds (no register
-// staging), NS steps deep; the waits count those copies exactly (they are
+// staging), NS steps deep, the copies of a later step interleaved with the
+// MFMAs of the current one; the waits count those copies exactly (they are
 // the only vector-memory instructions in the loop and issue in program
-// order).  Items run expert by expert with the m-blocks innermost (the
-// m-blocks of one (expert, weight block) reuse its weights from L2), and the
-// logical workgroup index is remapped so consecutive items share an XCD.
+// order).  BM is picked per call so that most experts fit one m-block (each
+// weight panel is then read once).  The logical workgroup index is remapped
+// so consecutive items share an XCD and its L2.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 typedef __attribute__((address_space(1))) void *glb_ptr_t;
@@ -316,11 +321,11 @@ struct TileShape {
   static constexpr int A_BYTES = BM * ROWB;
   static constexpr int A_COPIES = A_BYTES / 4096;    // 1 KiB copies per wave per stage
   static constexpr int RPW = BM / 4;                 // scale rows copied per wave
-  static constexpr int C = A_COPIES + 1 + 8;         // copies per wave per stage
+  static constexpr int C = A_COPIES + 1 + 4 + 1;     // copies per wave per stage
   static constexpr int OFF_AS = A_BYTES;             // [4 waves][64 slots] dwords
-  static constexpr int OFF_B = OFF_AS + 1024;
-  static constexpr int OFF_BS = OFF_B + 4 * 4096;
-  static constexpr int STAGE = OFF_BS + 4 * 1024;
+  static constexpr int OFF_B = OFF_AS + 1024;        // [4 waves][4 tiles] 1 KiB fragments
+  static constexpr int OFF_BS = OFF_B + 4 * 4096;    // [4 waves][64 lanes] scale dwords
+  static constexpr int STAGE = OFF_BS + 4 * 256;
   static_assert(A_BYTES % 4096 == 0, "activation tile must fill whole copies");
   static_assert(RPW <= 64, "scale rows per wave");
   // LDS slot of row r's scale dword
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
   const size_t arow = FMT == 0 ? (size_t)K : (size_t)K / 2;
   const size_t srow = (size_t)K / 32;
   const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
-  const size_t tile_bytes = (size_t)S * 1024, tile_dwords = (size_t)((S + 3) / 4) * 64;
+  const size_t tile_bytes = (size_t)S * 1024, quad_dwords = (size_t)S * 64;
   const uint8_t *__restrict__ A = SECOND ? p.a2c : p.a1c;
   const uint8_t *__restrict__ As = SECOND ? p.a2s : p.a1s;
   const int G = gridDim.x;
@@ -357,6 +362,8 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
   const int aoff_hi = r16 * ROWB + 16 * ((4 + g) ^ swz);
 
   for (long w = L; w < total; w += G) {
+    // item w = (global m-block, n-block), n-block minor: consecutive items
+    // (neighbouring CUs of one XCD) share the activation tile through L2
     const int gmb = (int)(w / NB), nb = (int)(w % NB);
     const int e = uniform(p.mbexp[gmb]);
     const int mb = gmb - uniform(p.mtoff[e]);
@@ -384,30 +391,35 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
     const bool active = tile0 < ntiles;
     const size_t tbase = (size_t)e * ntiles + (active ? tile0 : 0);
     const uint8_t *wsrc = p.wp + tbase * tile_bytes + (size_t)lane * 16;
-    const uint32_t *wssrc = p.wsp + tbase * tile_dwords + lane;
+    const uint32_t *wssrc = p.wsp + (tbase / 4) * quad_dwords + lane;
 
     // Copies of K step s into stage buffer s % NS.  Past the last step the
     // same number of copies is issued from one fixed address (every lane
     // reads the same 16 bytes) into a buffer no step reads any more, so each
     // loop iteration issues exactly C copies and one wait count fits all.
     const uint8_t *dummy = p.wp + tbase * tile_bytes;
-    auto issue = [&](int s) __attribute__((always_inline)) {
+    // copy i (0 <= i < C) of K step s: activation chunks, the activation
+    // scale dword, the four weight fragments, the four weight scale dwords
+    auto issue_one = [&](int s, int i) __attribute__((always_inline)) {
       const bool real = s < S;
       uint8_t *st = lds + (s % NS) * TS::STAGE;
-#pragma unroll
-      for (int i = 0; i < TS::A_COPIES; ++i)
+      if (i < TS::A_COPIES) {
         copy16_to_lds(real ? asrc[i] + (size_t)ROWB * s : dummy,
                       st + (wave * TS::A_COPIES + i) * 1024);
-      copy4_to_lds(real ? ssrc + 4 * s : dummy, st + TS::OFF_AS + wave * 256);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
+      } else if (i == TS::A_COPIES) {
+        copy4_to_lds(real ? ssrc + 4 * s : dummy, st + TS::OFF_AS + wave * 256);
+      } else if (i < TS::A_COPIES + 5) {
+        const int q = i - TS::A_COPIES - 1;
         copy16_to_lds(real ? wsrc + q * tile_bytes + (size_t)s * 1024 : dummy,
                       st + TS::OFF_B + wave * 4096 + q * 1024);
+      } else {
+        copy4_to_lds(real ? (const void *)(wssrc + (size_t)s * 64) : (const void *)dummy,
+                     st + TS::OFF_BS + wave * 256);
+      }
+    };
+    auto issue = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        copy4_to_lds(real ? (const void *)(wssrc + q * tile_dwords + (size_t)(s >> 2) * 64)
-                          : (const void *)dummy,
-                     st + TS::OFF_BS + wave * 1024 + q * 256);
+      for (int i = 0; i < TS::C; ++i) issue_one(s, i);
     };
 
     v4f acc[MT][4];
@@ -429,10 +441,10 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
       }
       return a;
     };
+    // the scale operands are read as single bytes, so the MFMA takes the load
+    // result as it is and no VALU op waits on the read inside the sequence
     auto read_sa = [&](const uint8_t *st, int m) __attribute__((always_inline)) {
-      const uint32_t d = *reinterpret_cast<const uint32_t *>(st + TS::OFF_AS +
-                                                             4 * TS::sslot(16 * m + r16));
-      return (int)((d >> (8 * g)) & 0xffu);
+      return (int)st[TS::OFF_AS + 4 * TS::sslot(16 * m + r16) + g];
     };
 
 #pragma unroll
@@ -441,26 +453,27 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
     __syncthreads();
 
     for (int s = 0; s < S; ++s) {
-      issue(s + NS - 1);
+      // the copies of step s + NS - 1 are spread over the MFMA sequence of
+      // step s, so the wave never stalls on a full memory queue with the
+      // matrix cores idle
       {  // inactive waves (past the last weight tile) compute on valid data and never store
         const uint8_t *st = lds + (s % NS) * TS::STAGE;
         v8i b[4];
-        int sb[4];
+        const int sb = *reinterpret_cast<const int *>(st + TS::OFF_BS + wave * 256 + lane * 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const u32x4 v = *reinterpret_cast<const u32x4 *>(st + TS::OFF_B + wave * 4096 +
                                                           q * 1024 + lane * 16);
           b[q][0] = (int)v[0]; b[q][1] = (int)v[1]; b[q][2] = (int)v[2]; b[q][3] = (int)v[3];
           b[q][4] = 0; b[q][5] = 0; b[q][6] = 0; b[q][7] = 0;
-          const uint32_t d = *reinterpret_cast<const uint32_t *>(st + TS::OFF_BS + wave * 1024 +
-                                                                 q * 256 + lane * 4);
-          sb[q] = (int)((d >> (8 * (s & 3))) & 0xffu);
         }
         // activation fragment m+1 is read from LDS while the MFMAs of m run
         v8i acur = read_a(st, 0);
         int sacur = read_sa(st, 0);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
+#pragma unroll
+          for (int i = m * TS::C / MT; i < (m + 1) * TS::C / MT; ++i) issue_one(s + NS - 1, i);
           v8i anext = acur;
           int sanext = sacur;
           if (m + 1 < MT) {
@@ -469,8 +482,7 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            acc[m][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(acur, b[q], acc[m][q],
-                                                                         FMT, 4, 0, sacur, 0, sb[q]);
+            acc[m][q] = mfma_q<FMT>(q, acur, b[q], acc[m][q], sacur, sb);
           __builtin_amdgcn_sched_barrier(0);
           acur = anext;
           sacur = sanext;
@@ -515,15 +527,23 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
 }
 
 GemmPlan choose_plan(int T, int top_k, int E, int act) {
-  // average rows per expert decides between weight streaming (few rows) and
-  // the pipelined tiled kernel, and that kernel's rows per item (an MXFP4
-  // activation tile needs at least 64 rows to fill whole 4 KiB copies)
+  // The average rows per expert decides between weight streaming (few rows)
+  // and the pipelined tiled kernel.  The tiled kernel's BM covers the mean
+  // plus 2.5 standard deviations of a binomial expert load, so that under
+  // uniform routing nearly every expert is one m-block and its weights are
+  // read once; an activation tile must fill whole 4 KiB copies (MXFP8: MT
+  // even; MXFP4: MT a multiple of 4), and MT <= 10 keeps the accumulators
+  // in registers.
   const long N = (long)T * top_k;
   const double avg = (double)N / E;
   if (avg < 6.0) return GemmPlan{false, 1};
-  if (avg < 24.0) return GemmPlan{true, act == MOE_ACT_MXFP8_E4M3 ? 2 : 4};
-  if (avg < 56.0) return GemmPlan{true, 4};
-  return GemmPlan{true, 8};
+  const double want = avg + 2.5 * sqrt(avg);
+  if (act == MOE_ACT_MXFP8_E4M3) {
+    int mt = (int)ceil(want / 16.0);
+    mt = mt + (mt & 1);
+    return GemmPlan{true, mt < 2 ? 2 : (mt > 10 ? 10 : mt)};
+  }
+  return GemmPlan{true, want <= 64.0 ? 4 : 8};
 }
 
 static KArgs make_args(const GemmArgs &a, bool second) {
@@ -550,7 +570,9 @@ static hipError_t launch_tiled(const GemmArgs &a, const KArgs &k, hipStream_t s)
     switch (a.plan.mt) {
       case 2: tiled_kernel<0, 2, SECOND><<<grid, 256, 0, s>>>(k); break;
       case 4: tiled_kernel<0, 4, SECOND><<<grid, 256, 0, s>>>(k); break;
+      case 6: tiled_kernel<0, 6, SECOND><<<grid, 256, 0, s>>>(k); break;
       case 8: tiled_kernel<0, 8, SECOND><<<grid, 256, 0, s>>>(k); break;
+      case 10: tiled_kernel<0, 10, SECOND><<<grid, 256, 0, s>>>(k); break;
       default: return hipErrorInvalidValue;
     }
   } else {

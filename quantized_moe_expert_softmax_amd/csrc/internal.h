@@ -15,20 +15,21 @@ constexpr int kUnit = 32;        // h columns per GEMM1 work unit (one requant b
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
-// Prepacked weight layout of one matrix of R rows and K columns (R % 16 == 0,
+// Prepacked weight layout of one matrix of R rows and K columns (R % 64 == 0,
 // K % 128 == 0): codes [R/16 n-tiles][K/128 steps][64 lanes][16 B], scales
-// [R/16][ceil(K/512) groups][64 lanes][4 B].  Lane l = 16*g + c holds row
-// 16*tile + c, columns [128*step + 32*g, +32) (the gfx950 scaled-MFMA B
-// operand of one 16x16x128 step); its scale dword holds the E8M0 bytes of
-// blocks 4*step + g for the four steps of a group.
+// [R/64 tile quads][K/128 steps][64 lanes][4 B].  Lane l = 16*g + c of tile t
+// holds row 16*t + c, columns [128*step + 32*g, +32) (the gfx950 scaled-MFMA
+// B operand of one 16x16x128 step); byte q of lane l's scale dword of quad u
+// is the E8M0 scale of that lane's block in tile 4*u + q (the MFMA picks the
+// byte with its scale op_sel, so one dword serves the four tiles a wave owns).
 struct PackDims {
-  int R, K, steps, groups;
+  int R, K, steps;
   size_t code_bytes_per_tile() const { return (size_t)steps * 1024; }
-  size_t scale_bytes_per_tile() const { return (size_t)groups * 256; }
+  size_t scale_bytes_per_quad() const { return (size_t)steps * 256; }
   size_t code_bytes() const { return (size_t)(R / 16) * code_bytes_per_tile(); }
-  size_t scale_bytes() const { return (size_t)(R / 16) * scale_bytes_per_tile(); }
+  size_t scale_bytes() const { return (size_t)(R / 64) * scale_bytes_per_quad(); }
 };
-inline PackDims pack_dims(int R, int K) { return PackDims{R, K, K / 128, (K / 128 + 3) / 4}; }
+inline PackDims pack_dims(int R, int K) { return PackDims{R, K, K / 128}; }
 
 struct WsLayout {
   size_t off[MOE_WS_NUM];
