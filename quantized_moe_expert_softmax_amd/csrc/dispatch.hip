@@ -188,7 +188,9 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
                                                            int E, int top_k,
                                                            const int32_t *__restrict__ base,
                                                            int32_t *__restrict__ perm,
-                                                           int32_t *__restrict__ inv) {
+                                                           int32_t *__restrict__ inv,
+                                                           const float *__restrict__ w,
+                                                           float *__restrict__ wsorted) {
   extern __shared__ unsigned long long masks[];  // [4 waves][E]
   for (int i = threadIdx.x; i < 4 * E; i += 256) masks[i] = 0ull;
   __syncthreads();
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
       const int32_t pos = base[(long)blockIdx.x * E + e] + r;
       perm[pos] = (int32_t)(t * top_k + j);
       inv[t * top_k + j] = pos;
+      if (wsorted) wsorted[pos] = w[t * top_k + j];
     }
   }
 }
@@ -228,9 +231,11 @@ hipError_t launch_sort_scan(int32_t *hist, int nb, int E, int32_t *counts, int32
 }
 
 hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, const int32_t *hist,
-                               int32_t *perm, int32_t *inv, hipStream_t s) {
+                               int32_t *perm, int32_t *inv, const float *w, float *wsorted,
+                               hipStream_t s) {
   const int nb = ceil_div(T, kSortBlock);
-  sort_scatter_kernel<<<nb, 256, (size_t)E * 4 * 8, s>>>(ids, T, E, top_k, hist, perm, inv);
+  sort_scatter_kernel<<<nb, 256, (size_t)E * 4 * 8, s>>>(ids, T, E, top_k, hist, perm, inv, w,
+                                                         wsorted);
   return hipGetLastError();
 }
 
@@ -238,7 +243,7 @@ hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, cons
 // Step 3: 1x32 MX quantisation of BF16 rows (FlyDSL #972 Technical Details:
 // BF16 activations to MXFP4 -- or MXFP8 on the A8W4 path -- with per-1x32
 // E8M0 scales, once per token before dispatch).  One thread per 32-element
-// block: amax over the bit patterns, block exponent, integer RNE encode.
+// block: amax over the bit patterns, block exponent, RNE encode.
 // ---------------------------------------------------------------------------
 template <class F>
 __global__ __launch_bounds__(256) void quant_kernel(const uint16_t *__restrict__ x, long nblocks,

@@ -47,7 +47,7 @@ struct KArgs {
   const uint8_t *a1c, *a1s;
   uint8_t *a2c, *a2s;
   const int32_t *perm, *offsets, *mtoff, *mbexp;
-  const float *wts;
+  const float *wts;  // [N] routing weight of sorted row p
   const uint8_t *wp;
   const uint32_t *wsp;
   float *rows;  // [N][H] weighted GEMM2 rows (sorted order)
@@ -134,11 +134,13 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
 // GEMM1 epilogue for one accumulator register r: lane c = l%16 of row group
 // l/16 holds gate/up columns 32j + c (lo) and 32j + 16 + c (hi) of one token
 // row; h = silu(gate) * up; the 32 h values of the row form one 1x32 block
-// (amax over the 16 lanes), requantised and stored to the A2 row (all lanes
-// must call; only `valid` rows store).
+// (amax over the 16 lanes), requantised and stored to the A2 row.  All lanes
+// call and store: the two lanes of an E2M1 byte both write it whole, all 16
+// lanes write the scale byte, and a padded row (computed from the last valid
+// row's data) rewrites that row's values, so no store needs a branch.
 template <class F, int FMT>
 __device__ __forceinline__ void swiglu_requant(float glo, float ghi, float ulo, float uhi,
-                                               bool valid, uint8_t *__restrict__ a2row,
+                                               uint8_t *__restrict__ a2row,
                                                uint8_t *__restrict__ a2srow, int j, int c) {
   const float hlo = silu(glo) * ulo;
   const float hhi = silu(ghi) * uhi;
@@ -148,16 +150,15 @@ __device__ __forceinline__ void swiglu_requant(float glo, float ghi, float ulo, 
   const uint32_t chi = encode_element<F>(f32_bits(hhi), X);
   const uint32_t plo = dpp<0xB1>(clo);  // code of lane c ^ 1
   const uint32_t phi = dpp<0xB1>(chi);
-  if (valid) {
-    if (FMT == 0) {
-      a2row[32 * j + c] = (uint8_t)clo;
-      a2row[32 * j + 16 + c] = (uint8_t)chi;
-    } else if ((c & 1) == 0) {
-      a2row[16 * j + c / 2] = (uint8_t)(clo | (plo << 4));
-      a2row[16 * j + 8 + c / 2] = (uint8_t)(chi | (phi << 4));
-    }
-    if (c == 0) a2srow[j] = (uint8_t)(X + 127);
+  if (FMT == 0) {
+    a2row[32 * j + c] = (uint8_t)clo;
+    a2row[32 * j + 16 + c] = (uint8_t)chi;
+  } else {
+    const bool odd = c & 1;
+    a2row[16 * j + c / 2] = (uint8_t)(odd ? (plo | (clo << 4)) : (clo | (plo << 4)));
+    a2row[16 * j + 8 + c / 2] = (uint8_t)(odd ? (phi | (chi << 4)) : (chi | (phi << 4)));
   }
+  a2srow[j] = (uint8_t)(X + 127);
 }
 
 template <int FMT>
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(256) void gemm1_kernel(KArgs p) {
         // tiles: 0 = gate cols [32j, +16), 1 = gate [32j+16, +16), 2/3 = up
         const int m = 4 * (lane >> 4) + r;
         const size_t prow = (size_t)(row0 + min(m, nrows - 1));
-        swiglu_requant<F, FMT>(v[0 * 4 + r], v[1 * 4 + r], v[2 * 4 + r], v[3 * 4 + r], m < nrows,
+        swiglu_requant<F, FMT>(v[0 * 4 + r], v[1 * 4 + r], v[2 * 4 + r], v[3 * 4 + r],
                                p.a2c + prow * a2row, p.a2s + prow * (p.I / 32), j, c);
       }
     }
@@ -255,16 +256,15 @@ __global__ __launch_bounds__(256) void gemm2_kernel(KArgs p) {
       const int c = lane & 15;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = 4 * (lane >> 4) + r;
-        if (m < nrows) {
-          const float wt_a = p.wts[p.perm[row0 + m]];
-          float *dst = p.rows + (size_t)(row0 + m) * p.H + 64 * nb + c;
+        // a padded row recomputes the last valid row and stores the same values
+        const int m = min(4 * (lane >> 4) + r, nrows - 1);
+        const float wt_a = p.wts[row0 + m];
+        float *dst = p.rows + (size_t)(row0 + m) * p.H + 64 * nb + c;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int i = 4 * q + r;
-            const float o = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
-            dst[16 * q] = wt_a * o;
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int i = 4 * q + r;
+          const float o = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
+          dst[16 * q] = wt_a * o;
         }
       }
     }
@@ -503,22 +503,26 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
             const int mrow = 16 * m + 4 * g + r;
             const size_t prow = (size_t)(row0 + min(mrow, nrows - 1));
             swiglu_requant<F, FMT>(acc[m][0][r], acc[m][1][r], acc[m][2][r], acc[m][3][r],
-                                   mrow < nrows, p.a2c + prow * a2row,
+                                   p.a2c + prow * a2row,
                                    p.a2s + prow * (p.I / 32), j, r16);
           }
         }
       } else {
+        // a padded row (loaded from the last valid row) stores the same
+        // values as that row, so every store is unconditional
+        float wa[MT][4];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) wa[m][r] = p.wts[row0 + min(16 * m + 4 * g + r, nrows - 1)];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int mrow = 16 * m + 4 * g + r;
-            if (mrow < nrows) {
-              const float wa = p.wts[p.perm[row0 + mrow]];
-              float *d = p.rows + (size_t)(row0 + mrow) * p.H + 16 * (size_t)tile0 + r16;
+            const int mrow = min(16 * m + 4 * g + r, nrows - 1);
+            float *d = p.rows + (size_t)(row0 + mrow) * p.H + 16 * (size_t)tile0 + r16;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) d[16 * q] = wa * acc[m][q][r];
-            }
+            for (int q = 0; q < 4; ++q) d[16 * q] = wa[m][r] * acc[m][q][r];
           }
         }
       }

@@ -36,6 +36,7 @@ struct WsLayout {
   size_t hist;    // [nb][E] int32 per-sort-block histograms, then bases
   size_t mtoff;   // [E+1] int32 prefix sum of m-blocks per expert
   size_t mbexp;   // [N/16 + E] int32 expert of each m-block
+  size_t wsorted; // [N] fp32 routing weight of sorted row p (assignment perm[p])
   size_t total;
   int nb;
 };
@@ -55,6 +56,7 @@ inline WsLayout ws_layout(int T, int top_k, int E, int H, int I, int act) {
   L.mtoff = take((size_t)(E + 1) * 4);
   L.mbexp = take((N / kMTile + E + 1) * 4);
   L.hist = take((size_t)L.nb * E * 4);
+  L.wsorted = take(N * 4);
   L.off[MOE_WS_PERM] = take(N * 4);
   L.off[MOE_WS_A1_CODES] = take((size_t)T * a1row);
   L.off[MOE_WS_A1_SCALES] = take((size_t)T * (H / 32));
@@ -92,7 +94,8 @@ hipError_t launch_sort_hist(const int32_t *ids, int T, int E, int top_k, int32_t
 hipError_t launch_sort_scan(int32_t *hist, int nb, int E, int32_t *counts, int32_t *offsets,
                             int32_t *mtoff, int32_t *mbexp, int bm, hipStream_t s);
 hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, const int32_t *hist,
-                               int32_t *perm, int32_t *inv, hipStream_t s);
+                               int32_t *perm, int32_t *inv, const float *w, float *wsorted,
+                               hipStream_t s);
 hipError_t launch_quant(const uint16_t *x, long rows, int K, int act, uint8_t *codes,
                         uint8_t *scales, hipStream_t s);
 hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int E, int R, int K,
@@ -118,7 +121,7 @@ struct GemmArgs {
   const uint8_t *a1c, *a1s;
   uint8_t *a2c, *a2s;
   const int32_t *perm, *offsets, *mtoff, *mbexp;
-  const float *wts;
+  const float *wts;  // [N] routing weight of sorted row p
   const uint8_t *w13p, *w13sp, *w2p, *w2sp;
   float *rows;  // [N][H] weighted GEMM2 rows
 };

@@ -195,6 +195,7 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
   uint8_t *a2s = base + W.off[MOE_WS_A2_SCALES];
   float *rows = reinterpret_cast<float *>(base + W.off[MOE_WS_ROWS]);
   int32_t *inv = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_SLOT]);
+  float *wsorted = reinterpret_cast<float *>(base + W.wsorted);
 
   GemmArgs g{};
   g.T = T; g.top_k = top_k; g.E = L->E; g.H = L->H; g.I = L->I; g.act = act;
@@ -202,7 +203,7 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
   g.max_mtiles = ((long)T * top_k + g.plan.bm() - 1) / g.plan.bm() + L->E;
   g.num_cus = L->num_cus;
   g.a1c = a1c; g.a1s = a1s; g.a2c = a2c; g.a2s = a2s;
-  g.perm = perm; g.offsets = offsets; g.mtoff = mtoff; g.mbexp = mbexp; g.wts = wts;
+  g.perm = perm; g.offsets = offsets; g.mtoff = mtoff; g.mbexp = mbexp; g.wts = wsorted;
   g.w13p = L->w13p; g.w13sp = L->w13sp; g.w2p = L->w2p; g.w2sp = L->w2sp;
   g.rows = rows;
 
@@ -222,7 +223,8 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
   if (e == hipSuccess)
     e = launch_sort_scan(hist, W.nb, L->E, counts, offsets, mtoff, mbexp, g.plan.bm(), s);
   mark();
-  if (e == hipSuccess) e = launch_sort_scatter(ids, T, L->E, top_k, hist, perm, inv, s);
+  if (e == hipSuccess)
+    e = launch_sort_scatter(ids, T, L->E, top_k, hist, perm, inv, wts, wsorted, s);
   mark();
   if (e == hipSuccess)
     e = launch_quant(static_cast<const uint16_t *>(x), T, L->H, act, a1c, a1s, s);
@@ -279,7 +281,8 @@ moe_status moe_sort(const int32_t *ids, int T, int E, int top_k, int32_t *counts
   hipError_t e = hipSuccess;
   if (nb > 0) e = launch_sort_hist(ids, T, E, top_k, hist, nb, s);
   if (e == hipSuccess) e = launch_sort_scan(hist, nb, E, counts, offsets, mtoff, mbexp, kMTile, s);
-  if (e == hipSuccess && nb > 0) e = launch_sort_scatter(ids, T, E, top_k, hist, perm, inv, s);
+  if (e == hipSuccess && nb > 0)
+    e = launch_sort_scatter(ids, T, E, top_k, hist, perm, inv, nullptr, nullptr, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "sort launch");
 }
 

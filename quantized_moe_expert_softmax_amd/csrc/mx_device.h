@@ -1,8 +1,7 @@
 // mx_device.h -- device-side MX (OCP microscaling) and BF16 conversions.
 //
-// All conversions work on IEEE bit patterns with integer arithmetic, so the
-// results do not depend on the floating-point mode of the kernel.  They
-// implement the 1x32-block rule the pages quantise with ("quantize BF16
+// Conversions take IEEE bit patterns; element rounding uses exact fp32 adds
+// under the default round-to-nearest-even mode.  They implement the 1x32-block rule the pages quantise with ("quantize BF16
 // activations to MXFP4 with per-1x32 E8M0 scales", FlyDSL #972 Technical
 // Details): block exponent X = floor(log2(amax)) - emax of the element type,
 // clamped to [-127, 127]; each element rounded to nearest even on the
@@ -24,50 +23,49 @@ struct E2M1 {  // magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
   static constexpr uint32_t kMaxCode = 0x7;
 };
 
+// 2^k as an fp32 for -126 <= k <= 127.
+__device__ __forceinline__ float exp2i(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
 // floor(log2(|v|)) of a finite, non-zero |v| given as fp32 bits.
 __device__ __forceinline__ int ilog2_bits(uint32_t a) {
-  uint32_t e = a >> 23;
-  if (e) return (int)e - 127;
-  return (31 - __builtin_clz(a & 0x7fffffu)) - 149;
+  const int e = (int)(a >> 23);
+  return e ? e - 127 : (31 - __builtin_clz(a & 0x7fffffu)) - 149;
 }
 
 // Shared block exponent from the largest |v| (fp32 bits, sign cleared).
 template <class F>
 __device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
-  if (amax_bits == 0) return -127;
-  int X = ilog2_bits(amax_bits) - F::kEmax;
-  return X < -127 ? -127 : (X > 127 ? 127 : X);
+  const int X = ilog2_bits(amax_bits | 1u) - F::kEmax;  // (| 1: no clz of 0; amax 0 is handled below)
+  return amax_bits == 0 ? -127 : (X < -127 ? -127 : (X > 127 ? 127 : X));
 }
 
-// Code of v * 2^-X (v as fp32 bits, finite) in element type F.
+// Code of v * 2^-X (v as fp32 bits, finite, |v| <= 2^(X + emax + 1)) in
+// element type F, without branches.
+//   y = |v| * 2^-X is exact whenever it is an fp32 normal (a power-of-two
+//   scaling; X <= 127 - emax keeps 2^-X a normal); a y below 2^-126 lies far
+//   under half the smallest element step and gives code 0 however it rounds.
+//   The grid step at y is u = 2^(max(floor(log2 y), emin) - mbits); adding and
+//   subtracting c = 2^23 * u rounds y to a multiple of u, ties to even (c is
+//   an even multiple of u, and y + c stays in c's binade).
+//   The code of a grid point r >= 2^emin is its biased binade and top mbits
+//   of fraction; below 2^emin it is r / 2^(emin - mbits); past the largest
+//   finite element it saturates.
 template <class F>
 __device__ __forceinline__ uint32_t encode_element(uint32_t v, int X) {
   const uint32_t sign = (v >> 31) << (F::kBits - 1);
-  const uint32_t a = v & 0x7fffffffu;
-  if (a == 0) return sign;
-  // |v| = M * 2^E with M a 24-bit integer significand
-  uint32_t e = a >> 23;
-  uint32_t M = a & 0x7fffffu;
-  int E;
-  if (e) { M |= 0x800000u; E = (int)e - 150; } else { E = -149; }
-  const int lg = (31 - __builtin_clz(M)) + E - X;  // floor(log2(|v| * 2^-X))
-  const int ex = lg < F::kEmin ? F::kEmin : lg;    // binade (subnormals share emin's spacing)
-  const int sh = (ex - F::kMbits) - (E - X);       // right shift giving multiples of the ulp
-  uint32_t r;
-  if (sh <= 0) {
-    r = M << (-sh);  // exact; r < 2^(kMbits+1) so no overflow
-  } else if (sh >= 25) {
-    r = 0;           // below half an ulp
-  } else {
-    r = M >> sh;
-    const uint32_t rem = M & ((1u << sh) - 1u);
-    const uint32_t half = 1u << (sh - 1);
-    if (rem > half || (rem == half && (r & 1u))) r += 1u;
-  }
-  // In the binade of exponent ex the code is (ex - emin) * 2^mbits + r; a
-  // rounding carry (r == 2^(mbits+1)) lands on the next binade's first code.
-  uint32_t code = ((uint32_t)(ex - F::kEmin) << F::kMbits) + r;
-  if (code > F::kMaxCode) code = F::kMaxCode;
+  const float y = __uint_as_float(v & 0x7fffffffu) * exp2i(-X);
+  const int ey = (int)(__float_as_uint(y) >> 23) - 127;
+  const int eb = ey > F::kEmin ? ey : F::kEmin;
+  const float c = exp2i(eb + 23 - F::kMbits);
+  const float t = y + c;
+  const float r = t - c;
+  const uint32_t rb = __float_as_uint(r);
+  const int er = (int)(rb >> 23) - 127;
+  const uint32_t normal = ((uint32_t)(er - F::kEmin + 1) << F::kMbits) |
+                          ((rb >> (23 - F::kMbits)) & ((1u << F::kMbits) - 1u));
+  const uint32_t sub = (uint32_t)(r * exp2i(F::kMbits - F::kEmin));
+  uint32_t code = er >= F::kEmin ? normal : sub;
+  code = code < F::kMaxCode ? code : F::kMaxCode;
   return sign | code;
 }
 
