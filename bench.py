@@ -10,11 +10,16 @@ workload (T=1, 2, 8, 32) are timed too and reported under "sweep".
 Between steps the router logits rotate over 8 pre-drawn sets, so successive
 calls touch different experts (the touched weights of one call are larger
 than the MI355X last-level cache at T >= 8, and rotate through ~1.7 GB at
-T = 1).  Per-kernel times come from HIP events the library records around
-every kernel of the timed calls; the roofline entry is for the dominant
-kernel (GEMM1) against HBM bandwidth, with its algorithmic bytes per launch:
-touched experts x gate/up weight bytes (codes + E8M0 scales) + the quantised
-token rows read + the requantised rows written.
+T = 1).  Each token count is timed three ways over the same calls: eager
+launches (this is `value` and `ms_per_step`), HIP-graph replay (one graph
+captured per logits set; `ms_per_step_graph`, slower than eager launches on
+this stack), and eager launches with HIP events the library records around
+every kernel (per-kernel times; an event record costs a few microseconds, so
+this pass is not used for the step time).  The roofline
+entry is for the dominant kernel (GEMM1) against HBM bandwidth, with its
+algorithmic bytes per launch: touched experts x gate/up weight bytes (codes
++ E8M0 scales) + the quantised token rows read + the requantised rows
+written.
 
 cpu_baseline: the CPU oracle (test infrastructure, single-threaded C)
 timed on a bounded sample of the same workload: routing, sort and
@@ -89,7 +94,10 @@ def layer_weight_bytes(layer, U):
     return U * (I * H + 2 * I * H // 32 + H * I // 2 + H * I // 32)
 
 
-def time_T(moe, torch, layer, wl, T, act, steps, warmup, profile):
+def time_T(moe, torch, layer, wl, T, act, steps, warmup):
+    """Three passes over the same `steps` calls (logits rotating over 8 sets):
+    eager launches, HIP-graph replays (one graph captured per logits set),
+    both with no events, then an eager pass with per-kernel HIP events."""
     x = torch.from_numpy(wl.x(T).view("int16")).cuda().view(torch.bfloat16)
     lgs = [torch.from_numpy(wl.logits(T, r)).cuda() for r in range(8)]
     ws = moe.alloc_workspace(layer, T, wl.top_k, act)
@@ -101,20 +109,41 @@ def time_T(moe, torch, layer, wl, T, act, steps, warmup, profile):
         torch.cuda.synchronize()
         Us.append(touched_experts(moe, layer, ws, T, wl.top_k, act))
     for i in range(warmup):
-        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws)
-    if profile:
-        moe.moe_profile_enable(layer, True, steps)
+        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream)
     torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    kern, ncalls = (moe.moe_profile_read(layer) if profile else ({}, 0))
-    if profile:
-        moe.moe_profile_enable(layer, False)
-    U_timed = [Us[i % 8] for i in range(steps)]
-    return dt, kern, ncalls, U_timed, x, lgs
+    dt_eager = time.perf_counter() - t0
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    graphs = []
+    for r in range(8):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            moe.moe_forward(layer, x, lgs[r], wl.top_k, act, y=y, ws=ws, stream=cap)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % 8].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % 8].replay()
+    torch.cuda.synchronize()
+    dt_graph = time.perf_counter() - t0
+    del graphs
+
+    moe.moe_profile_enable(layer, True, steps)
+    for i in range(steps):
+        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    kern, ncalls = moe.moe_profile_read(layer)
+    moe.moe_profile_enable(layer, False)
+    U = sum(Us[i % 8] for i in range(ncalls)) / max(ncalls, 1)
+    return {"dt_eager": dt_eager, "dt_graph": dt_graph, "kern": kern, "ncalls": ncalls, "U": U}
 
 
 def cpu_baseline(moe, torch, layer_dev_weights, wl, T, act, rows):
@@ -178,40 +207,42 @@ def main():
     torch.cuda.synchronize()
     log("weights ready in %.1f s" % (time.perf_counter() - t0))
 
-    dt, kern, ncalls, Us, _, _ = time_T(moe, torch, layer, wl, T, act, args.steps, args.warmup,
-                                        profile=True)
-    ms_step = dt * 1e3 / args.steps
-    value = T * args.steps / dt
-    g1_ms = kern["gemm1"] / max(ncalls, 1)
-    U_mean = sum(Us[:ncalls]) / max(ncalls, 1)
+    r = time_T(moe, torch, layer, wl, T, act, args.steps, args.warmup)
+    ms_step = r["dt_eager"] * 1e3 / args.steps
+    value = T * args.steps / r["dt_eager"]
+    ncalls = max(r["ncalls"], 1)
+    g1_ms = r["kern"]["gemm1"] / ncalls
+    U_mean = r["U"]
     g1_bytes = gemm1_bytes(layer, U_mean, T, wl.top_k, act)
     achieved = g1_bytes / (g1_ms * 1e-3) / 1e9
-    kernels_us = {k: round(v / max(ncalls, 1) * 1e3, 2) for k, v in kern.items()}
-    layer_gbs = layer_weight_bytes(layer, U_mean) / (ms_step * 1e-3) / 1e9
-    log("T=%d: %.1f us/step, %.0f tokens/s, gemm1 %.1f us (%.0f GB/s), kernels %s"
-        % (T, ms_step * 1e3, value, g1_ms * 1e3, achieved, kernels_us))
+    kernels_us = {k: round(v / ncalls * 1e3, 2) for k, v in r["kern"].items()}
+    log("T=%d: %.1f us/step (eager), %.1f graph, %.0f tokens/s, gemm1 %.1f us (%.0f GB/s), "
+        "kernels %s" % (T, ms_step * 1e3, r["dt_graph"] * 1e6 / args.steps, value, g1_ms * 1e3,
+                        achieved, kernels_us))
+
+    def entry(t, r):
+        nc = max(r["ncalls"], 1)
+        g1 = r["kern"]["gemm1"] / nc
+        d = r["dt_eager"] / args.steps
+        return {
+            "us_per_call": round(d * 1e6, 2),
+            "us_per_call_graph": round(r["dt_graph"] * 1e6 / args.steps, 2),
+            "tokens_per_s": round(t / d, 1),
+            "touched_experts": round(r["U"], 1),
+            "layer_weight_GBps": round(layer_weight_bytes(layer, r["U"]) / d / 1e9, 1),
+            "gemm1_us": round(g1 * 1e3, 2),
+            "gemm1_GBps": round(gemm1_bytes(layer, r["U"], t, wl.top_k, act) / (g1 * 1e-3) / 1e9, 1),
+            "kernels_us": {k: round(v / nc * 1e3, 2) for k, v in r["kern"].items()},
+        }
 
     sweep = {}
     if not args.no_sweep:
         for t in wl.Ts:
             if t == T:
                 continue
-            d, kk, nc, us, _, _ = time_T(moe, torch, layer, wl, t, act, args.steps, args.warmup,
-                                         profile=True)
-            um = sum(us[:nc]) / max(nc, 1)
-            g1 = kk["gemm1"] / max(nc, 1)
-            sweep[str(t)] = {
-                "us_per_call": round(d * 1e6 / args.steps, 2),
-                "tokens_per_s": round(t * args.steps / d, 1),
-                "touched_experts": round(um, 1),
-                "layer_weight_GBps": round(layer_weight_bytes(layer, um) / (d / args.steps) / 1e9, 1),
-                "gemm1_us": round(g1 * 1e3, 2),
-                "gemm1_GBps": round(gemm1_bytes(layer, um, t, wl.top_k, act) / (g1 * 1e-3) / 1e9, 1),
-            }
+            sweep[str(t)] = entry(t, time_T(moe, torch, layer, wl, t, act, args.steps, args.warmup))
             log("T=%d: %s" % (t, sweep[str(t)]))
-    sweep[str(T)] = {"us_per_call": round(ms_step * 1e3, 2), "tokens_per_s": round(value, 1),
-                     "touched_experts": round(U_mean, 1), "layer_weight_GBps": round(layer_gbs, 1),
-                     "gemm1_us": round(g1_ms * 1e3, 2), "gemm1_GBps": round(achieved, 1)}
+    sweep[str(T)] = entry(T, r)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -227,6 +258,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_graph": round(r["dt_graph"] * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -17,20 +17,22 @@ namespace moe {
 // which equals the full softmax renormalised over the picks (the softmax
 // denominator over all E cancels).
 // ---------------------------------------------------------------------------
+// Lane l of a wave holds logits l, l + 64, ... of one token row.
 template <int NV>
-__global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ logits, int T, int E,
-                                                    int top_k, int32_t *__restrict__ ids,
-                                                    float *__restrict__ wts) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long t = (long)blockIdx.x * 4 + wave;
-  if (t >= T) return;  // wave-uniform; no barriers below
-  const float *row = logits + t * E;
-  float v[NV];
+__device__ __forceinline__ void load_logits(const float *__restrict__ row, int E, int lane,
+                                            float v[NV]) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
     v[i] = e < E ? row[e] : 0.0f;
   }
+}
+
+// One wave routes the token whose logits it holds (load_logits); lanes <
+// top_k write ids[j], w[j].
+template <int NV>
+__device__ __forceinline__ void route_values(const float v[NV], int E, int top_k, int lane,
+                                             int32_t *__restrict__ ids, float *__restrict__ wts) {
   uint32_t taken = 0;
   float selv[8];
   int seli[8];
@@ -83,9 +85,21 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ lo
         id = seli[j];
         e = ex[j];
       }
-    ids[t * top_k + lane] = id;
-    wts[t * top_k + lane] = (float)(e / sum);
+    ids[lane] = id;
+    wts[lane] = (float)(e / sum);
   }
+}
+
+template <int NV>
+__global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ logits, int T, int E,
+                                                    int top_k, int32_t *__restrict__ ids,
+                                                    float *__restrict__ wts) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long t = (long)blockIdx.x * 4 + wave;
+  if (t >= T) return;  // wave-uniform; no barriers below
+  float v[NV];
+  load_logits<NV>(logits + t * E, E, lane, v);
+  route_values<NV>(v, E, top_k, lane, ids + t * top_k, wts + t * top_k);
 }
 
 hipError_t launch_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w,
@@ -245,12 +259,11 @@ hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, cons
 // E8M0 scales, once per token before dispatch).  One thread per 32-element
 // block: amax over the bit patterns, block exponent, RNE encode.
 // ---------------------------------------------------------------------------
+// 1x32 block b of the row-major bf16 matrix x.
 template <class F>
-__global__ __launch_bounds__(256) void quant_kernel(const uint16_t *__restrict__ x, long nblocks,
-                                                    uint8_t *__restrict__ codes,
-                                                    uint8_t *__restrict__ scales) {
-  const long b = (long)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblocks) return;
+__device__ __forceinline__ void quant_block(const uint16_t *__restrict__ x, long b,
+                                            uint8_t *__restrict__ codes,
+                                            uint8_t *__restrict__ scales) {
   const uint4 *src = reinterpret_cast<const uint4 *>(x + b * 32);
   uint32_t w[16];
 #pragma unroll
@@ -300,6 +313,14 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t *__restrict__
   scales[b] = (uint8_t)(X + 127);
 }
 
+template <class F>
+__global__ __launch_bounds__(256) void quant_kernel(const uint16_t *__restrict__ x, long nblocks,
+                                                    uint8_t *__restrict__ codes,
+                                                    uint8_t *__restrict__ scales) {
+  const long b = (long)blockIdx.x * 256 + threadIdx.x;
+  if (b < nblocks) quant_block<F>(x, b, codes, scales);
+}
+
 hipError_t launch_quant(const uint16_t *x, long rows, int K, int act, uint8_t *codes,
                         uint8_t *scales, hipStream_t s) {
   const long nblocks = rows * (K / 32);
@@ -309,6 +330,116 @@ hipError_t launch_quant(const uint16_t *x, long rows, int K, int act, uint8_t *c
     quant_kernel<E4M3><<<grid, 256, 0, s>>>(x, nblocks, codes, scales);
   else
     quant_kernel<E2M1><<<grid, 256, 0, s>>>(x, nblocks, codes, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Steps 1-3 in one launch for T <= kSortBlock tokens (decode sizes), where
+// separate launches would cost more than the work: workgroup 0 routes every
+// token (one wave per token) and sorts the assignments exactly as the
+// hist/scan/scatter kernels do for a single sort block; workgroups 1.. quantise
+// the token rows.  The outputs are the same as those kernels' outputs.
+// ---------------------------------------------------------------------------
+template <int NV>
+__global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x > 0) {
+    const long nblocks = (long)p.T * (p.H / 32);
+    const long stride = (long)(gridDim.x - 1) * 1024;
+    for (long b = (long)(blockIdx.x - 1) * 1024 + tid; b < nblocks; b += stride) {
+      if (p.act == MOE_ACT_MXFP8_E4M3)
+        quant_block<E4M3>(p.x, b, p.codes, p.scales);
+      else
+        quant_block<E2M1>(p.x, b, p.codes, p.scales);
+    }
+    return;
+  }
+  __shared__ int32_t sid[kSortBlock * 8];
+  __shared__ float sw[kSortBlock * 8];
+  __shared__ int32_t cnt[1024], sc[1024], sm[1024];
+  __shared__ unsigned long long masks[4][1024];
+  const int wave = tid >> 6, lane = tid & 63;
+  const int T = p.T, E = p.E, k = p.top_k, N = T * k;
+  for (int e = tid; e < E; e += 1024) {
+    cnt[e] = 0;
+    masks[0][e] = 0ull; masks[1][e] = 0ull; masks[2][e] = 0ull; masks[3][e] = 0ull;
+  }
+  // wave w routes tokens w, w + 16, ...; the logits of four of them are
+  // loaded before the first is routed
+  for (int t0 = wave; t0 < T; t0 += 64) {
+    float v[4][NV];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (t0 + 16 * u < T) load_logits<NV>(p.logits + (long)(t0 + 16 * u) * E, E, lane, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + 16 * u;
+      if (t < T) route_values<NV>(v[u], E, k, lane, sid + t * k, sw + t * k);
+    }
+  }
+  __syncthreads();
+  for (int a = tid; a < N; a += 1024) {
+    p.ids[a] = sid[a];
+    p.wts[a] = sw[a];
+    atomicAdd(&cnt[sid[a]], 1);
+  }
+  __syncthreads();
+  const int c = tid < E ? cnt[tid] : 0;
+  const int m = (c + p.bm - 1) / p.bm;
+  sc[tid] = c;
+  sm[tid] = m;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int ac = tid >= d ? sc[tid - d] : 0;
+    const int am = tid >= d ? sm[tid - d] : 0;
+    __syncthreads();
+    sc[tid] += ac;
+    sm[tid] += am;
+    __syncthreads();
+  }
+  if (tid < E) {
+    p.counts[tid] = c;
+    p.offsets[tid] = sc[tid] - c;
+    p.mtoff[tid] = sm[tid] - m;
+    if (tid == E - 1) {
+      p.offsets[E] = sc[tid];
+      p.mtoff[E] = sm[tid];
+    }
+    for (int i = 0; i < m; ++i) p.mbexp[sm[tid] - m + i] = tid;
+  }
+  const unsigned long long bit = 1ull << lane;
+  if (tid < T)
+    for (int j = 0; j < k; ++j) atomicOr(&masks[wave][sid[tid * k + j]], bit);
+  __syncthreads();
+  if (tid < T) {
+    for (int j = 0; j < k; ++j) {
+      const int a = tid * k + j, e = sid[a];
+      int r = __popcll(masks[wave][e] & (bit - 1ull));
+      for (int w = 0; w < wave; ++w) r += __popcll(masks[w][e]);
+      const int pos = sc[e] - cnt[e] + r;
+      p.perm[pos] = a;
+      p.inv[a] = pos;
+      p.wsorted[pos] = sw[a];
+    }
+  }
+}
+
+hipError_t launch_front(const FrontArgs &a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if (a.T > kSortBlock || a.E > 1024 || a.top_k > 8) return hipErrorInvalidValue;
+  const long nq = ((long)a.T * (a.H / 32) + 1023) / 1024;
+  const dim3 grid((unsigned)(1 + nq)), block(1024);
+#define FRONT_CASE(NV_)                                \
+  case NV_:                                            \
+    front_kernel<NV_><<<grid, block, 0, s>>>(a);       \
+    break;
+  switch (ceil_div(a.E, 64)) {
+    FRONT_CASE(1) FRONT_CASE(2) FRONT_CASE(3) FRONT_CASE(4) FRONT_CASE(5) FRONT_CASE(6)
+    FRONT_CASE(7) FRONT_CASE(8) FRONT_CASE(9) FRONT_CASE(10) FRONT_CASE(11) FRONT_CASE(12)
+    FRONT_CASE(13) FRONT_CASE(14) FRONT_CASE(15) FRONT_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef FRONT_CASE
   return hipGetLastError();
 }
 

@@ -86,7 +86,7 @@ __device__ __forceinline__ v8i load_a(const uint8_t *__restrict__ row, int s, in
 }
 
 // acc[q] += A(rows of this lane's m-tile) x B(prepacked tile q of one quad)
-// over the K steps [s0, s1).
+// over the K steps [s0, s1), four steps per unrolled group.
 template <int FMT>
 __device__ __forceinline__ void mma_4tiles(v4f acc[4], const uint8_t *__restrict__ arow,
                                            const uint8_t *__restrict__ asrow,
@@ -94,18 +94,24 @@ __device__ __forceinline__ void mma_4tiles(v4f acc[4], const uint8_t *__restrict
                                            const uint32_t *__restrict__ wsq, size_t tile_bytes,
                                            int s0, int s1, int lane) {
   const int g = lane >> 4;
-  for (int s = s0; s < s1; ++s) {
-    const v8i a = load_a<FMT>(arow, s, g);
-    const int sa = asrow[4 * s + g];
-    const int sb = (int)wsq[(size_t)s * 64 + lane];
+  for (int s4 = s0; s4 < s1; s4 += 4) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 bq = *reinterpret_cast<const uint4 *>(wt + q * tile_bytes +
-                                                       ((size_t)s * 64 + lane) * 16);
-      v8i b;
-      b[0] = (int)bq.x; b[1] = (int)bq.y; b[2] = (int)bq.z; b[3] = (int)bq.w;
-      b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
-      acc[q] = mfma_q<FMT>(q, a, b, acc[q], sa, sb);
+    for (int u = 0; u < 4; ++u) {
+      const int s = s4 + u;
+      if (s < s1) {
+        const v8i a = load_a<FMT>(arow, s, g);
+        const int sa = asrow[4 * s + g];
+        const int sb = (int)wsq[(size_t)s * 64 + lane];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 bq = *reinterpret_cast<const uint4 *>(wt + q * tile_bytes +
+                                                           ((size_t)s * 64 + lane) * 16);
+          v8i b;
+          b[0] = (int)bq.x; b[1] = (int)bq.y; b[2] = (int)bq.z; b[3] = (int)bq.w;
+          b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
+          acc[q] = mfma_q<FMT>(q, a, b, acc[q], sa, sb);
+        }
+      }
     }
   }
 }

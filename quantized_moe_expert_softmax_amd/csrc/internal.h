@@ -96,6 +96,19 @@ hipError_t launch_sort_scan(int32_t *hist, int nb, int E, int32_t *counts, int32
 hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, const int32_t *hist,
                                int32_t *perm, int32_t *inv, const float *w, float *wsorted,
                                hipStream_t s);
+// Fused route + sort + quant for T <= kSortBlock (same outputs as the
+// separate kernels; hist is not used).
+struct FrontArgs {
+  const float *logits;
+  const uint16_t *x;
+  int T, E, top_k, H, act, bm;
+  int32_t *ids;
+  float *wts;
+  int32_t *counts, *offsets, *mtoff, *mbexp, *perm, *inv;
+  float *wsorted;
+  uint8_t *codes, *scales;
+};
+hipError_t launch_front(const FrontArgs &a, hipStream_t s);
 hipError_t launch_quant(const uint16_t *x, long rows, int K, int act, uint8_t *codes,
                         uint8_t *scales, hipStream_t s);
 hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int E, int R, int K,

@@ -216,19 +216,32 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
     ++stage;
   };
   mark();
-  if (e == hipSuccess) e = launch_route(logits, T, L->E, top_k, ids, wts, s);
-  mark();
-  if (e == hipSuccess) e = launch_sort_hist(ids, T, L->E, top_k, hist, W.nb, s);
-  mark();
-  if (e == hipSuccess)
-    e = launch_sort_scan(hist, W.nb, L->E, counts, offsets, mtoff, mbexp, g.plan.bm(), s);
-  mark();
-  if (e == hipSuccess)
-    e = launch_sort_scatter(ids, T, L->E, top_k, hist, perm, inv, wts, wsorted, s);
-  mark();
-  if (e == hipSuccess)
-    e = launch_quant(static_cast<const uint16_t *>(x), T, L->H, act, a1c, a1s, s);
-  mark();
+  if (T <= kSortBlock) {
+    // decode sizes: route, sort and quantisation in one launch (its time is
+    // recorded as the route stage; the sort and quant stages record ~0)
+    FrontArgs f{};
+    f.logits = logits; f.x = static_cast<const uint16_t *>(x);
+    f.T = T; f.E = L->E; f.top_k = top_k; f.H = L->H; f.act = act; f.bm = g.plan.bm();
+    f.ids = ids; f.wts = wts; f.counts = counts; f.offsets = offsets; f.mtoff = mtoff;
+    f.mbexp = mbexp; f.perm = perm; f.inv = inv; f.wsorted = wsorted; f.codes = a1c;
+    f.scales = a1s;
+    if (e == hipSuccess) e = launch_front(f, s);
+    for (int i = 0; i < 5; ++i) mark();
+  } else {
+    if (e == hipSuccess) e = launch_route(logits, T, L->E, top_k, ids, wts, s);
+    mark();
+    if (e == hipSuccess) e = launch_sort_hist(ids, T, L->E, top_k, hist, W.nb, s);
+    mark();
+    if (e == hipSuccess)
+      e = launch_sort_scan(hist, W.nb, L->E, counts, offsets, mtoff, mbexp, g.plan.bm(), s);
+    mark();
+    if (e == hipSuccess)
+      e = launch_sort_scatter(ids, T, L->E, top_k, hist, perm, inv, wts, wsorted, s);
+    mark();
+    if (e == hipSuccess)
+      e = launch_quant(static_cast<const uint16_t *>(x), T, L->H, act, a1c, a1s, s);
+    mark();
+  }
   if (e == hipSuccess) e = launch_gemm1(g, s);
   mark();
   if (e == hipSuccess) e = launch_gemm2(g, s);

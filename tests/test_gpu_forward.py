@@ -82,6 +82,8 @@ CASES = [
     (3, 128, 128, 1, 1),
     (130, 512, 640, 32, 8),
     (1, 1024, 1152, 64, 6),
+    # more than one 256-token sort block: the separate route/sort/quant kernels
+    (300, 256, 256, 16, 4),
 ]
 
 
