@@ -463,14 +463,15 @@ __global__ __launch_bounds__(256) void prepack_codes_kernel(const uint8_t *__res
                                                             uint8_t *__restrict__ dst) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
-  const int steps = K / 128, ntile = R / 16;
+  const int steps = K / 128, nquad = R / 64;
   const int lane = (int)(idx & 63);
-  const long rest = idx >> 6;
+  const int q = (int)((idx >> 6) & 3);
+  const long rest = idx >> 8;
   const int s = (int)(rest % steps);
   const long rest2 = rest / steps;
-  const int tile = (int)(rest2 % ntile);
-  const long e = rest2 / ntile;
-  const long row = packed_row(tile, lane & 15, R / 2, gate_up);
+  const int u = (int)(rest2 % nquad);
+  const long e = rest2 / nquad;
+  const long row = packed_row(4 * u + q, lane & 15, R / 2, gate_up);
   const uint8_t *p = src + (e * R + row) * (long)(K / 2) + 64 * s + 16 * (lane >> 4);
   *reinterpret_cast<uint4 *>(dst + idx * 16) = *reinterpret_cast<const uint4 *>(p);
 }
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(256) void prepack_scales_kernel(const uint8_t *__re
 hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int E, int R, int K,
                           bool gate_up, uint8_t *pcodes, uint8_t *pscales, hipStream_t s) {
   const PackDims d = pack_dims(R, K);
-  const long nc = (long)E * (R / 16) * d.steps * 64;
+  const long nc = (long)E * (R / 64) * d.steps * 256;
   const long ns = (long)E * (R / 64) * d.steps * 64;
   prepack_codes_kernel<<<(unsigned)((nc + 255) / 256), 256, 0, s>>>(codes, nc, R, K, gate_up,
                                                                    pcodes);

@@ -91,8 +91,8 @@ template <int FMT>
 __device__ __forceinline__ void mma_4tiles(v4f acc[4], const uint8_t *__restrict__ arow,
                                            const uint8_t *__restrict__ asrow,
                                            const uint8_t *__restrict__ wt,
-                                           const uint32_t *__restrict__ wsq, size_t tile_bytes,
-                                           int s0, int s1, int lane) {
+                                           const uint32_t *__restrict__ wsq, int s0, int s1,
+                                           int lane) {
   const int g = lane >> 4;
   for (int s4 = s0; s4 < s1; s4 += 4) {
 #pragma unroll
@@ -104,8 +104,8 @@ __device__ __forceinline__ void mma_4tiles(v4f acc[4], const uint8_t *__restrict
         const int sb = (int)wsq[(size_t)s * 64 + lane];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint4 bq = *reinterpret_cast<const uint4 *>(wt + q * tile_bytes +
-                                                           ((size_t)s * 64 + lane) * 16);
+          const uint4 bq = *reinterpret_cast<const uint4 *>(wt + (size_t)s * 4096 + q * 1024 +
+                                                           lane * 16);
           v8i b;
           b[0] = (int)bq.x; b[1] = (int)bq.y; b[2] = (int)bq.z; b[3] = (int)bq.w;
           b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
@@ -174,20 +174,19 @@ struct ActFmt<0> { using F = E4M3; };
 template <>
 struct ActFmt<4> { using F = E2M1; };
 
-template <int FMT>
-__global__ __launch_bounds__(256) void gemm1_kernel(KArgs p) {
+template <int FMT, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm1_kernel(KArgs p) {
   using F = typename ActFmt<FMT>::F;
-  __shared__ float red[4][16][64];
+  __shared__ float red[NW][16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int NU = p.I / 32;
   const int n_mt = uniform(p.mtoff[p.E]);
   const long total = (long)n_mt * NU;
   const int S = p.H / 128;
-  const int s0 = wave * S / 4, s1 = (wave + 1) * S / 4;
+  const int s0 = wave * S / NW, s1 = (wave + 1) * S / NW;
   const size_t a1row = FMT == 0 ? (size_t)p.H : (size_t)p.H / 2;
   const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
-  const size_t ntiles = (size_t)(2 * p.I) / 16;
-  const size_t tile_bytes = (size_t)S * 1024;
+  const size_t nquads = (size_t)(2 * p.I) / 64;
   for (long w = blockIdx.x; w < total; w += gridDim.x) {
     const int j = (int)(w / n_mt), mt = (int)(w % n_mt);
     const int e = uniform(p.mbexp[mt]);
@@ -197,12 +196,12 @@ __global__ __launch_bounds__(256) void gemm1_kernel(KArgs p) {
     const int tok = p.perm[pr] / p.top_k;
     const uint8_t *arow = p.a1c + (size_t)tok * a1row;
     const uint8_t *asrow = p.a1s + (size_t)tok * (p.H / 32);
-    const uint8_t *wt = p.wp + ((size_t)e * ntiles + 4 * (size_t)j) * tile_bytes;
-    const uint32_t *wsq = p.wsp + ((size_t)e * (ntiles / 4) + j) * (size_t)S * 64;
+    const uint8_t *wt = p.wp + ((size_t)e * nquads + j) * (size_t)S * 4096;
+    const uint32_t *wsq = p.wsp + ((size_t)e * nquads + j) * (size_t)S * 64;
     v4f acc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
-    mma_4tiles<FMT>(acc, arow, asrow, wt, wsq, tile_bytes, s0, s1, lane);
+    mma_4tiles<FMT>(acc, arow, asrow, wt, wsq, s0, s1, lane);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -211,8 +210,11 @@ __global__ __launch_bounds__(256) void gemm1_kernel(KArgs p) {
     if (wave == 0) {
       float v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        v[i] = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
+      for (int i = 0; i < 16; ++i) {
+        v[i] = red[0][i][lane];
+#pragma unroll
+        for (int u = 1; u < NW; ++u) v[i] += red[u][i][lane];
+      }
       const int c = lane & 15;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -227,18 +229,17 @@ __global__ __launch_bounds__(256) void gemm1_kernel(KArgs p) {
   }
 }
 
-template <int FMT>
-__global__ __launch_bounds__(256) void gemm2_kernel(KArgs p) {
-  __shared__ float red[4][16][64];
+template <int FMT, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm2_kernel(KArgs p) {
+  __shared__ float red[NW][16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int NB = p.H / 64;
   const int n_mt = uniform(p.mtoff[p.E]);
   const long total = (long)n_mt * NB;
   const int S = p.I / 128;
-  const int s0 = wave * S / 4, s1 = (wave + 1) * S / 4;
+  const int s0 = wave * S / NW, s1 = (wave + 1) * S / NW;
   const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
-  const size_t ntiles = (size_t)p.H / 16;
-  const size_t tile_bytes = (size_t)S * 1024;
+  const size_t nquads = (size_t)p.H / 64;
   for (long w = blockIdx.x; w < total; w += gridDim.x) {
     const int nb = (int)(w / n_mt), mt = (int)(w % n_mt);
     const int e = uniform(p.mbexp[mt]);
@@ -247,12 +248,12 @@ __global__ __launch_bounds__(256) void gemm2_kernel(KArgs p) {
     const size_t pr = (size_t)(row0 + min(lane & 15, nrows - 1));
     const uint8_t *arow = p.a2c + pr * a2row;
     const uint8_t *asrow = p.a2s + pr * (p.I / 32);
-    const uint8_t *wt = p.wp + ((size_t)e * ntiles + 4 * (size_t)nb) * tile_bytes;
-    const uint32_t *wsq = p.wsp + ((size_t)e * (ntiles / 4) + nb) * (size_t)S * 64;
+    const uint8_t *wt = p.wp + ((size_t)e * nquads + nb) * (size_t)S * 4096;
+    const uint32_t *wsq = p.wsp + ((size_t)e * nquads + nb) * (size_t)S * 64;
     v4f acc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
-    mma_4tiles<FMT>(acc, arow, asrow, wt, wsq, tile_bytes, s0, s1, lane);
+    mma_4tiles<FMT>(acc, arow, asrow, wt, wsq, s0, s1, lane);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -269,7 +270,9 @@ __global__ __launch_bounds__(256) void gemm2_kernel(KArgs p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int i = 4 * q + r;
-          const float o = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
+          float o = red[0][i][lane];
+#pragma unroll
+          for (int u = 1; u < NW; ++u) o += red[u][i][lane];
           dst[16 * q] = wt_a * o;
         }
       }
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
   const size_t arow = FMT == 0 ? (size_t)K : (size_t)K / 2;
   const size_t srow = (size_t)K / 32;
   const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
-  const size_t tile_bytes = (size_t)S * 1024, quad_dwords = (size_t)S * 64;
+  const size_t quad_bytes = (size_t)S * 4096, quad_dwords = (size_t)S * 64;
   const uint8_t *__restrict__ A = SECOND ? p.a2c : p.a1c;
   const uint8_t *__restrict__ As = SECOND ? p.a2s : p.a1s;
   const int G = gridDim.x;
@@ -395,15 +398,15 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
     }
     const int tile0 = 16 * nb + 4 * wave;
     const bool active = tile0 < ntiles;
-    const size_t tbase = (size_t)e * ntiles + (active ? tile0 : 0);
-    const uint8_t *wsrc = p.wp + tbase * tile_bytes + (size_t)lane * 16;
-    const uint32_t *wssrc = p.wsp + (tbase / 4) * quad_dwords + lane;
+    const size_t qbase = (size_t)e * (ntiles / 4) + (active ? tile0 / 4 : 0);
+    const uint8_t *wsrc = p.wp + qbase * quad_bytes + (size_t)lane * 16;
+    const uint32_t *wssrc = p.wsp + qbase * quad_dwords + lane;
 
     // Copies of K step s into stage buffer s % NS.  Past the last step the
     // same number of copies is issued from one fixed address (every lane
     // reads the same 16 bytes) into a buffer no step reads any more, so each
     // loop iteration issues exactly C copies and one wait count fits all.
-    const uint8_t *dummy = p.wp + tbase * tile_bytes;
+    const uint8_t *dummy = p.wp + qbase * quad_bytes;
     // copy i (0 <= i < C) of K step s: activation chunks, the activation
     // scale dword, the four weight fragments, the four weight scale dwords
     auto issue_one = [&](int s, int i) __attribute__((always_inline)) {
@@ -416,7 +419,7 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
         copy4_to_lds(real ? ssrc + 4 * s : dummy, st + TS::OFF_AS + wave * 256);
       } else if (i < TS::A_COPIES + 5) {
         const int q = i - TS::A_COPIES - 1;
-        copy16_to_lds(real ? wsrc + q * tile_bytes + (size_t)s * 1024 : dummy,
+        copy16_to_lds(real ? wsrc + (size_t)s * 4096 + q * 1024 : dummy,
                       st + TS::OFF_B + wave * 4096 + q * 1024);
       } else {
         copy4_to_lds(real ? (const void *)(wssrc + (size_t)s * 64) : (const void *)dummy,
@@ -567,6 +570,15 @@ static KArgs make_args(const GemmArgs &a, bool second) {
   return k;
 }
 
+// Waves per stream workgroup (each takes 1/NW of the K steps).  Measured on
+// the 7168 x 3072 layer: GEMM1 runs faster with eight once there are more
+// items than four per CU (below that, eight-wave workgroups at two per CU
+// leave part of the items for a second round); GEMM2 (K = I, a third of
+// GEMM1's steps) is faster with four at every decode size.
+static int stream_waves(long items_upper, int num_cus, bool second) {
+  return !second && items_upper > 4L * num_cus ? 8 : 4;
+}
+
 static unsigned persistent_grid(long items_upper, int num_cus) {
   const long cap = (long)num_cus * 4;
   return (unsigned)(items_upper < cap ? items_upper : cap);
@@ -598,18 +610,32 @@ static hipError_t launch_tiled(const GemmArgs &a, const KArgs &k, hipStream_t s)
 hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s) {
   const KArgs k = make_args(a, false);
   if (a.plan.tiled) return launch_tiled<false>(a, k, s);
-  const unsigned grid = persistent_grid(a.max_mtiles * (a.I / 32), a.num_cus);
-  if (a.act == MOE_ACT_MXFP8_E4M3) gemm1_kernel<0><<<grid, 256, 0, s>>>(k);
-  else gemm1_kernel<4><<<grid, 256, 0, s>>>(k);
+  const long items = a.max_mtiles * (a.I / 32);
+  const unsigned grid = persistent_grid(items, a.num_cus);
+  const bool f8 = a.act == MOE_ACT_MXFP8_E4M3;
+  if (stream_waves(items, a.num_cus, false) == 8) {
+    if (f8) gemm1_kernel<0, 8><<<grid, 512, 0, s>>>(k);
+    else gemm1_kernel<4, 8><<<grid, 512, 0, s>>>(k);
+  } else {
+    if (f8) gemm1_kernel<0, 4><<<grid, 256, 0, s>>>(k);
+    else gemm1_kernel<4, 4><<<grid, 256, 0, s>>>(k);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s) {
   const KArgs k = make_args(a, true);
   if (a.plan.tiled) return launch_tiled<true>(a, k, s);
-  const unsigned grid = persistent_grid(a.max_mtiles * (a.H / 64), a.num_cus);
-  if (a.act == MOE_ACT_MXFP8_E4M3) gemm2_kernel<0><<<grid, 256, 0, s>>>(k);
-  else gemm2_kernel<4><<<grid, 256, 0, s>>>(k);
+  const long items = a.max_mtiles * (a.H / 64);
+  const unsigned grid = persistent_grid(items, a.num_cus);
+  const bool f8 = a.act == MOE_ACT_MXFP8_E4M3;
+  if (stream_waves(items, a.num_cus, true) == 8) {
+    if (f8) gemm2_kernel<0, 8><<<grid, 512, 0, s>>>(k);
+    else gemm2_kernel<4, 8><<<grid, 512, 0, s>>>(k);
+  } else {
+    if (f8) gemm2_kernel<0, 4><<<grid, 256, 0, s>>>(k);
+    else gemm2_kernel<4, 4><<<grid, 256, 0, s>>>(k);
+  }
   return hipGetLastError();
 }
 

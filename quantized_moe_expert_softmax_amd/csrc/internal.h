@@ -16,12 +16,14 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 // Prepacked weight layout of one matrix of R rows and K columns (R % 64 == 0,
-// K % 128 == 0): codes [R/16 n-tiles][K/128 steps][64 lanes][16 B], scales
-// [R/64 tile quads][K/128 steps][64 lanes][4 B].  Lane l = 16*g + c of tile t
-// holds row 16*t + c, columns [128*step + 32*g, +32) (the gfx950 scaled-MFMA
-// B operand of one 16x16x128 step); byte q of lane l's scale dword of quad u
-// is the E8M0 scale of that lane's block in tile 4*u + q (the MFMA picks the
-// byte with its scale op_sel, so one dword serves the four tiles a wave owns).
+// K % 128 == 0), in quads of four 16-row tiles (tile t = 4*u + q): codes
+// [R/64 quads u][K/128 steps][4 tiles q][64 lanes][16 B], scales [R/64][K/128
+// steps][64 lanes][4 B].  Lane l = 16*g + c of tile t holds row 16*t + c,
+// columns [128*step + 32*g, +32) (the gfx950 scaled-MFMA B operand of one
+// 16x16x128 step), so one K step of a quad is 4 KiB contiguous and a quad's
+// steps follow each other; byte q of lane l's scale dword is the E8M0 scale
+// of that lane's block in tile q (the MFMA picks the byte with its scale
+// op_sel, so one dword serves the four tiles a wave owns).
 struct PackDims {
   int R, K, steps;
   size_t code_bytes_per_tile() const { return (size_t)steps * 1024; }
@@ -129,7 +131,7 @@ GemmPlan choose_plan(int T, int top_k, int E, int act);
 struct GemmArgs {
   int T, top_k, E, H, I, act;
   GemmPlan plan;
-  long max_mtiles;  // host upper bound of m-blocks (N/bm + E)
+  long max_mtiles;  // host upper bound of m-blocks (ceil(N/bm) + min(N, E))
   int num_cus;
   const uint8_t *a1c, *a1s;
   uint8_t *a2c, *a2s;

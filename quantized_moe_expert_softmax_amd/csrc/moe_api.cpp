@@ -200,7 +200,10 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
   GemmArgs g{};
   g.T = T; g.top_k = top_k; g.E = L->E; g.H = L->H; g.I = L->I; g.act = act;
   g.plan = choose_plan(T, top_k, L->E, act);
-  g.max_mtiles = ((long)T * top_k + g.plan.bm() - 1) / g.plan.bm() + L->E;
+  {  // each non-empty expert adds at most one partial m-block
+    const long N = (long)T * top_k;
+    g.max_mtiles = (N + g.plan.bm() - 1) / g.plan.bm() + (N < L->E ? N : L->E);
+  }
   g.num_cus = L->num_cus;
   g.a1c = a1c; g.a1s = a1s; g.a2c = a2c; g.a2s = a2s;
   g.perm = perm; g.offsets = offsets; g.mtoff = mtoff; g.mbexp = mbexp; g.wts = wsorted;
