@@ -40,6 +40,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "quantized_moe_expert_softmax_amd", "csrc")
+# sources that decide GEMM1's memory traffic: the kernels, the weight layout
+GEMM_SOURCES = ("gemm.hip", "prepack.hip", "mx_device.h", "internal.h")
 
 
 def log(*a):
@@ -72,6 +76,39 @@ def copy_calibration(torch, mib, reps=3):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": n, "reps": reps}), flush=True)
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, T, act):
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 --pmc summary
+    (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by what the
+    same counter reads for a plain copy of known size), or (None, None) when
+    there is none for this workload or the GEMM sources changed since the
+    counters were taken."""
+    import glob
+    src = gemm_source_hash()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                line = line.strip()
+                if not line.startswith("traffic:"):
+                    continue
+                kv = dict(t.split("=", 1) for t in line[len("traffic:"):].split())
+                if (kv.get("kernel") == "gemm1" and kv.get("workload") == workload
+                        and int(kv.get("T", -1)) == T and int(kv.get("act", -1)) == act
+                        and kv.get("source") == src):
+                    b = (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
+                         float(kv["write_kib"]) * float(kv["write_scale"])) * 1024.0
+                    return b, os.path.relpath(path, ROOT)
+    return None, None
 
 
 def touched_experts(moe, layer, ws, T, top_k, act):
@@ -248,6 +285,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         cpu = cpu_baseline(moe, torch, w, wl, T, act, args.cpu_rows)
+    traffic, traffic_src = measured_traffic(wl.name, T, act)
     dtype = "mxfp8xmxfp4" if act == 0 else "mxfp4xmxfp4"
     line = {
         "metric": "MoE layer tokens/s at T=%d (%s) on one MI355X; us/call vs T in sweep"
@@ -269,7 +307,8 @@ def main():
             "global_batch": T, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "gemm1", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": int(g1_bytes),
+                     "traffic": None if traffic is None else int(traffic),
+                     "traffic_source": traffic_src, "bytes_per_launch": int(g1_bytes),
                      "avg_launch_us": round(g1_ms * 1e3, 2)},
         "kernels_us": kernels_us,
         "sweep": sweep,

@@ -322,6 +322,12 @@ __device__ __forceinline__ void barrier_keep_copies() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
   __builtin_amdgcn_s_barrier();
 }
+// LDS of the tiled kernel: a ring of NA activation stages (the BM rows of
+// one K step and their scale dwords) and a ring of NB weight stages (each
+// wave's four 1 KiB fragments and scale dword).  Weights stream from HBM and
+// are fetched NB - 1 steps ahead, activations come from L2 and are fetched
+// NA - 1 = 2 steps ahead.  (Weight rings deeper than 4 fit in 160 KiB but
+// measured slower on the 7168 x 3072 layer.)
 template <int FMT, int MT>
 struct TileShape {
   static constexpr int BM = 16 * MT;
@@ -330,13 +336,23 @@ struct TileShape {
   static constexpr int A_BYTES = BM * ROWB;
   static constexpr int A_COPIES = A_BYTES / 4096;    // 1 KiB copies per wave per stage
   static constexpr int RPW = BM / 4;                 // scale rows copied per wave
-  static constexpr int C = A_COPIES + 1 + 4 + 1;     // copies per wave per stage
+  static constexpr int CA = A_COPIES + 1;            // activation copies per wave per step
+  static constexpr int CB = 4 + 1;                   // weight copies per wave per step
+  static constexpr int C = CA + CB;
   static constexpr int OFF_AS = A_BYTES;             // [4 waves][64 slots] dwords
-  static constexpr int OFF_B = OFF_AS + 1024;        // [4 waves][4 tiles] 1 KiB fragments
-  static constexpr int OFF_BS = OFF_B + 4 * 4096;    // [4 waves][64 lanes] scale dwords
-  static constexpr int STAGE = OFF_BS + 4 * 256;
+  static constexpr int A_STAGE = OFF_AS + 1024;
+  static constexpr int OFF_BS = 4 * 4096;            // after [4 waves][4 tiles] fragments
+  static constexpr int B_STAGE = OFF_BS + 4 * 256;   // + [4 waves][64 lanes] scale dwords
+  static constexpr int NA = 3;
+  static constexpr int NB_FIT = (160 * 1024 - NA * A_STAGE) / B_STAGE;
+  static constexpr int NB = NB_FIT < 4 ? NB_FIT : 4;  // deeper measured slower
+  static constexpr int D = NB - NA;                  // weight lead over activations, in steps
+  static constexpr int B_BASE = NA * A_STAGE;
+  static constexpr int LDS = B_BASE + NB * B_STAGE;
   static_assert(A_BYTES % 4096 == 0, "activation tile must fill whole copies");
   static_assert(RPW <= 64, "scale rows per wave");
+  static_assert(D >= 1, "weights must lead activations");
+  static_assert((NA - 1) * CA + (NB - 1) * CB < 64, "vmcnt range");
   // LDS slot of row r's scale dword
   static __device__ __forceinline__ int sslot(int r) { return (r / RPW) * 64 + (r % RPW); }
 };
@@ -345,18 +361,18 @@ template <int FMT, int MT, bool SECOND>
 __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
   using F = typename ActFmt<FMT>::F;
   using TS = TileShape<FMT, MT>;
-  constexpr int NS = 4;  // K steps in flight
+  constexpr int NA = TS::NA, NB = TS::NB, D = TS::D;
   constexpr int BM = TS::BM, ROWB = TS::ROWB, CH = TS::CH;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * TS::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[TS::LDS];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, r16 = lane & 15;
   const int K = SECOND ? p.I : p.H;
   const int S = K / 128;
   const int ntiles = (SECOND ? p.H : 2 * p.I) / 16;
-  const int NB = (ntiles + 15) / 16;
+  const int NBLK = (ntiles + 15) / 16;  // n-blocks of 256 weight rows
   const int n_mb = uniform(p.mtoff[p.E]);
-  const long total = (long)n_mb * NB;
+  const long total = (long)n_mb * NBLK;
   const size_t arow = FMT == 0 ? (size_t)K : (size_t)K / 2;
   const size_t srow = (size_t)K / 32;
   const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
@@ -373,7 +389,7 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
   for (long w = L; w < total; w += G) {
     // item w = (global m-block, n-block), n-block minor: consecutive items
     // (neighbouring CUs of one XCD) share the activation tile through L2
-    const int gmb = (int)(w / NB), nb = (int)(w % NB);
+    const int gmb = (int)(w / NBLK), nb = (int)(w % NBLK);
     const int e = uniform(p.mbexp[gmb]);
     const int mb = gmb - uniform(p.mtoff[e]);
     const int row0 = uniform(p.offsets[e]) + BM * mb;
@@ -402,33 +418,41 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
     const uint8_t *wsrc = p.wp + qbase * quad_bytes + (size_t)lane * 16;
     const uint32_t *wssrc = p.wsp + qbase * quad_dwords + lane;
 
-    // Copies of K step s into stage buffer s % NS.  Past the last step the
-    // same number of copies is issued from one fixed address (every lane
-    // reads the same 16 bytes) into a buffer no step reads any more, so each
-    // loop iteration issues exactly C copies and one wait count fits all.
+    // Copy group p = the weight copies of K step p + D (the weights run D
+    // steps further ahead), then the activation copies of step p.  Copies of
+    // a step past the last are issued from one fixed address (every lane
+    // reads the same 16 bytes) into a ring slot no step reads any more, so
+    // every group has C copies and one wait count fits all.  Copies retire
+    // in issue order, so "at most N outstanding" names exactly what landed;
+    // the weight copies (from HBM) go first so that they have the longest
+    // time to land before a wait covers them.
     const uint8_t *dummy = p.wp + qbase * quad_bytes;
-    // copy i (0 <= i < C) of K step s: activation chunks, the activation
-    // scale dword, the four weight fragments, the four weight scale dwords
-    auto issue_one = [&](int s, int i) __attribute__((always_inline)) {
-      const bool real = s < S;
-      uint8_t *st = lds + (s % NS) * TS::STAGE;
-      if (i < TS::A_COPIES) {
-        copy16_to_lds(real ? asrc[i] + (size_t)ROWB * s : dummy,
-                      st + (wave * TS::A_COPIES + i) * 1024);
-      } else if (i == TS::A_COPIES) {
-        copy4_to_lds(real ? ssrc + 4 * s : dummy, st + TS::OFF_AS + wave * 256);
-      } else if (i < TS::A_COPIES + 5) {
-        const int q = i - TS::A_COPIES - 1;
-        copy16_to_lds(real ? wsrc + (size_t)s * 4096 + q * 1024 : dummy,
-                      st + TS::OFF_B + wave * 4096 + q * 1024);
-      } else {
-        copy4_to_lds(real ? (const void *)(wssrc + (size_t)s * 64) : (const void *)dummy,
-                     st + TS::OFF_BS + wave * 256);
-      }
+    // weight copy i (0 <= i < CB) of K step sb: four fragments, scale dword
+    auto issue_b = [&](int sb, int i) __attribute__((always_inline)) {
+      const bool real = sb < S;
+      uint8_t *sw = lds + TS::B_BASE + (sb % NB) * TS::B_STAGE;
+      if (i < 4)
+        copy16_to_lds(real ? wsrc + (size_t)sb * 4096 + i * 1024 : dummy,
+                      sw + wave * 4096 + i * 1024);
+      else
+        copy4_to_lds(real ? (const void *)(wssrc + (size_t)sb * 64) : (const void *)dummy,
+                     sw + TS::OFF_BS + wave * 256);
     };
-    auto issue = [&](int s) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < TS::C; ++i) issue_one(s, i);
+    // copy i (0 <= i < C) of group p: the four weight fragments, the weight
+    // scale dword, the activation chunks, the activation scale dword
+    auto issue_one = [&](int pg, int i) __attribute__((always_inline)) {
+      if (i < TS::CB) {
+        issue_b(pg + D, i);
+      } else {
+        const int ia = i - TS::CB;
+        const bool real = pg < S;
+        uint8_t *st = lds + (pg % NA) * TS::A_STAGE;
+        if (ia < TS::A_COPIES)
+          copy16_to_lds(real ? asrc[ia] + (size_t)ROWB * pg : dummy,
+                        st + (wave * TS::A_COPIES + ia) * 1024);
+        else
+          copy4_to_lds(real ? ssrc + 4 * pg : dummy, st + TS::OFF_AS + wave * 256);
+      }
     };
 
     v4f acc[MT][4];
@@ -456,23 +480,33 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
       return (int)st[TS::OFF_AS + 4 * TS::sslot(16 * m + r16) + g];
     };
 
+    // prologue: the weight lead (steps 0 .. D-1), then groups 0 .. NA-2
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(s);
-    wait_vm<(NS - 2) * TS::C>();  // step 0 has landed
+    for (int sb = 0; sb < D; ++sb)
+#pragma unroll
+      for (int i = 0; i < TS::CB; ++i) issue_b(sb, i);
+#pragma unroll
+    for (int pg = 0; pg < NA - 1; ++pg)
+#pragma unroll
+      for (int i = 0; i < TS::C; ++i) issue_one(pg, i);
+    // step 0 has landed: what may still be in flight is issued after its
+    // activation copies (groups 1 .. NA-2)
+    wait_vm<(NA - 2) * TS::C>();
     __syncthreads();
 
     for (int s = 0; s < S; ++s) {
-      // the copies of step s + NS - 1 are spread over the MFMA sequence of
+      // the copies of group s + NA - 1 are spread over the MFMA sequence of
       // step s, so the wave never stalls on a full memory queue with the
       // matrix cores idle
       {  // inactive waves (past the last weight tile) compute on valid data and never store
-        const uint8_t *st = lds + (s % NS) * TS::STAGE;
+        const uint8_t *st = lds + (s % NA) * TS::A_STAGE;
+        const uint8_t *sw = lds + TS::B_BASE + (s % NB) * TS::B_STAGE;
         v8i b[4];
-        const int sb = *reinterpret_cast<const int *>(st + TS::OFF_BS + wave * 256 + lane * 4);
+        const int sb = *reinterpret_cast<const int *>(sw + TS::OFF_BS + wave * 256 + lane * 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const u32x4 v = *reinterpret_cast<const u32x4 *>(st + TS::OFF_B + wave * 4096 +
-                                                          q * 1024 + lane * 16);
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(sw + wave * 4096 + q * 1024 +
+                                                          lane * 16);
           b[q][0] = (int)v[0]; b[q][1] = (int)v[1]; b[q][2] = (int)v[2]; b[q][3] = (int)v[3];
           b[q][4] = 0; b[q][5] = 0; b[q][6] = 0; b[q][7] = 0;
         }
@@ -482,7 +516,7 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
 #pragma unroll
-          for (int i = m * TS::C / MT; i < (m + 1) * TS::C / MT; ++i) issue_one(s + NS - 1, i);
+          for (int i = m * TS::C / MT; i < (m + 1) * TS::C / MT; ++i) issue_one(s + NA - 1, i);
           v8i anext = acur;
           int sanext = sacur;
           if (m + 1 < MT) {
@@ -498,7 +532,7 @@ __global__ __launch_bounds__(256, 1) void tiled_kernel(KArgs p) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<(NS - 2) * TS::C>();  // step s+1 has landed
+      wait_vm<(NA - 2) * TS::C>();  // step s+1 has landed
       barrier_keep_copies();
     }
 

@@ -9,6 +9,7 @@
 namespace moe {
 
 constexpr int kSortBlock = 256;  // tokens per sort workgroup
+constexpr int kFrontMaxT = 16;   // largest T routed/sorted/quantised by one fused launch
 constexpr int kMTile = 16;       // rows per MFMA m-tile
 constexpr int kUnit = 32;        // h columns per GEMM1 work unit (one requant block)
 

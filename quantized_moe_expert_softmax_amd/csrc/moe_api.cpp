@@ -219,9 +219,11 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
     ++stage;
   };
   mark();
-  if (T <= kSortBlock) {
-    // decode sizes: route, sort and quantisation in one launch (its time is
-    // recorded as the route stage; the sort and quant stages record ~0)
+  if (T <= kFrontMaxT) {
+    // small decode batches: route, sort and quantisation in one launch (its
+    // time is recorded as the route stage; the sort and quant stages record
+    // ~0).  One workgroup routes every token there, which is slower than
+    // the separate kernels beyond a few tens of tokens.
     FrontArgs f{};
     f.logits = logits; f.x = static_cast<const uint16_t *>(x);
     f.T = T; f.E = L->E; f.top_k = top_k; f.H = L->H; f.act = act; f.bm = g.plan.bm();
