@@ -42,8 +42,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "quantized_moe_expert_softmax_amd", "csrc")
-# sources that decide GEMM1's memory traffic: the kernels, the weight layout
-GEMM_SOURCES = ("gemm.hip", "prepack.hip", "mx_device.h", "internal.h")
+# sources that decide the decode GEMM1's memory traffic: its kernel, the weight layout
+GEMM_SOURCES = ("gemm_common.h", "gemm_stream.hip", "prepack.hip", "mx_device.h", "internal.h")
 
 
 def log(*a):

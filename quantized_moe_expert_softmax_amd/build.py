@@ -38,7 +38,8 @@ CFLAGS = [
 # Per-file extra flags.  The expert GEMMs keep their MFMA accumulators in
 # ordinary VGPRs: with the accumulation-register form the register allocator
 # shuffles accumulators between register files on every K step.
-FILE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+FILE_FLAGS = {"gemm_stream.hip": _VGPR_FORM, "gemm_tiled.hip": _VGPR_FORM}
 
 
 def sources():

@@ -1,0 +1,145 @@
+// gemm_common.h -- shared pieces of the grouped scaled-MFMA expert GEMMs
+// (gemm_stream.hip: decode variant; gemm_tiled.hip: prefill variant).
+//
+// GEMM1 ("add A4W4 and FP8 P2P transport support to MegaMoE", Technical
+// Details: consume FP4/FP8 activations in GEMM1, emit A2 activations and
+// scales; "feat(moe): FlyDSL MegaMoE fused EP-MoE integration": interleaved
+// gate/up pairing for SwiGLU): per expert, the quantised token rows routed to
+// it times the expert's MXFP4 gate and up rows, FP32 accumulate, then
+// h = silu(gate) * up requantised to the activation format in 1x32 blocks.
+//
+// GEMM2 (same page: FP4xFP4 GEMM2, weighted rows, FP32 accumulation of the
+// top-k contributions): per expert, the A2 rows times the MXFP4 down rows,
+// each output row scaled by its routing weight and stored as an FP32 row in
+// sorted order; the combine kernel sums a token's top-k rows.
+//
+// Both use the gfx950 block-scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4
+// (A = activations, E4M3 or E2M1; B = weights, E2M1; one E8M0 scale per lane
+// per 32-wide K block).  Operand layouts (measured on the device):
+//   E2M1 operand: lane l holds row l%16, K [32*(l/16), +32), low nibble first
+//   E4M3 operand: lane l holds row l%16, bytes 0..15 = K [16*(l/16), +16) and
+//                 bytes 16..31 = K [64 + 16*(l/16), +16)
+//   scale:        lane l gives the scale of row l%16, K block l/16
+//   result:       lane l, register r holds row 4*(l/16) + r, column l%16
+//
+// Two variants, chosen per call from the rows per expert.  Stream (decode):
+// a work item is one 16-row m-tile of one expert times one 64-row weight
+// quad; the four or eight waves of a workgroup split the K steps and reduce
+// in LDS.  Tiled (prefill): gemm_tiled.hip.  Both schedule persistently from
+// the sort's m-block table; the padded rows of a partial m-block load the
+// last valid row, compute its values again and store them to that row.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+#include "mx_device.h"
+
+namespace moe {
+
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct KArgs {
+  int T, top_k, E, H, I;
+  const uint8_t *a1c, *a1s;
+  uint8_t *a2c, *a2s;
+  const int32_t *perm, *offsets, *mtoff, *mbexp;
+  const float *wts;  // [N] routing weight of sorted row p
+  const uint8_t *wp;
+  const uint32_t *wsp;
+  float *rows;  // [N][H] weighted GEMM2 rows (sorted order)
+};
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+
+// One scaled MFMA with the weight scale taken from byte q of sb (q is a
+// compile-time constant after unrolling: the byte is the MFMA's op_sel).
+template <int FMT>
+__device__ __forceinline__ v4f mfma_q(int q, v8i a, v8i b, v4f c, int sa, int sb) {
+  switch (q) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, 4, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, 4, 0, sa, 1, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, 4, 0, sa, 2, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, 4, 0, sa, 3, sb);
+  }
+}
+
+// silu(g) = g / (1 + exp(-g)) with the hardware exp2 and reciprocal; for very
+// negative g the exponential overflows to inf and silu goes to (-)0.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// Cross-lane moves within 16-lane rows (DPP, no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+// maximum over the 16 lanes of a row: quad_perm [1,0,3,2], [2,3,0,1], then
+// row_half_mirror and row_mirror
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, dpp<0xB1>(v));
+  v = max(v, dpp<0x4E>(v));
+  v = max(v, dpp<0x141>(v));
+  v = max(v, dpp<0x140>(v));
+  return v;
+}
+
+// GEMM1 epilogue for one accumulator register r: lane c = l%16 of row group
+// l/16 holds gate/up columns 32j + c (lo) and 32j + 16 + c (hi) of one token
+// row; h = silu(gate) * up; the 32 h values of the row form one 1x32 block
+// (amax over the 16 lanes), requantised and stored to the A2 row.  All lanes
+// call and store: the two lanes of an E2M1 byte both write it whole, all 16
+// lanes write the scale byte, and a padded row (computed from the last valid
+// row's data) rewrites that row's values, so no store needs a branch.
+template <class F, int FMT>
+__device__ __forceinline__ void swiglu_requant(float glo, float ghi, float ulo, float uhi,
+                                               uint8_t *__restrict__ a2row,
+                                               uint8_t *__restrict__ a2srow, int j, int c) {
+  const float hlo = silu(glo) * ulo;
+  const float hhi = silu(ghi) * uhi;
+  const uint32_t am = row16_max(max(f32_bits(hlo) & 0x7fffffffu, f32_bits(hhi) & 0x7fffffffu));
+  const int X = block_exponent<F>(am);
+  const uint32_t clo = encode_element<F>(f32_bits(hlo), X);
+  const uint32_t chi = encode_element<F>(f32_bits(hhi), X);
+  const uint32_t plo = dpp<0xB1>(clo);  // code of lane c ^ 1
+  const uint32_t phi = dpp<0xB1>(chi);
+  if (FMT == 0) {
+    a2row[32 * j + c] = (uint8_t)clo;
+    a2row[32 * j + 16 + c] = (uint8_t)chi;
+  } else {
+    const bool odd = c & 1;
+    a2row[16 * j + c / 2] = (uint8_t)(odd ? (plo | (clo << 4)) : (clo | (plo << 4)));
+    a2row[16 * j + 8 + c / 2] = (uint8_t)(odd ? (phi | (chi << 4)) : (chi | (phi << 4)));
+  }
+  a2srow[j] = (uint8_t)(X + 127);
+}
+
+template <int FMT>
+struct ActFmt;
+template <>
+struct ActFmt<0> { using F = E4M3; };
+template <>
+struct ActFmt<4> { using F = E2M1; };
+
+inline KArgs make_args(const GemmArgs &a, bool second) {
+  KArgs k{};
+  k.T = a.T; k.top_k = a.top_k; k.E = a.E; k.H = a.H; k.I = a.I;
+  k.a1c = a.a1c; k.a1s = a.a1s; k.a2c = a.a2c; k.a2s = a.a2s;
+  k.perm = a.perm; k.offsets = a.offsets; k.mtoff = a.mtoff; k.mbexp = a.mbexp; k.wts = a.wts;
+  k.wp = second ? a.w2p : a.w13p;
+  k.wsp = reinterpret_cast<const uint32_t *>(second ? a.w2sp : a.w13sp);
+  k.rows = a.rows;
+  return k;
+}
+
+// Tiled (prefill) variant, in gemm_tiled.hip.
+hipError_t launch_tiled_gemm1(const GemmArgs &a, const KArgs &k, hipStream_t s);
+hipError_t launch_tiled_gemm2(const GemmArgs &a, const KArgs &k, hipStream_t s);
+
+}  // namespace moe

@@ -124,7 +124,8 @@ hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int E, in
 //           waves, each wave owning 64 weight rows (prefill)
 struct GemmPlan {
   bool tiled;
-  int mt;  // 16-row MFMA tiles per work item (1 for stream)
+  int mt;   // 16-row MFMA tiles per work item (1 for stream)
+  int split;  // tiled: 1 = each wave all BM rows x one quad, 2 = BM/2 rows x two quads
   int bm() const { return 16 * mt; }
 };
 GemmPlan choose_plan(int T, int top_k, int E, int act);
