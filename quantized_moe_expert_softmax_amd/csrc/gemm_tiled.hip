@@ -355,13 +355,12 @@ static hipError_t launch_tiled_w(const GemmArgs &a, const KArgs &k, hipStream_t 
   return hipGetLastError();
 }
 
+// Only the one-row-split form is built: the 2 x 2 and eight-wave forms
+// (launch_tiled_w<2, 2> / <2, 1>) measured no faster on the 7168 x 3072 layer.
 template <bool SECOND>
 static hipError_t launch_tiled(const GemmArgs &a, const KArgs &k, hipStream_t s) {
-  switch (a.plan.split) {
-    case 1: return launch_tiled_w<1, 1, SECOND>(a, k, s);
-    case 2: return launch_tiled_w<2, 2, SECOND>(a, k, s);
-    default: return hipErrorInvalidValue;
-  }
+  if (a.plan.split != 1) return hipErrorInvalidValue;
+  return launch_tiled_w<1, 1, SECOND>(a, k, s);
 }
 
 hipError_t launch_tiled_gemm1(const GemmArgs &a, const KArgs &k, hipStream_t s) {
