@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4, help="tokens the oracle FFN runs on")
+    p.add_argument("--plans", default=None, metavar="JSON",
+                   help="install a plan table written by quantized_moe_expert_softmax_amd.tune")
     p.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the "
                         "known-size kernel that scales the HBM byte counters)")
@@ -243,6 +245,9 @@ def main():
     layer = moe.moe_prepare_weights(wl.E, wl.H, wl.I, *w)
     torch.cuda.synchronize()
     log("weights ready in %.1f s" % (time.perf_counter() - t0))
+    if args.plans:
+        with open(args.plans) as fh:
+            moe.moe_set_plans(layer, json.load(fh)["plans"])
 
     r = time_T(moe, torch, layer, wl, T, act, args.steps, args.warmup)
     ms_step = r["dt_eager"] * 1e3 / args.steps

@@ -167,6 +167,41 @@ moe_status moe_sort(const int32_t *ids, int T, int E, int top_k, int32_t *counts
 moe_status moe_quant_act(const void *x, int T, int H, moe_act_dtype act, uint8_t *codes,
                          uint8_t *scales, hipStream_t s);
 
+/* ---- per-layer plan table ---------------------------------------------------
+ * The GEMM variant and tile height of a forward call follow a table keyed by
+ * token count, like the tuned configuration tables the pages keep per token
+ * bucket ("[HIP] gfx950 A8W4 fused_moe configs for DSv4.1 TP-sharded
+ * experts", Changes: tuned entries per token count; "add A4W4 and FP8 P2P
+ * transport support to MegaMoE", Technical Details: BM profiles chosen by
+ * token count).  A layer starts with an empty table; calls no entry matches
+ * use the built-in choice (stream below 1.5 rows per expert, else tiled with
+ * BM from the expected expert load).  Every plan computes the same result
+ * (parity is tested per plan); plans differ only in speed. */
+typedef enum {
+    MOE_PLAN_STREAM = 0, /* 16-row m-tiles, K split over the waves, weights to VGPRs */
+    MOE_PLAN_TILED = 1   /* BM-row m-blocks staged in LDS, 256 weight rows per item */
+} moe_plan_variant;
+
+typedef struct {
+    int32_t act;     /* moe_act_dtype the entry applies to                        */
+    int32_t top_k;   /* top_k the entry applies to                                */
+    int32_t t_max;   /* applies to calls with T <= t_max; the first matching entry
+                        in table order is used                                    */
+    int32_t variant; /* moe_plan_variant                                          */
+    int32_t rows;    /* token rows per work item: 16 for MOE_PLAN_STREAM; for
+                        MOE_PLAN_TILED 32, 64, 96, 128 or 160 (MXFP8) and 64 or
+                        128 (MXFP4)                                               */
+} moe_plan;
+
+/* Replace the layer's table with plans[0 .. n-1] (host array, copied; at most
+ * 256 entries; n == 0 clears it).  Every entry is validated first; on an
+ * invalid one the table is left unchanged and MOE_ERR_INVALID_ARG returned.
+ * Mutates the handle: not concurrent with forward calls on the same layer. */
+moe_status moe_set_plans(moe_layer_t layer, const moe_plan *plans, int n);
+
+/* The plan a forward call (T, top_k, act) on this layer uses (host out). */
+moe_status moe_get_plan(moe_layer_t layer, int T, int top_k, moe_act_dtype act, moe_plan *out);
+
 /* ---- kernel timing for benchmarks (not thread-safe; mutates the handle) -- */
 
 /* Kernels moe_forward launches, in order. */

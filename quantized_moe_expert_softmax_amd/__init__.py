@@ -41,8 +41,20 @@ MOE_K_NUM = len(KERNELS)
 
 EXPORTS = ("moe_prepare_weights", "moe_destroy", "moe_workspace_bytes", "moe_forward",
            "moe_workspace_offsets", "moe_route", "moe_sort_workspace_bytes", "moe_sort",
-           "moe_quant_act", "moe_profile_enable", "moe_profile_read", "moe_status_str",
-           "moe_last_error")
+           "moe_quant_act", "moe_set_plans", "moe_get_plan", "moe_profile_enable",
+           "moe_profile_read", "moe_status_str", "moe_last_error")
+
+MOE_PLAN_STREAM = 0
+MOE_PLAN_TILED = 1
+
+
+class MoePlan(ctypes.Structure):
+    """One plan-table entry (moe_plan in include/moe.h)."""
+    _fields_ = [("act", ctypes.c_int32), ("top_k", ctypes.c_int32), ("t_max", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("rows", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 _lock = threading.Lock()
 _lib = None
@@ -78,6 +90,8 @@ def load_library(path: str = LIB_PATH):
         lib.moe_sort_workspace_bytes.restype = Z
         lib.moe_sort.argtypes = [P, I, I, I, P, P, P, P, Z, P]
         lib.moe_quant_act.argtypes = [P, I, I, I, P, P, P]
+        lib.moe_set_plans.argtypes = [P, P, I]
+        lib.moe_get_plan.argtypes = [P, I, I, I, P]
         lib.moe_profile_enable.argtypes = [P, I, I]
         lib.moe_profile_read.argtypes = [P, P, P]
         lib.moe_status_str.argtypes = [I]
@@ -85,7 +99,8 @@ def load_library(path: str = LIB_PATH):
         lib.moe_last_error.argtypes = []
         lib.moe_last_error.restype = ctypes.c_char_p
         for name in ("moe_prepare_weights", "moe_forward", "moe_workspace_offsets", "moe_route",
-                     "moe_sort", "moe_quant_act", "moe_profile_enable", "moe_profile_read"):
+                     "moe_sort", "moe_quant_act", "moe_set_plans", "moe_get_plan",
+                     "moe_profile_enable", "moe_profile_read"):
             getattr(lib, name).restype = I
         _lib = lib
         return lib
@@ -231,6 +246,24 @@ def moe_quant_act(x, act: int, stream=None):
     scales = torch.empty((T, H // 32), dtype=torch.uint8, device=x.device)
     _check(lib.moe_quant_act(_ptr(x), T, H, act, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
+
+
+def moe_set_plans(layer: MoeLayer, plans):
+    """Install a plan table: a sequence of dicts (or MoePlan) with keys act, top_k,
+    t_max, variant, rows; [] clears it."""
+    arr = (MoePlan * max(len(plans), 1))()
+    for i, pl in enumerate(plans):
+        d = pl.as_dict() if isinstance(pl, MoePlan) else pl
+        arr[i] = MoePlan(int(d["act"]), int(d["top_k"]), int(d["t_max"]), int(d["variant"]),
+                         int(d["rows"]))
+    _check(load_library().moe_set_plans(layer.handle, arr, len(plans)))
+
+
+def moe_get_plan(layer: MoeLayer, T: int, top_k: int, act: int) -> dict:
+    """The plan a forward call (T, top_k, act) uses, as a dict."""
+    out = MoePlan()
+    _check(load_library().moe_get_plan(layer.handle, T, top_k, act, ctypes.byref(out)))
+    return out.as_dict()
 
 
 def moe_profile_enable(layer: MoeLayer, enable: bool = True, max_calls: int = 1024):

@@ -17,6 +17,7 @@ struct moe_layer {
   int device;
   int num_cus;
   uint8_t *w13p, *w13sp, *w2p, *w2sp;
+  std::vector<moe_plan> plans;  // per-layer plan table (moe_set_plans)
   // kernel timing (benchmarks only)
   bool profiling;
   int prof_max, prof_calls;
@@ -166,6 +167,52 @@ moe_status moe_workspace_offsets(moe_layer_t L, int T, int top_k, moe_act_dtype 
   return MOE_OK;
 }
 
+namespace {
+
+GemmPlan plan_for(const moe_layer *L, int T, int top_k, int act) {
+  for (const moe_plan &p : L->plans)
+    if (p.act == act && p.top_k == top_k && T <= p.t_max)
+      return p.variant == MOE_PLAN_STREAM ? GemmPlan{false, 1, 1} : GemmPlan{true, p.rows / 16, 1};
+  return choose_plan(T, top_k, L->E, act);
+}
+
+}  // namespace
+
+moe_status moe_set_plans(moe_layer_t L, const moe_plan *plans, int n) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "null layer handle");
+  if (n < 0 || n > 256) return fail(MOE_ERR_INVALID_ARG, "plan count %d outside [0, 256]", n);
+  if (n > 0 && !plans) return fail(MOE_ERR_INVALID_ARG, "null plan array");
+  for (int i = 0; i < n; ++i) {
+    const moe_plan &p = plans[i];
+    if (p.act != MOE_ACT_MXFP8_E4M3 && p.act != MOE_ACT_MXFP4_E2M1)
+      return fail(MOE_ERR_INVALID_ARG, "plan %d: act %d", i, p.act);
+    if (p.top_k < 1 || p.top_k > 8 || p.top_k > L->E)
+      return fail(MOE_ERR_INVALID_ARG, "plan %d: top_k %d", i, p.top_k);
+    if (p.t_max < 1) return fail(MOE_ERR_INVALID_ARG, "plan %d: t_max %d", i, p.t_max);
+    if (p.variant == MOE_PLAN_STREAM) {
+      if (p.rows != 16) return fail(MOE_ERR_INVALID_ARG, "plan %d: stream rows must be 16", i);
+    } else if (p.variant == MOE_PLAN_TILED) {
+      if (p.rows % 16 != 0 || !tiled_mt_built(p.act, p.rows / 16))
+        return fail(MOE_ERR_INVALID_ARG, "plan %d: no tiled kernel with %d rows for act %d", i,
+                    p.rows, p.act);
+    } else {
+      return fail(MOE_ERR_INVALID_ARG, "plan %d: variant %d", i, p.variant);
+    }
+  }
+  L->plans.assign(plans, plans + n);
+  return MOE_OK;
+}
+
+moe_status moe_get_plan(moe_layer_t L, int T, int top_k, moe_act_dtype act, moe_plan *out) {
+  moe_status st = check_call(L, T, top_k, act);
+  if (st != MOE_OK) return st;
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "null output");
+  const GemmPlan g = plan_for(L, T, top_k, act);
+  *out = moe_plan{(int32_t)act, top_k, T, g.tiled ? MOE_PLAN_TILED : MOE_PLAN_STREAM,
+                  g.tiled ? 16 * g.mt : 16};
+  return MOE_OK;
+}
+
 moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T, int top_k,
                        moe_act_dtype act, void *y, void *ws, size_t ws_bytes, hipStream_t s) {
   moe_status st = check_call(L, T, top_k, act);
@@ -199,7 +246,7 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
 
   GemmArgs g{};
   g.T = T; g.top_k = top_k; g.E = L->E; g.H = L->H; g.I = L->I; g.act = act;
-  g.plan = choose_plan(T, top_k, L->E, act);
+  g.plan = plan_for(L, T, top_k, act);
   {  // each non-empty expert adds at most one partial m-block
     const long N = (long)T * top_k;
     g.max_mtiles = (N + g.plan.bm() - 1) / g.plan.bm() + (N < L->E ? N : L->E);

@@ -117,3 +117,10 @@ def test_product_path_has_no_oracle_dependency():
                 src = open(os.path.join(root, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
                 assert "moe_oracle" not in src and "liboracle" not in src, f
+
+
+def test_plan_calls_validate(lib):
+    entry = (moe.MoePlan * 1)(moe.MoePlan(0, 2, 16, moe.MOE_PLAN_STREAM, 16))
+    assert lib.moe_set_plans(None, entry, 1) == moe.MOE_ERR_INVALID_ARG and "handle" in _err(lib)
+    out = moe.MoePlan()
+    assert lib.moe_get_plan(None, 4, 2, 0, ctypes.byref(out)) == moe.MOE_ERR_INVALID_ARG

@@ -1,0 +1,93 @@
+"""The per-layer plan table: every GEMM plan the library builds gives the
+oracle's result (bit-exact ids / perm / A1 bytes, the output within the
+stated tolerances), the table is looked up in order, invalid entries are
+rejected, and the tuner produces a valid table."""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_moe_expert_softmax_amd as moe
+from quantized_moe_expert_softmax_amd import tune
+from tests.gpu_util import assert_output_close, bf16_dev, dev
+from tests.test_gpu_forward import _check_workspace, _layer, _run, _small
+
+pytestmark = pytest.mark.gpu
+
+# ragged: 300 tokens x 4 slots over 16 experts (~75 rows each): every tile
+# height leaves a partial m-block, and the stream plan many partial m-tiles
+SHAPE = (300, 256, 256, 16, 4)
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_every_plan_matches_oracle(act):
+    T, H, I, E, k = SHAPE
+    w, x, lg = _small(T, H, I, E, k, seed=11)
+    layer = _layer(*w)
+    ref, a2c, a2s = oracle.forward(x, lg, *w, k, act, want_a2=True)
+    for variant, rows in tune.candidates(act):
+        plan = dict(act=act, top_k=k, t_max=T, variant=variant, rows=rows)
+        moe.moe_set_plans(layer, [plan])
+        got = moe.moe_get_plan(layer, T, k, act)
+        assert (got["variant"], got["rows"]) == (variant, rows)
+        y, ws = _run(layer, x, lg, k, act)
+        assert_output_close(y, ref, "plan %s" % plan)
+        mism, smism = _check_workspace(layer, ws, x, lg, k, act, (a2c, a2s))
+        assert mism < 1e-2 and smism < 1e-2, (plan, mism, smism)
+
+
+def test_table_lookup_order_and_fallback():
+    T, H, I, E, k = 64, 256, 128, 8, 2
+    w, _, _ = _small(T, H, I, E, k, seed=12)
+    layer = _layer(*w)
+    builtin_100 = moe.moe_get_plan(layer, 100, k, 0)
+    builtin_4 = moe.moe_get_plan(layer, 4, k, 0)
+    builtin_k1 = moe.moe_get_plan(layer, 100, 1, 1)
+    moe.moe_set_plans(layer, [
+        dict(act=0, top_k=k, t_max=8, variant=moe.MOE_PLAN_TILED, rows=160),
+        dict(act=0, top_k=k, t_max=64, variant=moe.MOE_PLAN_STREAM, rows=16),
+        dict(act=1, top_k=k, t_max=1000, variant=moe.MOE_PLAN_TILED, rows=128),
+    ])
+    assert moe.moe_get_plan(layer, 4, k, 0)["rows"] == 160
+    assert moe.moe_get_plan(layer, 8, k, 0)["rows"] == 160
+    assert moe.moe_get_plan(layer, 9, k, 0)["variant"] == moe.MOE_PLAN_STREAM
+    assert moe.moe_get_plan(layer, 100, k, 0) == builtin_100  # no entry: built-in choice
+    assert moe.moe_get_plan(layer, 100, k, 1)["rows"] == 128
+    assert moe.moe_get_plan(layer, 100, 1, 1) == builtin_k1  # top_k must match too
+    moe.moe_set_plans(layer, [])
+    assert moe.moe_get_plan(layer, 4, k, 0) == builtin_4
+
+
+@pytest.mark.parametrize("bad", [
+    dict(rows=48), dict(rows=160, act=1), dict(variant=2), dict(act=5), dict(top_k=0),
+    dict(top_k=9), dict(t_max=0), dict(variant=moe.MOE_PLAN_STREAM, rows=32),
+])
+def test_invalid_plans_rejected(bad):
+    w, _, _ = _small(16, 256, 128, 8, 2, seed=13)
+    layer = _layer(*w)
+    good = dict(act=0, top_k=2, t_max=16, variant=moe.MOE_PLAN_TILED, rows=64)
+    moe.moe_set_plans(layer, [good])
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_set_plans(layer, [good, dict(good, **bad)])
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    assert moe.moe_get_plan(layer, 16, 2, 0)["rows"] == 64  # table unchanged
+
+
+def test_tuner_installs_a_valid_table():
+    import torch
+    T1, T2, H, I, E, k = 24, 200, 256, 256, 16, 4
+    w, _, _ = _small(T2, H, I, E, k, seed=14)
+    layer = _layer(*w)
+    inputs = {}
+    for T in (T1, T2):
+        _, x, lg = _small(T, H, I, E, k, seed=15 + T)
+        inputs[T] = (bf16_dev(x), [dev(lg)])
+    table, report = tune.tune(layer, inputs, k, 0, steps=2, warmup=1)
+    assert [e["t_max"] for e in table] == [T1, T2]
+    for e in table:
+        assert (e["variant"], e["rows"]) in tune.candidates(0)
+        assert moe.moe_get_plan(layer, e["t_max"], k, 0)["rows"] == e["rows"]
+    # the tuned layer still matches the oracle
+    _, x, lg = _small(T2, H, I, E, k, seed=15 + T2)
+    y, _ = _run(layer, x, lg, k, 0)
+    assert_output_close(y, oracle.forward(x, lg, *w, k, 0), "tuned")
+    torch.cuda.synchronize()
