@@ -166,18 +166,19 @@ constexpr int kTiledSplit = 1;
 
 GemmPlan choose_plan(int T, int top_k, int E, int act) {
   // The average rows per expert decides between weight streaming (fewer than
-  // 1.5 rows; measured on the 7168 x 3072 layer with the plan tuner: the
-  // 32-row tiled plan is 3.6% faster at 2 rows per expert and 10% at 4) and
-  // the pipelined tiled kernel.  The tiled kernel's BM covers the mean
-  // plus 2.5 standard deviations of a binomial expert load, so that under
-  // uniform routing nearly every expert is one m-block and its weights are
-  // read once; an activation tile must fill whole 4 KiB copies (MXFP8: MT
-  // even; MXFP4: MT a multiple of 4), and MT <= 10 keeps the accumulators
-  // in registers.
+  // 2 rows) and the pipelined tiled kernel, whose BM covers the mean plus 1.5
+  // standard deviations of a binomial expert load (under uniform routing
+  // most experts are then one m-block and their weights are read once).  An
+  // activation tile must fill whole 1 KiB copies per wave (MXFP8: MT even;
+  // MXFP4: MT a multiple of 4) and MT <= 10 keeps the accumulators in
+  // registers.  Both thresholds follow the plan tuner's measurements on the
+  // 7168 x 3072 (E = 384, top_k = 6) and 5120 x {640, 1152} (E = 384 x 6 and
+  // 128 x 3) layers: its pick matches this rule wherever the two differ by
+  // more than ~2%.
   const long N = (long)T * top_k;
   const double avg = (double)N / E;
-  if (avg < 1.5) return GemmPlan{false, 1, 1};
-  const double want = avg + 2.5 * sqrt(avg);
+  if (avg < 2.0) return GemmPlan{false, 1, 1};
+  const double want = avg + 1.5 * sqrt(avg);
   if (act == MOE_ACT_MXFP8_E4M3) {
     int mt = (int)ceil(want / 16.0);
     mt = mt + (mt & 1);
