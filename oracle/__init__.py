@@ -60,7 +60,7 @@ def _load():
         lib.oracle_route.argtypes = [P, i32, i32, i32, P, P]
         lib.oracle_sort.argtypes = [P, i32, i32, i32, P, P, P]
         lib.oracle_forward.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, P, P, i32,
-                                       P, P, P, P, P]
+                                       i32, P, P, P, P, P]
         for f in (lib.oracle_mx_quantize, lib.oracle_mx_quantize_bf16, lib.oracle_mx_dequantize,
                   lib.oracle_float_to_bf16, lib.oracle_route, lib.oracle_sort,
                   lib.oracle_forward):
@@ -146,16 +146,24 @@ def sort(ids, E: int):
     return counts, offsets, perm
 
 
+COMBINE_FP32, COMBINE_BF16, COMBINE_FP8 = 0, 1, 2
+
+
 def forward(x_bits, logits, w13, w13s, w2, w2s, top_k: int, fmt: int,
             acc_double: bool = False, want_f32: bool = False, want_a2: bool = False,
-            expert_map=None):
+            expert_map=None, combine: int = COMBINE_FP32):
     """The whole layer for every token of x.
 
     x_bits [T, H] uint16 (bf16), logits [T, E] fp32, w13 [E, 2I, H/2] (gate rows
     first, then up rows), w13s [E, 2I, H/32], w2 [E, H, I/2], w2s [E, H, I/32].
     Returns y [T, H] as bf16 bit patterns (uint16), plus optionally the fp32
     combine and the requantised SwiGLU activations (indexed by assignment).
+    combine: how each weighted GEMM2 row enters the FP32 top-k sum -- as it is
+    (COMBINE_FP32), rounded to bf16 (COMBINE_BF16), or MXFP8-quantised along H
+    and dequantised (COMBINE_FP8); the last two need acc_double False.
     """
+    assert combine in (COMBINE_FP32, COMBINE_BF16, COMBINE_FP8)
+    assert combine == COMBINE_FP32 or not acc_double
     x = _c(x_bits, np.uint16)
     logits = _c(logits, np.float32)
     w13 = _c(w13, np.uint8)
@@ -181,7 +189,7 @@ def forward(x_bits, logits, w13, w13s, w2, w2s, top_k: int, fmt: int,
     a2s = np.zeros((T * top_k, I // 32), np.uint8) if want_a2 else None
     _load().oracle_forward(_ptr(x), _ptr(logits), T, H, I, E, top_k, fmt,
                            _ptr(w13), _ptr(w13s), _ptr(w2), _ptr(w2s), int(bool(acc_double)),
-                           _ptr(y), _ptr(yf), _ptr(a2c), _ptr(a2s), _ptr(emap))
+                           int(combine), _ptr(y), _ptr(yf), _ptr(a2c), _ptr(a2s), _ptr(emap))
     out = [y]
     if want_f32:
         out.append(yf)
@@ -191,7 +199,7 @@ def forward(x_bits, logits, w13, w13s, w2, w2s, top_k: int, fmt: int,
 
 
 def forward_rows(x_bits, logits, rows, weights_for, top_k: int, fmt: int,
-                 acc_double: bool = False):
+                 acc_double: bool = False, combine: int = COMBINE_FP32):
     """The layer on a subset of tokens, fetching only the experts they use.
 
     Every step of the layer is per token, so the output rows of a subset equal
@@ -215,4 +223,4 @@ def forward_rows(x_bits, logits, rows, weights_for, top_k: int, fmt: int,
     w2 = np.stack([p[2] for p in parts])
     w2s = np.stack([p[3] for p in parts])
     return forward(np.asarray(x_bits)[rows], lg, w13, w13s, w2, w2s, top_k, fmt,
-                   acc_double=acc_double, expert_map=emap)
+                   acc_double=acc_double, expert_map=emap, combine=combine)

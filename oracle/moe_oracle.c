@@ -372,6 +372,13 @@ void oracle_sort(const int32_t *ids, int T, int E, int top_k,
  * fmt      activation format: 0 = MXFP8 E4M3 (A8W4), 1 = MXFP4 E2M1 (A4W4)
  * acc_double  0: FP32 evaluation (products and sums in float, ascending
  *             K, no contraction); 1: the same steps in double.
+ * combine  how each weighted GEMM2 row w_j * o_j (FP32, length H) reaches the
+ *             FP32 top-k sum: 0 as it is; 1 rounded to BF16 (nearest even);
+ *             2 quantised to MXFP8 (E4M3 with one E8M0 scale per 1x32 block
+ *             along H, the activation rule) and dequantised.  Modes 1 and 2
+ *             are the compressed combine transports of "add A4W4 and FP8 P2P
+ *             transport support to MegaMoE" (Technical Details: BF16 or
+ *             fp8 1x32 blockwise combine payloads); they need acc_double = 0.
  * y        [T][H] bf16 (round to nearest even of the FP32 combine)
  * y_f32    optional [T][H] fp32 combine before the bf16 rounding
  * a2_codes / a2_scales  optional [T*top_k][I or I/2] / [T*top_k][I/32]
@@ -384,7 +391,7 @@ void oracle_forward(const uint16_t *x, const float *logits, int T, int H, int I,
                     int top_k, int fmt,
                     const uint8_t *w13, const uint8_t *w13s,
                     const uint8_t *w2, const uint8_t *w2s,
-                    int acc_double, uint16_t *y, float *y_f32,
+                    int acc_double, int combine, uint16_t *y, float *y_f32,
                     uint8_t *a2_codes, uint8_t *a2_scales, const int32_t *expert_map)
 {
     long a1_row = (fmt == FMT_E4M3) ? H : H / 2;
@@ -403,6 +410,10 @@ void oracle_forward(const uint16_t *x, const float *logits, int T, int H, int I,
     double *hdq = (double *)malloc(sizeof(double) * (size_t)I);
     float *cf = (float *)malloc(sizeof(float) * (size_t)H);
     double *cd = (double *)malloc(sizeof(double) * (size_t)H);
+    float *trow = (float *)malloc(sizeof(float) * (size_t)H);   /* weighted row */
+    double *tdq = (double *)malloc(sizeof(double) * (size_t)H);
+    uint8_t *tq = (uint8_t *)malloc((size_t)H + 1);
+    uint8_t *ts = (uint8_t *)malloc((size_t)H / 32 + 1);
 
     init_tables();
 
@@ -473,9 +484,24 @@ void oracle_forward(const uint16_t *x, const float *logits, int T, int H, int I,
                         float prod = (float)hdq[i] * (float)wrow[i];
                         acc = acc + prod;
                     }
-                    float contrib = wj * acc;
-                    cf[hh] = cf[hh] + contrib;
+                    trow[hh] = wj * acc;
                 }
+            }
+            if (!acc_double) {
+                /* the row's transport to the combine, then the FP32 slot-order sum */
+                if (combine == 1) {
+                    for (int hh = 0; hh < H; ++hh)
+                        trow[hh] = bf16_to_float(float_to_bf16(trow[hh]));
+                } else if (combine == 2) {
+                    for (int hh = 0; hh < H; ++hh)
+                        tdq[hh] = (double)trow[hh];
+                    mx_quantize_rows_d(tdq, 1, H, FMT_E4M3, tq, ts);
+                    dequant_row(tq, ts, H, FMT_E4M3, tdq);
+                    for (int hh = 0; hh < H; ++hh)
+                        trow[hh] = (float)tdq[hh];
+                }
+                for (int hh = 0; hh < H; ++hh)
+                    cf[hh] = cf[hh] + trow[hh];
             }
         }
         /* step 7: BF16 output */
@@ -488,4 +514,5 @@ void oracle_forward(const uint16_t *x, const float *logits, int T, int H, int I,
     }
     free(ids); free(wts); free(xa); free(xs); free(xdq); free(wrow); free(gu);
     free(hbuf); free(ha); free(hs); free(hdq); free(cf); free(cd);
+    free(trow); free(tdq); free(tq); free(ts);
 }

@@ -238,3 +238,52 @@ def test_fp32_vs_double_bound():
         _, y32 = oracle.forward(x, lg, w13, w13s, w2, w2s, k, fmt, want_f32=True)
         _, y64 = oracle.forward(x, lg, w13, w13s, w2, w2s, k, fmt, want_f32=True, acc_double=True)
         assert np.linalg.norm(y32 - y64) / np.linalg.norm(y64) < 2e-3
+
+
+# ---- compressed combine transports ("add A4W4 and FP8 P2P transport support to
+# MegaMoE", Technical Details: BF16 or fp8 1x32 blockwise combine payloads) ----
+
+@pytest.mark.parametrize("fmt", [E4M3, E2M1])
+def test_combine_transports_reduce_to_rounding_at_top1(fmt):
+    """top_k = 1: the routing weight is exactly 1, the combine sum has one term,
+    so BF16 transport changes nothing after the final BF16 rounding, and FP8
+    transport is exactly the MXFP8 codec (pinned on its own) applied to the
+    FP32-transport result along H."""
+    x, lg, w13, w13s, w2, w2s, _ = _small_case(T=12, seed=21)
+    y32, f32 = oracle.forward(x, lg, w13, w13s, w2, w2s, 1, fmt, want_f32=True)
+    yb, fb = oracle.forward(x, lg, w13, w13s, w2, w2s, 1, fmt, want_f32=True,
+                            combine=oracle.COMBINE_BF16)
+    assert np.array_equal(yb, y32)
+    assert np.array_equal(fb, mxref.bf16_to_f64(oracle.float_to_bf16(f32)).astype(np.float32))
+    y8, f8 = oracle.forward(x, lg, w13, w13s, w2, w2s, 1, fmt, want_f32=True,
+                            combine=oracle.COMBINE_FP8)
+    c, s = oracle.mx_quantize(f32, E4M3)
+    want = oracle.mx_dequantize(c, s, f32.shape[1], E4M3)
+    assert np.array_equal(f8, want)
+    assert np.array_equal(y8, oracle.float_to_bf16(want))
+    assert not np.array_equal(f8, f32)  # the quantisation is really applied
+
+
+def test_combine_transport_error_bounds():
+    """Identical experts: the k weighted rows are w_j * o with sum w_j = 1, so a
+    transport's error is bounded by its per-term rounding bound times |o|:
+    BF16 (nearest even, 8 significant bits: unit roundoff 2^-8) <= 2^-8 |o|
+    per element; MXFP8 (E4M3, one scale per 32 elements) <= 2^-3 times the
+    block's largest |o|: the scaled block maximum lies in [256, 512), where the
+    E4M3 step is 32 and values above 464 saturate to 448 (error < 64 <= amax/8);
+    below the top binade the error is smaller."""
+    x, lg, w13, w13s, w2, w2s, k = _small_case(T=16, k=4, seed=22)
+    same = [np.repeat(a[:1], a.shape[0], axis=0) for a in (w13, w13s, w2, w2s)]
+    _, f32 = oracle.forward(x, lg, *same, k, E4M3, want_f32=True)
+    _, fb = oracle.forward(x, lg, *same, k, E4M3, want_f32=True, combine=oracle.COMBINE_BF16)
+    _, f8 = oracle.forward(x, lg, *same, k, E4M3, want_f32=True, combine=oracle.COMBINE_FP8)
+    o = np.abs(f32.astype(np.float64))
+    slack = 8 * 2.0 ** -24 * o + 1e-30  # FP32 rounding of the k-term sums
+    db = np.abs(fb.astype(np.float64) - f32)
+    assert np.all(db <= 2.0 ** -8 * o * 1.001 + slack)
+    assert db.max() > 0
+    blk = o.reshape(o.shape[0], -1, 32).max(axis=2, keepdims=True)
+    blk = np.broadcast_to(blk, (o.shape[0], o.shape[1] // 32, 32)).reshape(o.shape)
+    d8 = np.abs(f8.astype(np.float64) - f32)
+    assert np.all(d8 <= 2.0 ** -3 * blk * 1.001 + slack)
+    assert d8.max() > db.max()  # coarser than BF16
