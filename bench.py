@@ -2,7 +2,8 @@
 
 A step is one moe_forward call (routing, expert sort, activation quant,
 GEMM1 + SwiGLU + requant, GEMM2 + weighted FP32 combine, BF16 finalize) on
-a batch of T synthetic tokens already resident in HBM.  The default workload
+a batch of T synthetic tokens already resident in HBM (--combine picks the
+transport of the weighted GEMM2 rows: fp32 by default, or bf16 / fp8).  The default workload
 is the DeepSeek-V4-Pro-shaped A8W4 decode layer (H=7168, I=3072, E=384,
 top_k=6, all experts resident) at T=64; the other decode sizes of that
 workload (T=1, 2, 8, 32) are timed too and reported under "sweep".
@@ -61,6 +62,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4, help="tokens the oracle FFN runs on")
+    p.add_argument("--combine", default="fp32", choices=("fp32", "bf16", "fp8"),
+                   help="transport of the weighted GEMM2 rows into the FP32 top-k sum")
     p.add_argument("--plans", default=None, metavar="JSON",
                    help="install a plan table written by quantized_moe_expert_softmax_amd.tune")
     p.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
@@ -133,7 +136,10 @@ def layer_weight_bytes(layer, U):
     return U * (I * H + 2 * I * H // 32 + H * I // 2 + H * I // 32)
 
 
-def time_T(moe, torch, layer, wl, T, act, steps, warmup):
+COMBINES = {"fp32": 0, "bf16": 1, "fp8": 2}
+
+
+def time_T(moe, torch, layer, wl, T, act, steps, warmup, combine=0):
     """Three passes over the same `steps` calls (logits rotating over 8 sets):
     eager launches, HIP-graph replays (one graph captured per logits set),
     both with no events, then an eager pass with per-kernel HIP events."""
@@ -144,15 +150,17 @@ def time_T(moe, torch, layer, wl, T, act, steps, warmup):
     stream = torch.cuda.current_stream()
     Us = []
     for r in range(8):
-        moe.moe_forward(layer, x, lgs[r], wl.top_k, act, y=y, ws=ws)
+        moe.moe_forward(layer, x, lgs[r], wl.top_k, act, y=y, ws=ws, combine=combine)
         torch.cuda.synchronize()
         Us.append(touched_experts(moe, layer, ws, T, wl.top_k, act))
     for i in range(warmup):
-        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream)
+        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream,
+                        combine=combine)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream)
+        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream,
+                        combine=combine)
     torch.cuda.synchronize()
     dt_eager = time.perf_counter() - t0
 
@@ -162,7 +170,8 @@ def time_T(moe, torch, layer, wl, T, act, steps, warmup):
     for r in range(8):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            moe.moe_forward(layer, x, lgs[r], wl.top_k, act, y=y, ws=ws, stream=cap)
+            moe.moe_forward(layer, x, lgs[r], wl.top_k, act, y=y, ws=ws, stream=cap,
+                            combine=combine)
         graphs.append(g)
     torch.cuda.synchronize()
     for i in range(warmup):
@@ -177,7 +186,8 @@ def time_T(moe, torch, layer, wl, T, act, steps, warmup):
 
     moe.moe_profile_enable(layer, True, steps)
     for i in range(steps):
-        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream)
+        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream,
+                        combine=combine)
     torch.cuda.synchronize()
     kern, ncalls = moe.moe_profile_read(layer)
     moe.moe_profile_enable(layer, False)
@@ -249,7 +259,8 @@ def main():
         with open(args.plans) as fh:
             moe.moe_set_plans(layer, json.load(fh)["plans"])
 
-    r = time_T(moe, torch, layer, wl, T, act, args.steps, args.warmup)
+    combine = COMBINES[args.combine]
+    r = time_T(moe, torch, layer, wl, T, act, args.steps, args.warmup, combine)
     ms_step = r["dt_eager"] * 1e3 / args.steps
     value = T * args.steps / r["dt_eager"]
     ncalls = max(r["ncalls"], 1)
@@ -282,7 +293,8 @@ def main():
         for t in wl.Ts:
             if t == T:
                 continue
-            sweep[str(t)] = entry(t, time_T(moe, torch, layer, wl, t, act, args.steps, args.warmup))
+            sweep[str(t)] = entry(t, time_T(moe, torch, layer, wl, t, act, args.steps, args.warmup,
+                                            combine))
             log("T=%d: %s" % (t, sweep[str(t)]))
     sweep[str(T)] = entry(T, r)
 
@@ -307,8 +319,9 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": "%s H=%d I=%d E=%d top_k=%d T=%d %s" % (
-            wl.name, wl.H, wl.I, wl.E, wl.top_k, T, "A8W4" if act == 0 else "A4W4"),
+        "config": {"workload": "%s H=%d I=%d E=%d top_k=%d T=%d %s%s" % (
+            wl.name, wl.H, wl.I, wl.E, wl.top_k, T, "A8W4" if act == 0 else "A4W4",
+            "" if combine == 0 else " combine=" + args.combine),
             "global_batch": T, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "gemm1", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -113,6 +113,26 @@ size_t moe_workspace_bytes(moe_layer_t layer, int T, int top_k, moe_act_dtype ac
 moe_status moe_forward(moe_layer_t layer, const void *x, const float *logits, int T, int top_k,
                        moe_act_dtype act, void *y, void *ws, size_t ws_bytes, hipStream_t s);
 
+/* How the weighted GEMM2 rows travel to the FP32 top-k sum ("add A4W4 and FP8
+ * P2P transport support to MegaMoE", Technical Details: the combine payload
+ * is BF16 or fp8 1x32 blockwise).  FP32 (the default) adds no rounding; BF16
+ * rounds each weighted row element to nearest even; FP8 quantises each row
+ * along H in 1x32 blocks exactly as the activation quantiser does (E4M3,
+ * E8M0 block exponent floor(log2 amax) - 8) and dequantises it in the
+ * combine.  The staging buffer shrinks from 4 to 2 or 33/32 bytes per
+ * element; the sum stays FP32 in slot order and is rounded once to BF16. */
+typedef enum {
+    MOE_COMBINE_FP32 = 0,
+    MOE_COMBINE_BF16 = 1,
+    MOE_COMBINE_FP8 = 2
+} moe_combine;
+
+/* moe_forward with the combine transport in flags (a moe_combine value; other
+ * bits must be zero).  moe_forward(...) == moe_forward_ex(..., 0, ...). */
+moe_status moe_forward_ex(moe_layer_t layer, const void *x, const float *logits, int T, int top_k,
+                          moe_act_dtype act, uint32_t flags, void *y, void *ws, size_t ws_bytes,
+                          hipStream_t s);
+
 /* Regions of the forward workspace, for inspection after a call (all device
  * pointers into ws; layouts as listed). */
 typedef enum {
@@ -127,8 +147,10 @@ typedef enum {
     MOE_WS_A2_CODES,    /* [T*top_k][I] or [..][I/2] SwiGLU codes, row p is
                            the assignment perm[p]                           */
     MOE_WS_A2_SCALES,   /* [T*top_k][I/32] E8M0, same rows                   */
-    MOE_WS_ROWS,        /* [T*top_k][H] fp32 GEMM2 rows times their routing
-                           weight, row p is the assignment perm[p]         */
+    MOE_WS_ROWS,        /* [T*top_k][H] GEMM2 rows times their routing weight,
+                           row p is the assignment perm[p]: fp32 (FP32
+                           transport), bf16 (BF16), or E4M3 codes followed by
+                           [T*top_k][H/32] E8M0 scales (FP8)                */
     MOE_WS_SLOT,        /* [T*top_k] int32: row of assignment a in perm    */
     MOE_WS_NUM
 } moe_ws_region;

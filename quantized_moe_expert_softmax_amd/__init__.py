@@ -40,9 +40,14 @@ KERNELS = ("route", "sort_hist", "sort_scan", "sort_scatter", "quant", "gemm1", 
 MOE_K_NUM = len(KERNELS)
 
 EXPORTS = ("moe_prepare_weights", "moe_destroy", "moe_workspace_bytes", "moe_forward",
+           "moe_forward_ex",
            "moe_workspace_offsets", "moe_route", "moe_sort_workspace_bytes", "moe_sort",
            "moe_quant_act", "moe_set_plans", "moe_get_plan", "moe_profile_enable",
            "moe_profile_read", "moe_status_str", "moe_last_error")
+
+MOE_COMBINE_FP32 = 0  # transport of the weighted GEMM2 rows into the FP32 top-k sum
+MOE_COMBINE_BF16 = 1
+MOE_COMBINE_FP8 = 2
 
 MOE_PLAN_STREAM = 0
 MOE_PLAN_TILED = 1
@@ -84,6 +89,7 @@ def load_library(path: str = LIB_PATH):
         lib.moe_workspace_bytes.argtypes = [P, I, I, I]
         lib.moe_workspace_bytes.restype = Z
         lib.moe_forward.argtypes = [P, P, P, I, I, I, P, P, Z, P]
+        lib.moe_forward_ex.argtypes = [P, P, P, I, I, I, ctypes.c_uint32, P, P, Z, P]
         lib.moe_workspace_offsets.argtypes = [P, I, I, I, P]
         lib.moe_route.argtypes = [P, I, I, I, P, P, P]
         lib.moe_sort_workspace_bytes.argtypes = [I, I, I]
@@ -98,7 +104,8 @@ def load_library(path: str = LIB_PATH):
         lib.moe_status_str.restype = ctypes.c_char_p
         lib.moe_last_error.argtypes = []
         lib.moe_last_error.restype = ctypes.c_char_p
-        for name in ("moe_prepare_weights", "moe_forward", "moe_workspace_offsets", "moe_route",
+        for name in ("moe_prepare_weights", "moe_forward", "moe_forward_ex",
+                     "moe_workspace_offsets", "moe_route",
                      "moe_sort", "moe_quant_act", "moe_set_plans", "moe_get_plan",
                      "moe_profile_enable", "moe_profile_read"):
             getattr(lib, name).restype = I
@@ -182,8 +189,11 @@ def alloc_workspace(layer: MoeLayer, T: int, top_k: int, act: int, device=None):
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 
 
-def moe_forward(layer: MoeLayer, x, logits, top_k: int, act: int, y=None, ws=None, stream=None):
-    """y [T, H] bf16 = MoE(x [T, H] bf16, logits [T, E] fp32); enqueue only."""
+def moe_forward(layer: MoeLayer, x, logits, top_k: int, act: int, y=None, ws=None, stream=None,
+                combine: int = MOE_COMBINE_FP32):
+    """y [T, H] bf16 = MoE(x [T, H] bf16, logits [T, E] fp32); enqueue only.
+    combine: transport of the weighted rows into the FP32 top-k sum
+    (MOE_COMBINE_FP32 -> moe_forward, else moe_forward_ex)."""
     import torch
     lib = load_library()
     T = x.shape[0]
@@ -194,8 +204,12 @@ def moe_forward(layer: MoeLayer, x, logits, top_k: int, act: int, y=None, ws=Non
     _require(y, 2, (T, layer.H), "y")
     if ws is None:
         ws = alloc_workspace(layer, T, top_k, act, x.device)
-    _check(lib.moe_forward(layer.handle, _ptr(x), _ptr(logits), T, top_k, act, _ptr(y), _ptr(ws),
-                           ws.numel(), _stream(stream)))
+    if combine == MOE_COMBINE_FP32:
+        _check(lib.moe_forward(layer.handle, _ptr(x), _ptr(logits), T, top_k, act, _ptr(y),
+                               _ptr(ws), ws.numel(), _stream(stream)))
+    else:
+        _check(lib.moe_forward_ex(layer.handle, _ptr(x), _ptr(logits), T, top_k, act, combine,
+                                  _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
     return y
 
 

@@ -448,11 +448,19 @@ hipError_t launch_front(const FrontArgs &a, hipStream_t s) {
 // Details: accumulate the top-k contributions in FP32): y[t] = bf16 of the
 // FP32 sum, in slot order j = 0..top_k-1, of the weighted GEMM2 rows of the
 // token's assignments (row inv[t*top_k + j]), rounded once to nearest even.
-// One thread per 8 outputs.
+// The rows arrive in the call's transport (FP32, BF16, or MXFP8 codes with
+// one E8M0 scale per 32 columns).  One thread per 8 outputs.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ rows,
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -v : v;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ rows,
                                                       const int32_t *__restrict__ inv, long n8,
-                                                      int H, int top_k,
+                                                      int H, int top_k, long N,
                                                       uint16_t *__restrict__ y) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
@@ -460,11 +468,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   const int h = (int)(i % (H / 8)) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < top_k; ++j) {
-    const float *r = rows + (size_t)inv[t * top_k + j] * H + h;
-    const float4 a = reinterpret_cast<const float4 *>(r)[0];
-    const float4 b = reinterpret_cast<const float4 *>(r)[1];
-    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    const size_t p = (size_t)inv[t * top_k + j];
+    float v[8];
+    if (MODE == MOE_COMBINE_FP32) {
+      const float4 *r = reinterpret_cast<const float4 *>(static_cast<const float *>(rows) +
+                                                         p * H + h);
+      const float4 a = r[0], b = r[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else if (MODE == MOE_COMBINE_BF16) {
+      const uint4 a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(rows) +
+                                                       p * H + h);
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __uint_as_float(w[k] << 16);
+        v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+    } else {
+      const uint8_t *base = static_cast<const uint8_t *>(rows);
+      const uint2 a = *reinterpret_cast<const uint2 *>(base + p * H + h);
+      const int X = (int)base[(size_t)N * H + p * (H / 32) + h / 32] - 127;
+      const uint32_t w[2] = {a.x, a.y};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = ldexpf(e4m3_value((w[k / 4] >> (8 * (k % 4))) & 0xffu), X);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += v[k];
   }
   uint4 o;
   o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
@@ -474,11 +503,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   reinterpret_cast<uint4 *>(y)[i] = o;
 }
 
-hipError_t launch_combine(const float *rows, const int32_t *inv, int T, int H, int top_k,
-                          uint16_t *y, hipStream_t s) {
+hipError_t launch_combine(const void *rows, const int32_t *inv, int T, int H, int top_k,
+                          int combine, uint16_t *y, hipStream_t s) {
   const long n8 = (long)T * H / 8;
   if (n8 == 0) return hipSuccess;
-  combine_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(rows, inv, n8, H, top_k, y);
+  const unsigned grid = (unsigned)((n8 + 255) / 256);
+  const long N = (long)T * top_k;
+  switch (combine) {
+    case MOE_COMBINE_FP32:
+      combine_kernel<MOE_COMBINE_FP32><<<grid, 256, 0, s>>>(rows, inv, n8, H, top_k, N, y);
+      break;
+    case MOE_COMBINE_BF16:
+      combine_kernel<MOE_COMBINE_BF16><<<grid, 256, 0, s>>>(rows, inv, n8, H, top_k, N, y);
+      break;
+    case MOE_COMBINE_FP8:
+      combine_kernel<MOE_COMBINE_FP8><<<grid, 256, 0, s>>>(rows, inv, n8, H, top_k, N, y);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

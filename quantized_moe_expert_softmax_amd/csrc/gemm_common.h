@@ -51,7 +51,8 @@ struct KArgs {
   const float *wts;  // [N] routing weight of sorted row p
   const uint8_t *wp;
   const uint32_t *wsp;
-  float *rows;  // [N][H] weighted GEMM2 rows (sorted order)
+  float *rows;  // [N][H] weighted GEMM2 rows (sorted order; layout by combine)
+  int combine;  // moe_combine transport
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -135,7 +136,40 @@ inline KArgs make_args(const GemmArgs &a, bool second) {
   k.wp = second ? a.w2p : a.w13p;
   k.wsp = reinterpret_cast<const uint32_t *>(second ? a.w2sp : a.w13sp);
   k.rows = a.rows;
+  k.combine = a.combine;
   return k;
+}
+
+// GEMM2 epilogue store of one row piece: lane c = l%16 of a row group holds
+// the weighted outputs t[q] of sorted row prow, columns col0 + c + 16q
+// (q = 0..3; col0 a multiple of 64), written in the row transport's format.
+// All 16 lanes of the row group call (the MXFP8 transport's block amax is a
+// DPP max across them); blocks of 32 columns are (q0, q1) and (q2, q3).
+__device__ __forceinline__ void stage_store(const KArgs &p, size_t prow, int col0, int c,
+                                            const float t[4]) {
+  const size_t H = (size_t)p.H;
+  if (p.combine == MOE_COMBINE_FP32) {
+    float *d = p.rows + prow * H + col0 + c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[16 * q] = t[q];
+  } else if (p.combine == MOE_COMBINE_BF16) {
+    uint16_t *d = reinterpret_cast<uint16_t *>(p.rows) + prow * H + col0 + c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[16 * q] = f32_to_bf16(t[q]);
+  } else {
+    uint8_t *base = reinterpret_cast<uint8_t *>(p.rows);
+    uint8_t *d = base + prow * H + col0 + c;
+    uint8_t *sc = base + (size_t)p.T * p.top_k * H + prow * (H / 32) + col0 / 32;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const uint32_t lo = f32_bits(t[2 * b]), hi = f32_bits(t[2 * b + 1]);
+      const uint32_t am = row16_max(max(lo & 0x7fffffffu, hi & 0x7fffffffu));
+      const int X = block_exponent<E4M3>(am);
+      d[32 * b] = (uint8_t)encode_element<E4M3>(lo, X);
+      d[32 * b + 16] = (uint8_t)encode_element<E4M3>(hi, X);
+      sc[b] = (uint8_t)(X + 127);  // every lane writes the same byte
+    }
+  }
 }
 
 // Tiled (prefill) variant, in gemm_tiled.hip.

@@ -145,15 +145,16 @@ __global__ __launch_bounds__(64 * NW) void gemm2_kernel(KArgs p) {
         // a padded row recomputes the last valid row and stores the same values
         const int m = min(4 * (lane >> 4) + r, nrows - 1);
         const float wt_a = p.wts[row0 + m];
-        float *dst = p.rows + (size_t)(row0 + m) * p.H + 64 * nb + c;
+        float t[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int i = 4 * q + r;
           float o = red[0][i][lane];
 #pragma unroll
           for (int u = 1; u < NW; ++u) o += red[u][i][lane];
-          dst[16 * q] = wt_a * o;
+          t[q] = wt_a * o;
         }
+        stage_store(p, (size_t)(row0 + m), 64 * nb, c, t);
       }
     }
     __syncthreads();

@@ -322,9 +322,10 @@ __global__ __launch_bounds__(64 * RS * 4 / QPW, 1) void tiled_kernel(KArgs p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int mrow = min(16 * (mw0 + m) + 4 * g + r, nrows - 1);
-            float *d = p.rows + (size_t)(row0 + mrow) * p.H + 16 * (size_t)tile0 + r16;
+            float t[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) d[16 * q] = wa[m][r] * acc[m][4 * u + q][r];
+            for (int q = 0; q < 4; ++q) t[q] = wa[m][r] * acc[m][4 * u + q][r];
+            stage_store(p, (size_t)(row0 + mrow), 16 * tile0, r16, t);
           }
         }
       }

@@ -145,11 +145,12 @@ struct GemmArgs {
   const int32_t *perm, *offsets, *mtoff, *mbexp;
   const float *wts;  // [N] routing weight of sorted row p
   const uint8_t *w13p, *w13sp, *w2p, *w2sp;
-  float *rows;  // [N][H] weighted GEMM2 rows
+  float *rows;  // [N][H] weighted GEMM2 rows (layout by combine)
+  int combine;  // moe_combine transport of the rows
 };
 hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s);
-hipError_t launch_combine(const float *rows, const int32_t *inv, int T, int H, int top_k,
-                          uint16_t *y, hipStream_t s);
+hipError_t launch_combine(const void *rows, const int32_t *inv, int T, int H, int top_k,
+                          int combine, uint16_t *y, hipStream_t s);
 
 }  // namespace moe

@@ -215,8 +215,16 @@ moe_status moe_get_plan(moe_layer_t L, int T, int top_k, moe_act_dtype act, moe_
 
 moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T, int top_k,
                        moe_act_dtype act, void *y, void *ws, size_t ws_bytes, hipStream_t s) {
+  return moe_forward_ex(L, x, logits, T, top_k, act, 0u, y, ws, ws_bytes, s);
+}
+
+moe_status moe_forward_ex(moe_layer_t L, const void *x, const float *logits, int T, int top_k,
+                          moe_act_dtype act, uint32_t flags, void *y, void *ws, size_t ws_bytes,
+                          hipStream_t s) {
   moe_status st = check_call(L, T, top_k, act);
   if (st != MOE_OK) return st;
+  if (flags != MOE_COMBINE_FP32 && flags != MOE_COMBINE_BF16 && flags != MOE_COMBINE_FP8)
+    return fail(MOE_ERR_INVALID_ARG, "flags 0x%x: not a moe_combine value", flags);
   if (T == 0) return MOE_OK;
   if (!x || !logits || !y || !ws) return fail(MOE_ERR_INVALID_ARG, "null data pointer");
   if (misaligned(x, 16) || misaligned(y, 16) || misaligned(logits, 4))
@@ -256,6 +264,7 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
   g.perm = perm; g.offsets = offsets; g.mtoff = mtoff; g.mbexp = mbexp; g.wts = wsorted;
   g.w13p = L->w13p; g.w13sp = L->w13sp; g.w2p = L->w2p; g.w2sp = L->w2sp;
   g.rows = rows;
+  g.combine = (int)flags;
 
   const bool prof = L->profiling && L->prof_calls < L->prof_max;
   hipEvent_t *ev = prof ? &L->events[(size_t)L->prof_calls * (MOE_K_NUM + 1)] : nullptr;
@@ -299,7 +308,7 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
   if (e == hipSuccess) e = launch_gemm2(g, s);
   mark();
   if (e == hipSuccess)
-    e = launch_combine(rows, inv, T, L->H, top_k, static_cast<uint16_t *>(y), s);
+    e = launch_combine(rows, inv, T, L->H, top_k, (int)flags, static_cast<uint16_t *>(y), s);
   mark();
   if (e != hipSuccess) return hip_fail(e, "moe_forward launch");
   if (prof) ++L->prof_calls;

@@ -22,12 +22,12 @@ def _layer(w13, w13s, w2, w2s):
     return moe.moe_prepare_weights(E, Hh * 2, I2 // 2, dev(w13), dev(w13s), dev(w2), dev(w2s))
 
 
-def _run(layer, x, lg, k, act):
+def _run(layer, x, lg, k, act, combine=moe.MOE_COMBINE_FP32):
     import torch
     T = x.shape[0]
     ws = moe.alloc_workspace(layer, T, k, act)
     ws.fill_(0xA5)  # poison: any read of an unwritten byte shows up
-    y = moe.moe_forward(layer, bf16_dev(x), dev(lg), k, act, ws=ws)
+    y = moe.moe_forward(layer, bf16_dev(x), dev(lg), k, act, ws=ws, combine=combine)
     torch.cuda.synchronize()
     return bf16_host_bits(y), ws
 
@@ -200,3 +200,32 @@ def test_graph_capture_replays():
         g.replay()
         torch.cuda.synchronize()
         assert_output_close(bf16_host_bits(y), eager, "graph replay")
+
+
+@pytest.mark.parametrize("combine", [moe.MOE_COMBINE_BF16, moe.MOE_COMBINE_FP8])
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("T,H,I,E,k", [CASES[0], CASES[4], CASES[5], CASES[6]])
+def test_forward_combine_transports(T, H, I, E, k, act, combine):
+    """The compressed combine transports against the oracle's same transport;
+    the FP8 one must differ from the FP32 transport (it quantises)."""
+    w, x, lg = _small(T, H, I, E, k, seed=T + H + I + E + k)
+    layer = _layer(*w)
+    y, ws = _run(layer, x, lg, k, act, combine=combine)
+    ref = oracle.forward(x, lg, *w, k, act, combine=combine)
+    rel, row = assert_output_close(y, ref, "T=%d act=%d combine=%d" % (T, act, combine))
+    _check_workspace(layer, ws, x, lg, k, act)
+    if combine == moe.MOE_COMBINE_FP8:
+        y32, _ = _run(layer, x, lg, k, act)
+        assert not np.array_equal(y, y32)
+    print("T=%d act=%d combine=%d rel=%.2e row=%.2e" % (T, act, combine, rel, row))
+
+
+def test_forward_rejects_unknown_flags():
+    import torch
+    w, x, lg = _small(8, 256, 128, 8, 2, seed=16)
+    layer = _layer(*w)
+    ws = moe.alloc_workspace(layer, 8, 2, 0)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_forward(layer, bf16_dev(x), dev(lg), 2, 0, ws=ws, combine=3)
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    torch.cuda.synchronize()

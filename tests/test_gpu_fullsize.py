@@ -48,7 +48,7 @@ def sample_rows(ids, E, n_random=2, seed=0):
     return sorted(set(int(r) for r in rows))
 
 
-def run_case(name, T, act=None, n_random=2):
+def run_case(name, T, act=None, n_random=2, combine=moe.MOE_COMBINE_FP32):
     import torch
     wl = synth.WORKLOADS[name]
     act = wl.act if act is None else act
@@ -56,7 +56,7 @@ def run_case(name, T, act=None, n_random=2):
     x = wl.x(T)
     lg = wl.logits(T)
     ws = moe.alloc_workspace(layer, T, wl.top_k, act)
-    y = moe.moe_forward(layer, bf16_dev(x), dev(lg), wl.top_k, act, ws=ws)
+    y = moe.moe_forward(layer, bf16_dev(x), dev(lg), wl.top_k, act, ws=ws, combine=combine)
     torch.cuda.synchronize()
     yb = bf16_host_bits(y)
     N = T * wl.top_k
@@ -81,9 +81,11 @@ def run_case(name, T, act=None, n_random=2):
         if e not in wcache:
             wcache[e] = tuple(a[e].cpu().numpy() for a in w)
         return wcache[e]
-    ref = oracle.forward_rows(x, lg, rows, wfor, wl.top_k, act)
-    rel, row = assert_output_close(yb[rows], ref, "%s T=%d act=%d rows=%s" % (name, T, act, rows))
-    print("%s T=%d act=%d rows=%d rel=%.2e max_row=%.2e" % (name, T, act, len(rows), rel, row))
+    ref = oracle.forward_rows(x, lg, rows, wfor, wl.top_k, act, combine=combine)
+    rel, row = assert_output_close(yb[rows], ref, "%s T=%d act=%d combine=%d rows=%s"
+                                   % (name, T, act, combine, rows))
+    print("%s T=%d act=%d combine=%d rows=%d rel=%.2e max_row=%.2e"
+          % (name, T, act, combine, len(rows), rel, row))
 
 
 @pytest.mark.parametrize("T", [1, 2, 8, 64])
@@ -108,3 +110,10 @@ def test_v4pro_a4w4(T):
                                     ("v41flash_i1152_e128", 32768), ("v41flash_i1152_e128", 2)])
 def test_v41flash(name, T):
     run_case(name, T, n_random=3)
+
+
+@pytest.mark.parametrize("combine", [moe.MOE_COMBINE_BF16, moe.MOE_COMBINE_FP8])
+@pytest.mark.parametrize("name,T", [("v4pro_decode", 8), ("v4pro_prefill", 8192),
+                                    ("v41flash_i640_e384", 32768)])
+def test_combine_transports(name, T, combine):
+    run_case(name, T, n_random=1, combine=combine)
