@@ -79,7 +79,8 @@ __device__ __forceinline__ float silu(float g) {
 // Cross-lane moves within 16-lane rows (DPP, no LDS traffic).
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+  // all rows and banks enabled: every lane is written, so no old value is kept
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 // maximum over the 16 lanes of a row: quad_perm [1,0,3,2], [2,3,0,1], then
 // row_half_mirror and row_mirror
@@ -91,34 +92,65 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
   return v;
 }
 
-// GEMM1 epilogue for one accumulator register r: lane c = l%16 of row group
-// l/16 holds gate/up columns 32j + c (lo) and 32j + 16 + c (hi) of one token
-// row; h = silu(gate) * up; the 32 h values of the row form one 1x32 block
-// (amax over the 16 lanes), requantised and stored to the A2 row.  All lanes
-// call and store: the two lanes of an E2M1 byte both write it whole, all 16
-// lanes write the scale byte, and a padded row (computed from the last valid
-// row's data) rewrites that row's values, so no store needs a branch.
-template <class F, int FMT>
-__device__ __forceinline__ void swiglu_requant(float glo, float ghi, float ulo, float uhi,
-                                               uint8_t *__restrict__ a2row,
-                                               uint8_t *__restrict__ a2srow, int j, int c) {
-  const float hlo = silu(glo) * ulo;
-  const float hhi = silu(ghi) * uhi;
-  const uint32_t am = row16_max(max(f32_bits(hlo) & 0x7fffffffu, f32_bits(hhi) & 0x7fffffffu));
-  const int X = block_exponent<F>(am);
-  const uint32_t clo = encode_element<F>(f32_bits(hlo), X);
-  const uint32_t chi = encode_element<F>(f32_bits(hhi), X);
-  const uint32_t plo = dpp<0xB1>(clo);  // code of lane c ^ 1
-  const uint32_t phi = dpp<0xB1>(chi);
-  if (FMT == 0) {
-    a2row[32 * j + c] = (uint8_t)clo;
-    a2row[32 * j + 16 + c] = (uint8_t)chi;
-  } else {
-    const bool odd = c & 1;
-    a2row[16 * j + c / 2] = (uint8_t)(odd ? (plo | (clo << 4)) : (clo | (plo << 4)));
-    a2row[16 * j + 8 + c / 2] = (uint8_t)(odd ? (phi | (chi << 4)) : (chi | (phi << 4)));
+// 16-lane row maximum of NR independent values, the NR chains advanced in
+// lock-step so that each DPP read follows other chains' work instead of
+// waiting out its own producer (a DPP operand written by the previous VALU
+// op needs wait states).
+template <int NR>
+__device__ __forceinline__ void row16_max_n(uint32_t (&v)[NR]) {
+#pragma unroll
+  for (int i = 0; i < NR; ++i) v[i] = max(v[i], dpp<0xB1>(v[i]));
+#pragma unroll
+  for (int i = 0; i < NR; ++i) v[i] = max(v[i], dpp<0x4E>(v[i]));
+#pragma unroll
+  for (int i = 0; i < NR; ++i) v[i] = max(v[i], dpp<0x141>(v[i]));
+#pragma unroll
+  for (int i = 0; i < NR; ++i) v[i] = max(v[i], dpp<0x140>(v[i]));
+}
+
+// GEMM1 epilogue for NR accumulator rows at once: for row i, lane c = l%16
+// holds gate/up columns 32j + c (lo) and 32j + 16 + c (hi) of one token row;
+// h = silu(gate) * up; the 32 h values of the row form one 1x32 block (amax
+// over the 16 lanes), requantised and stored to the A2 row.  All lanes call
+// and store: the two lanes of an E2M1 byte both write it whole, all 16 lanes
+// write the scale byte, and a padded row (computed from the last valid row's
+// data) rewrites that row's values, so no store needs a branch.
+template <class F, int FMT, int NR>
+__device__ __forceinline__ void swiglu_requant_n(const float (&glo)[NR], const float (&ghi)[NR],
+                                                 const float (&ulo)[NR], const float (&uhi)[NR],
+                                                 uint8_t *const (&a2row)[NR],
+                                                 uint8_t *const (&a2srow)[NR], int j, int c) {
+  float hlo[NR], hhi[NR];
+  uint32_t am[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    hlo[i] = silu(glo[i]) * ulo[i];
+    hhi[i] = silu(ghi[i]) * uhi[i];
+    am[i] = max(f32_bits(hlo[i]) & 0x7fffffffu, f32_bits(hhi[i]) & 0x7fffffffu);
   }
-  a2srow[j] = (uint8_t)(X + 127);
+  row16_max_n<NR>(am);
+  uint32_t clo[NR], chi[NR];
+  int X[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    X[i] = block_exponent<F>(am[i]);
+    clo[i] = encode_element<F>(f32_bits(hlo[i]), X[i]);
+    chi[i] = encode_element<F>(f32_bits(hhi[i]), X[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    if (FMT == 0) {
+      a2row[i][32 * j + c] = (uint8_t)clo[i];
+      a2row[i][32 * j + 16 + c] = (uint8_t)chi[i];
+    } else {
+      const uint32_t plo = dpp<0xB1>(clo[i]);  // code of lane c ^ 1
+      const uint32_t phi = dpp<0xB1>(chi[i]);
+      const bool odd = c & 1;
+      a2row[i][16 * j + c / 2] = (uint8_t)(odd ? (plo | (clo[i] << 4)) : (clo[i] | (plo << 4)));
+      a2row[i][16 * j + 8 + c / 2] = (uint8_t)(odd ? (phi | (chi[i] << 4)) : (chi[i] | (phi << 4)));
+    }
+    a2srow[i][j] = (uint8_t)(X[i] + 127);
+  }
 }
 
 template <int FMT>
@@ -140,34 +172,52 @@ inline KArgs make_args(const GemmArgs &a, bool second) {
   return k;
 }
 
-// GEMM2 epilogue store of one row piece: lane c = l%16 of a row group holds
-// the weighted outputs t[q] of sorted row prow, columns col0 + c + 16q
-// (q = 0..3; col0 a multiple of 64), written in the row transport's format.
-// All 16 lanes of the row group call (the MXFP8 transport's block amax is a
-// DPP max across them); blocks of 32 columns are (q0, q1) and (q2, q3).
-__device__ __forceinline__ void stage_store(const KArgs &p, size_t prow, int col0, int c,
-                                            const float t[4]) {
+// GEMM2 epilogue store of NR row pieces: for piece i, lane c = l%16 of a row
+// group holds the weighted outputs t[i][q] of sorted row prow[i], columns
+// col0 + c + 16q (q = 0..3; col0 a multiple of 64), written in the row
+// transport's format.  All 16 lanes of the row group call (the MXFP8
+// transport's block amax is a DPP max across them); blocks of 32 columns are
+// (q0, q1) and (q2, q3).
+template <int NR>
+__device__ __forceinline__ void stage_store_n(const KArgs &p, const size_t (&prow)[NR], int col0,
+                                              int c, const float (&t)[NR][4]) {
   const size_t H = (size_t)p.H;
   if (p.combine == MOE_COMBINE_FP32) {
-    float *d = p.rows + prow * H + col0 + c;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d[16 * q] = t[q];
+    for (int i = 0; i < NR; ++i) {
+      float *d = p.rows + prow[i] * H + col0 + c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d[16 * q] = t[i][q];
+    }
   } else if (p.combine == MOE_COMBINE_BF16) {
-    uint16_t *d = reinterpret_cast<uint16_t *>(p.rows) + prow * H + col0 + c;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d[16 * q] = f32_to_bf16(t[q]);
+    for (int i = 0; i < NR; ++i) {
+      uint16_t *d = reinterpret_cast<uint16_t *>(p.rows) + prow[i] * H + col0 + c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d[16 * q] = f32_to_bf16(t[i][q]);
+    }
   } else {
     uint8_t *base = reinterpret_cast<uint8_t *>(p.rows);
-    uint8_t *d = base + prow * H + col0 + c;
-    uint8_t *sc = base + (size_t)p.T * p.top_k * H + prow * (H / 32) + col0 / 32;
+    const size_t scale0 = (size_t)p.T * p.top_k * H + col0 / 32;
+    uint32_t am[2 * NR];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const uint32_t lo = f32_bits(t[2 * b]), hi = f32_bits(t[2 * b + 1]);
-      const uint32_t am = row16_max(max(lo & 0x7fffffffu, hi & 0x7fffffffu));
-      const int X = block_exponent<E4M3>(am);
-      d[32 * b] = (uint8_t)encode_element<E4M3>(lo, X);
-      d[32 * b + 16] = (uint8_t)encode_element<E4M3>(hi, X);
-      sc[b] = (uint8_t)(X + 127);  // every lane writes the same byte
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        am[2 * i + b] = max(f32_bits(t[i][2 * b]) & 0x7fffffffu,
+                            f32_bits(t[i][2 * b + 1]) & 0x7fffffffu);
+    row16_max_n<2 * NR>(am);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      uint8_t *d = base + prow[i] * H + col0 + c;
+      uint8_t *sc = base + scale0 + prow[i] * (H / 32);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int X = block_exponent<E4M3>(am[2 * i + b]);
+        d[32 * b] = (uint8_t)encode_element<E4M3>(f32_bits(t[i][2 * b]), X);
+        d[32 * b + 16] = (uint8_t)encode_element<E4M3>(f32_bits(t[i][2 * b + 1]), X);
+        sc[b] = (uint8_t)(X + 127);  // every lane writes the same byte
+      }
     }
   }
 }

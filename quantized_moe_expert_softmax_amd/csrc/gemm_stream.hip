@@ -95,14 +95,18 @@ __global__ __launch_bounds__(64 * NW) void gemm1_kernel(KArgs p) {
         for (int u = 1; u < NW; ++u) v[i] += red[u][i][lane];
       }
       const int c = lane & 15;
+      // tiles: 0 = gate cols [32j, +16), 1 = gate [32j+16, +16), 2/3 = up
+      float g0[4], g1[4], u0[4], u1[4];
+      uint8_t *ar[4], *sr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // tiles: 0 = gate cols [32j, +16), 1 = gate [32j+16, +16), 2/3 = up
         const int m = 4 * (lane >> 4) + r;
         const size_t prow = (size_t)(row0 + min(m, nrows - 1));
-        swiglu_requant<F, FMT>(v[0 * 4 + r], v[1 * 4 + r], v[2 * 4 + r], v[3 * 4 + r],
-                               p.a2c + prow * a2row, p.a2s + prow * (p.I / 32), j, c);
+        g0[r] = v[0 * 4 + r]; g1[r] = v[1 * 4 + r]; u0[r] = v[2 * 4 + r]; u1[r] = v[3 * 4 + r];
+        ar[r] = p.a2c + prow * a2row;
+        sr[r] = p.a2s + prow * (p.I / 32);
       }
+      swiglu_requant_n<F, FMT, 4>(g0, g1, u0, u1, ar, sr, j, c);
     }
     __syncthreads();
   }
@@ -140,22 +144,24 @@ __global__ __launch_bounds__(64 * NW) void gemm2_kernel(KArgs p) {
     __syncthreads();
     if (wave == 0) {
       const int c = lane & 15;
+      size_t prow[4];
+      float t[4][4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // a padded row recomputes the last valid row and stores the same values
         const int m = min(4 * (lane >> 4) + r, nrows - 1);
         const float wt_a = p.wts[row0 + m];
-        float t[4];
+        prow[r] = (size_t)(row0 + m);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int i = 4 * q + r;
           float o = red[0][i][lane];
 #pragma unroll
           for (int u = 1; u < NW; ++u) o += red[u][i][lane];
-          t[q] = wt_a * o;
+          t[r][q] = wt_a * o;
         }
-        stage_store(p, (size_t)(row0 + m), 64 * nb, c, t);
       }
+      stage_store_n<4>(p, prow, 64 * nb, c, t);
     }
     __syncthreads();
   }

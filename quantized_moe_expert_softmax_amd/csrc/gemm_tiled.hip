@@ -299,14 +299,18 @@ __global__ __launch_bounds__(64 * RS * 4 / QPW, 1) void tiled_kernel(KArgs p) {
         const int j = tile0 / 4;  // unit: h columns [32j, 32j + 32)
 #pragma unroll
         for (int m = 0; m < MTW; ++m) {
+          float g0[4], g1[4], u0[4], u1[4];
+          uint8_t *ar[4], *sr[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int mrow = 16 * (mw0 + m) + 4 * g + r;
             const size_t prow = (size_t)(row0 + min(mrow, nrows - 1));
-            swiglu_requant<F, FMT>(acc[m][4 * u][r], acc[m][4 * u + 1][r], acc[m][4 * u + 2][r],
-                                   acc[m][4 * u + 3][r], p.a2c + prow * a2row,
-                                   p.a2s + prow * (p.I / 32), j, r16);
+            g0[r] = acc[m][4 * u][r]; g1[r] = acc[m][4 * u + 1][r];
+            u0[r] = acc[m][4 * u + 2][r]; u1[r] = acc[m][4 * u + 3][r];
+            ar[r] = p.a2c + prow * a2row;
+            sr[r] = p.a2s + prow * (p.I / 32);
           }
+          swiglu_requant_n<F, FMT, 4>(g0, g1, u0, u1, ar, sr, j, r16);
         }
       } else {
         // a padded row (loaded from the last valid row) stores the same
@@ -319,14 +323,15 @@ __global__ __launch_bounds__(64 * RS * 4 / QPW, 1) void tiled_kernel(KArgs p) {
             wa[m][r] = p.wts[row0 + min(16 * (mw0 + m) + 4 * g + r, nrows - 1)];
 #pragma unroll
         for (int m = 0; m < MTW; ++m) {
+          size_t prow[4];
+          float t[4][4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int mrow = min(16 * (mw0 + m) + 4 * g + r, nrows - 1);
-            float t[4];
+            prow[r] = (size_t)(row0 + min(16 * (mw0 + m) + 4 * g + r, nrows - 1));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) t[q] = wa[m][r] * acc[m][4 * u + q][r];
-            stage_store(p, (size_t)(row0 + mrow), 16 * tile0, r16, t);
+            for (int q = 0; q < 4; ++q) t[r][q] = wa[m][r] * acc[m][4 * u + q][r];
           }
+          stage_store_n<4>(p, prow, 16 * tile0, r16, t);
         }
       }
     }
