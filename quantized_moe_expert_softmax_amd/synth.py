@@ -121,6 +121,31 @@ def router_logits(T: int, E: int, seed: int, skewed: bool = False) -> np.ndarray
     return lg
 
 
+def expert_ids(T: int, E: int, k: int, seed: int, hot: float = 0.0) -> np.ndarray:
+    """Expert ids [T, k] int32: k distinct experts per token drawn uniformly
+    from [0, E) (k <= E); with probability hot a token's first id becomes
+    expert 0 (an overloaded expert), its ids staying distinct."""
+    rng = np.random.default_rng([0x1D, T, E, k, seed])
+    ids = np.zeros((T, k), np.int64)
+    taken = np.zeros((T, 0), np.int64)
+    for j in range(k):
+        # a uniform pick among the E - j experts not yet taken: draw a rank and
+        # step it past every taken id at or below it, in ascending order
+        v = rng.integers(0, E - j, T)
+        for c in range(j):
+            v += v >= taken[:, c]
+        ids[:, j] = v
+        taken = np.sort(np.concatenate([taken, v[:, None]], axis=1), axis=1)
+    if hot > 0:
+        m = rng.random(T) < hot
+        first = ids[:, 0].copy()
+        for j in range(1, k):
+            clash = m & (ids[:, j] == 0)
+            ids[clash, j] = first[clash]
+        ids[m, 0] = 0
+    return ids.astype(np.int32)
+
+
 # Activation formats (the library's act dtype values).
 MXFP8 = 0  # A8W4
 MXFP4 = 1  # A4W4

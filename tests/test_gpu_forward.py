@@ -84,6 +84,10 @@ CASES = [
     (1, 1024, 1152, 64, 6),
     # more than one 256-token sort block: the separate route/sort/quant kernels
     (300, 256, 256, 16, 4),
+    # the largest expert count and top_k: fused front kernel (T <= 16) and not
+    (1, 256, 128, 1024, 8),
+    (16, 256, 128, 1024, 8),
+    (17, 256, 128, 1024, 8),
 ]
 
 

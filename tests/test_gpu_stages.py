@@ -57,6 +57,23 @@ def test_sort(moe, T, E, k):
     assert np.array_equal(host(perm), rp)
 
 
+# The largest sizes the interface takes (T = 2^20 tokens, E = 1024 experts,
+# top_k = 8): a uniform spread, one expert holding about a third of the 8M
+# assignments, every token on every expert, one expert only.
+SORT_LIMIT_CASES = [(1 << 20, 1024, 8, 0.0), (1 << 20, 1024, 8, 0.3), (1 << 20, 8, 8, 0.0),
+                    (1 << 16, 1, 1, 0.0)]
+
+
+@pytest.mark.parametrize("T,E,k,hot", SORT_LIMIT_CASES)
+def test_sort_limits(moe, T, E, k, hot):
+    rid = synth.expert_ids(T, E, k, seed=E + k, hot=hot)
+    counts, offsets, perm = moe.moe_sort(dev(rid), E)
+    rc, ro, rp = oracle.sort(rid, E)
+    assert np.array_equal(host(counts), rc)
+    assert np.array_equal(host(offsets), ro)
+    assert np.array_equal(host(perm), rp)
+
+
 def _special_bf16_rows(H):
     bits = np.arange(65536, dtype=np.uint32)
     f = (bits << 16).view(np.float32)
