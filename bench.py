@@ -62,6 +62,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=4, help="tokens the oracle FFN runs on")
+    p.add_argument("--prequant", action="store_true",
+                   help="feed MX-quantised activations (moe_forward_prequant)")
     p.add_argument("--combine", default="fp32", choices=("fp32", "bf16", "fp8"),
                    help="transport of the weighted GEMM2 rows into the FP32 top-k sum")
     p.add_argument("--plans", default=None, metavar="JSON",
@@ -139,28 +141,38 @@ def layer_weight_bytes(layer, U):
 COMBINES = {"fp32": 0, "bf16": 1, "fp8": 2}
 
 
-def time_T(moe, torch, layer, wl, T, act, steps, warmup, combine=0):
+def time_T(moe, torch, layer, wl, T, act, steps, warmup, combine=0, prequant=False):
     """Three passes over the same `steps` calls (logits rotating over 8 sets):
     eager launches, HIP-graph replays (one graph captured per logits set),
-    both with no events, then an eager pass with per-kernel HIP events."""
+    both with no events, then an eager pass with per-kernel HIP events.
+    prequant: the calls take x already MX-quantised (moe_forward_prequant; the
+    codes are made once, outside the timed region)."""
     x = torch.from_numpy(wl.x(T).view("int16")).cuda().view(torch.bfloat16)
     lgs = [torch.from_numpy(wl.logits(T, r)).cuda() for r in range(8)]
     ws = moe.alloc_workspace(layer, T, wl.top_k, act)
     y = torch.empty((T, wl.H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
+    if prequant:
+        xc, xs = moe.moe_quant_act(x, act)
+
+    def call(lg, s=None):
+        if prequant:
+            moe.moe_forward_prequant(layer, xc, xs, lg, wl.top_k, act, y=y, ws=ws, stream=s,
+                                     combine=combine)
+        else:
+            moe.moe_forward(layer, x, lg, wl.top_k, act, y=y, ws=ws, stream=s, combine=combine)
+
     Us = []
     for r in range(8):
-        moe.moe_forward(layer, x, lgs[r], wl.top_k, act, y=y, ws=ws, combine=combine)
+        call(lgs[r])
         torch.cuda.synchronize()
         Us.append(touched_experts(moe, layer, ws, T, wl.top_k, act))
     for i in range(warmup):
-        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream,
-                        combine=combine)
+        call(lgs[i % 8], stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream,
-                        combine=combine)
+        call(lgs[i % 8], stream)
     torch.cuda.synchronize()
     dt_eager = time.perf_counter() - t0
 
@@ -170,8 +182,7 @@ def time_T(moe, torch, layer, wl, T, act, steps, warmup, combine=0):
     for r in range(8):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            moe.moe_forward(layer, x, lgs[r], wl.top_k, act, y=y, ws=ws, stream=cap,
-                            combine=combine)
+            call(lgs[r], cap)
         graphs.append(g)
     torch.cuda.synchronize()
     for i in range(warmup):
@@ -186,8 +197,7 @@ def time_T(moe, torch, layer, wl, T, act, steps, warmup, combine=0):
 
     moe.moe_profile_enable(layer, True, steps)
     for i in range(steps):
-        moe.moe_forward(layer, x, lgs[i % 8], wl.top_k, act, y=y, ws=ws, stream=stream,
-                        combine=combine)
+        call(lgs[i % 8], stream)
     torch.cuda.synchronize()
     kern, ncalls = moe.moe_profile_read(layer)
     moe.moe_profile_enable(layer, False)
@@ -260,7 +270,7 @@ def main():
             moe.moe_set_plans(layer, json.load(fh)["plans"])
 
     combine = COMBINES[args.combine]
-    r = time_T(moe, torch, layer, wl, T, act, args.steps, args.warmup, combine)
+    r = time_T(moe, torch, layer, wl, T, act, args.steps, args.warmup, combine, args.prequant)
     ms_step = r["dt_eager"] * 1e3 / args.steps
     value = T * args.steps / r["dt_eager"]
     ncalls = max(r["ncalls"], 1)
@@ -294,7 +304,7 @@ def main():
             if t == T:
                 continue
             sweep[str(t)] = entry(t, time_T(moe, torch, layer, wl, t, act, args.steps, args.warmup,
-                                            combine))
+                                            combine, args.prequant))
             log("T=%d: %s" % (t, sweep[str(t)]))
     sweep[str(T)] = entry(T, r)
 
@@ -321,7 +331,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "%s H=%d I=%d E=%d top_k=%d T=%d %s%s" % (
             wl.name, wl.H, wl.I, wl.E, wl.top_k, T, "A8W4" if act == 0 else "A4W4",
-            "" if combine == 0 else " combine=" + args.combine),
+            ("" if combine == 0 else " combine=" + args.combine) +
+            (" prequant" if args.prequant else "")),
             "global_batch": T, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "gemm1", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

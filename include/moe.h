@@ -133,6 +133,22 @@ moe_status moe_forward_ex(moe_layer_t layer, const void *x, const float *logits,
                           moe_act_dtype act, uint32_t flags, void *y, void *ws, size_t ws_bytes,
                           hipStream_t s);
 
+/* The layer fed with activations that are already MX-quantised (the pages
+ * benchmark this "prequant" end to end beside the BF16 entry: "add A4W4 and
+ * FP8 P2P transport support to MegaMoE", Test Plan).  Steps 1, 2 and 4-7 run
+ * as in moe_forward_ex; step 3 is skipped and GEMM1 reads
+ *   x_codes  [T][H] E4M3 bytes (act MXFP8) or [T][H/2] packed E2M1 (MXFP4,
+ *            element 2c in the low nibble of byte c), 16-byte aligned
+ *   x_scales [T][H/32] E8M0 bytes, 4-byte aligned
+ * in the layout moe_quant_act writes, so moe_quant_act followed by this call
+ * gives exactly moe_forward_ex's output.  The buffers are read, never
+ * written; the workspace is the one moe_forward takes (its activation-code
+ * region is left unused).  Errors as for moe_forward_ex. */
+moe_status moe_forward_prequant(moe_layer_t layer, const uint8_t *x_codes, const uint8_t *x_scales,
+                                const float *logits, int T, int top_k, moe_act_dtype act,
+                                uint32_t flags, void *y, void *ws, size_t ws_bytes,
+                                hipStream_t s);
+
 /* Regions of the forward workspace, for inspection after a call (all device
  * pointers into ws; layouts as listed). */
 typedef enum {
@@ -201,7 +217,16 @@ moe_status moe_quant_act(const void *x, int T, int H, moe_act_dtype act, uint8_t
  * (parity is tested per plan); plans differ only in speed. */
 typedef enum {
     MOE_PLAN_STREAM = 0, /* 16-row m-tiles, K split over the waves, weights to VGPRs */
-    MOE_PLAN_TILED = 1   /* BM-row m-blocks staged in LDS, 256 weight rows per item */
+    MOE_PLAN_TILED = 1,  /* BM-row m-blocks staged in LDS, 256 weight rows per item */
+    MOE_PLAN_FUSED = 2   /* the stream items of both GEMMs in one persistent launch
+                            (the pages' MegaMoE runs Stage1 and Stage2 as one
+                            launch: "add A4W4 and FP8 P2P transport support to
+                            MegaMoE"); a GEMM2 item waits on a device-side count
+                            for its 16 rows' SwiGLU activations.  The launch
+                            sizes its grid to the workgroups the device holds at
+                            once; work on other streams that keeps CUs busy for
+                            seconds can make its bounded waits give up (wrong
+                            output).  Opt-in: never the built-in choice */
 } moe_plan_variant;
 
 typedef struct {
@@ -210,7 +235,8 @@ typedef struct {
     int32_t t_max;   /* applies to calls with T <= t_max; the first matching entry
                         in table order is used                                    */
     int32_t variant; /* moe_plan_variant                                          */
-    int32_t rows;    /* token rows per work item: 16 for MOE_PLAN_STREAM; for
+    int32_t rows;    /* token rows per work item: 16 for MOE_PLAN_STREAM and
+                        MOE_PLAN_FUSED; for
                         MOE_PLAN_TILED 32, 64, 96, 128 or 160 (MXFP8) and 64 or
                         128 (MXFP4)                                               */
 } moe_plan;

@@ -40,7 +40,7 @@ KERNELS = ("route", "sort_hist", "sort_scan", "sort_scatter", "quant", "gemm1", 
 MOE_K_NUM = len(KERNELS)
 
 EXPORTS = ("moe_prepare_weights", "moe_destroy", "moe_workspace_bytes", "moe_forward",
-           "moe_forward_ex",
+           "moe_forward_ex", "moe_forward_prequant",
            "moe_workspace_offsets", "moe_route", "moe_sort_workspace_bytes", "moe_sort",
            "moe_quant_act", "moe_set_plans", "moe_get_plan", "moe_profile_enable",
            "moe_profile_read", "moe_status_str", "moe_last_error")
@@ -51,6 +51,7 @@ MOE_COMBINE_FP8 = 2
 
 MOE_PLAN_STREAM = 0
 MOE_PLAN_TILED = 1
+MOE_PLAN_FUSED = 2
 
 
 class MoePlan(ctypes.Structure):
@@ -90,6 +91,7 @@ def load_library(path: str = LIB_PATH):
         lib.moe_workspace_bytes.restype = Z
         lib.moe_forward.argtypes = [P, P, P, I, I, I, P, P, Z, P]
         lib.moe_forward_ex.argtypes = [P, P, P, I, I, I, ctypes.c_uint32, P, P, Z, P]
+        lib.moe_forward_prequant.argtypes = [P, P, P, P, I, I, I, ctypes.c_uint32, P, P, Z, P]
         lib.moe_workspace_offsets.argtypes = [P, I, I, I, P]
         lib.moe_route.argtypes = [P, I, I, I, P, P, P]
         lib.moe_sort_workspace_bytes.argtypes = [I, I, I]
@@ -105,7 +107,7 @@ def load_library(path: str = LIB_PATH):
         lib.moe_last_error.argtypes = []
         lib.moe_last_error.restype = ctypes.c_char_p
         for name in ("moe_prepare_weights", "moe_forward", "moe_forward_ex",
-                     "moe_workspace_offsets", "moe_route",
+                     "moe_forward_prequant", "moe_workspace_offsets", "moe_route",
                      "moe_sort", "moe_quant_act", "moe_set_plans", "moe_get_plan",
                      "moe_profile_enable", "moe_profile_read"):
             getattr(lib, name).restype = I
@@ -210,6 +212,28 @@ def moe_forward(layer: MoeLayer, x, logits, top_k: int, act: int, y=None, ws=Non
     else:
         _check(lib.moe_forward_ex(layer.handle, _ptr(x), _ptr(logits), T, top_k, act, combine,
                                   _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_forward_prequant(layer: MoeLayer, codes, scales, logits, top_k: int, act: int, y=None,
+                         ws=None, stream=None, combine: int = MOE_COMBINE_FP32):
+    """y [T, H] bf16 = MoE of MX-quantised activations: codes [T, H] (MXFP8) or
+    [T, H/2] (MXFP4) uint8 and scales [T, H/32] uint8, as moe_quant_act writes
+    them; logits [T, E] fp32.  Enqueue only."""
+    import torch
+    lib = load_library()
+    T = codes.shape[0]
+    _require(codes, 1, (T, layer.H if act == MOE_ACT_MXFP8_E4M3 else layer.H // 2), "codes")
+    _require(scales, 1, (T, layer.H // 32), "scales")
+    _require(logits, 4, (T, layer.E), "logits")
+    if y is None:
+        y = torch.empty((T, layer.H), dtype=torch.bfloat16, device=codes.device)
+    _require(y, 2, (T, layer.H), "y")
+    if ws is None:
+        ws = alloc_workspace(layer, T, top_k, act, codes.device)
+    _check(lib.moe_forward_prequant(layer.handle, _ptr(codes), _ptr(scales), _ptr(logits), T,
+                                    top_k, act, combine, _ptr(y), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
     return y
 
 

@@ -127,10 +127,10 @@ hipError_t launch_route(const float *logits, int T, int E, int top_k, int32_t *i
 // support to MegaMoE", Technical Details: dispatch of the quantised payloads;
 // on one device the experts all live here, so dispatch is a permutation).
 //   hist:    per 256-token block, the number of assignments of each expert
-//   scan:    per expert, exclusive prefix over blocks -> block bases; counts,
-//            offsets (exclusive prefix over experts), the prefix of bm-row
-//            m-blocks per expert and the expert of every m-block, which the
-//            GEMMs schedule from
+//   scan:    per expert, exclusive prefix over blocks (relative to the
+//            expert's first row); counts, offsets (exclusive prefix over
+//            experts), the prefix of bm-row m-blocks per expert and the
+//            expert of every m-block, which the GEMMs schedule from
 //   scatter: within a block, the rank of a token among the tokens routed to
 //            the same expert comes from 64-bit per-wave masks (LDS atomic
 //            OR is order-free; popcount of the lanes below gives the rank),
@@ -158,13 +158,29 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ h
                                                          int32_t *__restrict__ counts,
                                                          int32_t *__restrict__ offsets,
                                                          int32_t *__restrict__ mtoff,
-                                                         int32_t *__restrict__ mbexp, int bm) {
+                                                         int32_t *__restrict__ mbexp, int bm,
+                                                         int32_t *__restrict__ sync, int nsync) {
   __shared__ int32_t sc[1024];
   __shared__ int32_t sm[1024];
   const int e = threadIdx.x;
+  for (int i = e; i < nsync; i += 1024) sync[i] = 0;
   int run = 0;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) {
+    // the blocks' counts are loaded 16 at a time so that the loads overlap
+    // (one dependent L2 round trip per block would dominate at large T)
+    constexpr int U = 16;
+    int b = 0;
+    for (; b + U <= nb; b += U) {
+      int v[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) v[i] = hist[(long)(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        hist[(long)(b + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    for (; b < nb; ++b) {
       const int v = hist[(long)b * E + e];
       hist[(long)b * E + e] = run;
       run += v;
@@ -192,7 +208,6 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ h
       offsets[E] = sc[e];
       mtoff[E] = sm[e];
     }
-    for (int b = 0; b < nb; ++b) hist[(long)b * E + e] += base;
     const int mb0 = sm[e] - m;
     for (int i = 0; i < m; ++i) mbexp[mb0 + i] = e;
   }
@@ -201,6 +216,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ h
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__restrict__ ids, int T,
                                                            int E, int top_k,
                                                            const int32_t *__restrict__ base,
+                                                           const int32_t *__restrict__ offsets,
                                                            int32_t *__restrict__ perm,
                                                            int32_t *__restrict__ inv,
                                                            const float *__restrict__ w,
@@ -224,7 +240,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
       if (e >= (uint32_t)E) continue;
       int r = __popcll(masks[wave * E + e] & (bit - 1ull));
       for (int w = 0; w < wave; ++w) r += __popcll(masks[w * E + e]);
-      const int32_t pos = base[(long)blockIdx.x * E + e] + r;
+      const int32_t pos = offsets[e] + base[(long)blockIdx.x * E + e] + r;
       perm[pos] = (int32_t)(t * top_k + j);
       inv[t * top_k + j] = pos;
       if (wsorted) wsorted[pos] = w[t * top_k + j];
@@ -239,17 +255,19 @@ hipError_t launch_sort_hist(const int32_t *ids, int T, int E, int top_k, int32_t
 }
 
 hipError_t launch_sort_scan(int32_t *hist, int nb, int E, int32_t *counts, int32_t *offsets,
-                            int32_t *mtoff, int32_t *mbexp, int bm, hipStream_t s) {
-  sort_scan_kernel<<<1, 1024, 0, s>>>(hist, nb, E, counts, offsets, mtoff, mbexp, bm);
+                            int32_t *mtoff, int32_t *mbexp, int bm, int32_t *sync, int nsync,
+                            hipStream_t s) {
+  sort_scan_kernel<<<1, 1024, 0, s>>>(hist, nb, E, counts, offsets, mtoff, mbexp, bm, sync,
+                                      nsync);
   return hipGetLastError();
 }
 
 hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, const int32_t *hist,
-                               int32_t *perm, int32_t *inv, const float *w, float *wsorted,
-                               hipStream_t s) {
+                               const int32_t *offsets, int32_t *perm, int32_t *inv,
+                               const float *w, float *wsorted, hipStream_t s) {
   const int nb = ceil_div(T, kSortBlock);
-  sort_scatter_kernel<<<nb, 256, (size_t)E * 4 * 8, s>>>(ids, T, E, top_k, hist, perm, inv, w,
-                                                         wsorted);
+  sort_scatter_kernel<<<nb, 256, (size_t)E * 4 * 8, s>>>(ids, T, E, top_k, hist, offsets, perm,
+                                                         inv, w, wsorted);
   return hipGetLastError();
 }
 
@@ -360,6 +378,7 @@ __global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
   __shared__ unsigned long long masks[4][1024];
   const int wave = tid >> 6, lane = tid & 63;
   const int T = p.T, E = p.E, k = p.top_k, N = T * k;
+  for (int i = tid; i < p.nsync; i += 1024) p.sync[i] = 0;
   for (int e = tid; e < E; e += 1024) {
     cnt[e] = 0;
     masks[0][e] = 0ull; masks[1][e] = 0ull; masks[2][e] = 0ull; masks[3][e] = 0ull;
@@ -427,7 +446,8 @@ __global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
 hipError_t launch_front(const FrontArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (a.T > kSortBlock || a.E > 1024 || a.top_k > 8) return hipErrorInvalidValue;
-  const long nq = ((long)a.T * (a.H / 32) + 1023) / 1024;
+  // no quantisation workgroups when the caller passes MX codes (x null)
+  const long nq = a.x ? ((long)a.T * (a.H / 32) + 1023) / 1024 : 0;
   const dim3 grid((unsigned)(1 + nq)), block(1024);
 #define FRONT_CASE(NV_)                                \
   case NV_:                                            \

@@ -53,6 +53,11 @@ struct KArgs {
   const uint32_t *wsp;
   float *rows;  // [N][H] weighted GEMM2 rows (sorted order; layout by combine)
   int combine;  // moe_combine transport
+  // fused launch only: the down weights beside the gate/up ones in wp/wsp,
+  // and the zeroed sync region (kSyncHead)
+  const uint8_t *w2p;
+  const uint32_t *w2sp;
+  int32_t *sync;
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -110,12 +115,23 @@ __device__ __forceinline__ void row16_max_n(uint32_t (&v)[NR]) {
 
 // GEMM1 epilogue for NR accumulator rows at once: for row i, lane c = l%16
 // holds gate/up columns 32j + c (lo) and 32j + 16 + c (hi) of one token row;
+// A byte store; COH: a device-coherent one (an agent-scope relaxed atomic
+// store, which writes through to the level all XCDs share), for data another
+// workgroup of the same launch reads.
+template <bool COH>
+__device__ __forceinline__ void store_u8(uint8_t *p, uint32_t v) {
+  if (COH)
+    __hip_atomic_store(p, (uint8_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = (uint8_t)v;
+}
+
 // h = silu(gate) * up; the 32 h values of the row form one 1x32 block (amax
 // over the 16 lanes), requantised and stored to the A2 row.  All lanes call
 // and store: the two lanes of an E2M1 byte both write it whole, all 16 lanes
 // write the scale byte, and a padded row (computed from the last valid row's
 // data) rewrites that row's values, so no store needs a branch.
-template <class F, int FMT, int NR>
+template <class F, int FMT, int NR, bool COH = false>
 __device__ __forceinline__ void swiglu_requant_n(const float (&glo)[NR], const float (&ghi)[NR],
                                                  const float (&ulo)[NR], const float (&uhi)[NR],
                                                  uint8_t *const (&a2row)[NR],
@@ -140,16 +156,17 @@ __device__ __forceinline__ void swiglu_requant_n(const float (&glo)[NR], const f
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     if (FMT == 0) {
-      a2row[i][32 * j + c] = (uint8_t)clo[i];
-      a2row[i][32 * j + 16 + c] = (uint8_t)chi[i];
+      store_u8<COH>(a2row[i] + 32 * j + c, clo[i]);
+      store_u8<COH>(a2row[i] + 32 * j + 16 + c, chi[i]);
     } else {
       const uint32_t plo = dpp<0xB1>(clo[i]);  // code of lane c ^ 1
       const uint32_t phi = dpp<0xB1>(chi[i]);
       const bool odd = c & 1;
-      a2row[i][16 * j + c / 2] = (uint8_t)(odd ? (plo | (clo[i] << 4)) : (clo[i] | (plo << 4)));
-      a2row[i][16 * j + 8 + c / 2] = (uint8_t)(odd ? (phi | (chi[i] << 4)) : (chi[i] | (phi << 4)));
+      store_u8<COH>(a2row[i] + 16 * j + c / 2, odd ? (plo | (clo[i] << 4)) : (clo[i] | (plo << 4)));
+      store_u8<COH>(a2row[i] + 16 * j + 8 + c / 2,
+                    odd ? (phi | (chi[i] << 4)) : (chi[i] | (phi << 4)));
     }
-    a2srow[i][j] = (uint8_t)(X[i] + 127);
+    store_u8<COH>(a2srow[i] + j, (uint32_t)(X[i] + 127));
   }
 }
 
@@ -169,6 +186,9 @@ inline KArgs make_args(const GemmArgs &a, bool second) {
   k.wsp = reinterpret_cast<const uint32_t *>(second ? a.w2sp : a.w13sp);
   k.rows = a.rows;
   k.combine = a.combine;
+  k.w2p = a.w2p;
+  k.w2sp = reinterpret_cast<const uint32_t *>(a.w2sp);
+  k.sync = a.sync;
   return k;
 }
 

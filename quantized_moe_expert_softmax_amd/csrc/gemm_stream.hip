@@ -167,6 +167,178 @@ __global__ __launch_bounds__(64 * NW) void gemm2_kernel(KArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused stream launch (MegaMoE's single launch of Stage1 and Stage2, "add
+// A4W4 and FP8 P2P transport support to MegaMoE"): the GEMM1 items (gate/up
+// unit, m-tile) and then the GEMM2 items (64 output columns, m-tile) of one
+// call form one list, which a persistent grid walks: workgroup b takes items
+// b, b + G, b + 2G, ...  A GEMM1 item publishes its SwiGLU rows with device-
+// coherent stores (they write through to the memory side all XCDs share),
+// waits for their completion, then increments its m-tile's count; a GEMM2
+// item waits until the count of its m-tile reaches I/32, then reads the
+// activations with device-coherent loads (which miss any stale copy in the
+// CU's and the XCD's caches), so no cache-wide writeback or invalidate is
+// needed.  A workgroup takes all its GEMM1 items before any GEMM2 item, and G
+// never exceeds the workgroups the device holds at once, so on an otherwise
+// idle device every GEMM1 item a wait depends on is held by a running
+// workgroup that never waits itself.  The wait is bounded all the same (a
+// guard against a bug, or against other work holding CUs for seconds): past
+// the limit it sets the flag word and goes on.
+// ---------------------------------------------------------------------------
+constexpr int kWaitLimit = 1 << 22;
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 (raw byte addressing)
+constexpr int kCoherent = 16;             // buffer load cache policy: sc1
+
+template <int FMT, int NW>
+__global__ __launch_bounds__(64 * NW) void fused_kernel(KArgs p) {
+  using F = typename ActFmt<FMT>::F;
+  __shared__ float red[NW][16][64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
+  const int NU = p.I / 32, NB2 = p.H / 64;
+  const int n_mt = uniform(p.mtoff[p.E]);
+  const long n1 = (long)n_mt * NU, total = n1 + (long)n_mt * NB2;
+  const int S1 = p.H / 128, S2 = p.I / 128;
+  const size_t a1row = FMT == 0 ? (size_t)p.H : (size_t)p.H / 2;
+  const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
+  const size_t nq1 = (size_t)(2 * p.I) / 64, nq2 = (size_t)p.H / 64;
+  int *const flag = p.sync, *const done = p.sync + kSyncHead;
+
+  for (long w = blockIdx.x; w < total; w += gridDim.x) {
+    if (w < n1) {
+      // GEMM1 item, m-tile minor as in the stream kernel
+      const int j = (int)(w / n_mt), mt = (int)(w % n_mt);
+      const int s0 = wave * S1 / NW, s1 = (wave + 1) * S1 / NW;
+      const int e = uniform(p.mbexp[mt]);
+      const int row0 = uniform(p.offsets[e]) + kMTile * (mt - uniform(p.mtoff[e]));
+      const int nrows = min(kMTile, uniform(p.offsets[e + 1]) - row0);
+      const int tok = p.perm[row0 + min(lane & 15, nrows - 1)] / p.top_k;
+      const uint8_t *wt = p.wp + ((size_t)e * nq1 + j) * (size_t)S1 * 4096;
+      const uint32_t *wsq = p.wsp + ((size_t)e * nq1 + j) * (size_t)S1 * 64;
+      v4f acc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
+      mma_4tiles<FMT>(acc, p.a1c + (size_t)tok * a1row, p.a1s + (size_t)tok * (p.H / 32), wt, wsq,
+                      s0, s1, lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][4 * q + r][lane] = acc[q][r];
+      __syncthreads();
+      if (wave == 0) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          v[i] = red[0][i][lane];
+#pragma unroll
+          for (int u = 1; u < NW; ++u) v[i] += red[u][i][lane];
+        }
+        float g0[4], g1[4], u0[4], u1[4];
+        uint8_t *ar[4], *sr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const size_t prow = (size_t)(row0 + min(4 * g + r, nrows - 1));
+          g0[r] = v[r]; g1[r] = v[4 + r]; u0[r] = v[8 + r]; u1[r] = v[12 + r];
+          ar[r] = p.a2c + prow * a2row;
+          sr[r] = p.a2s + prow * (p.I / 32);
+        }
+        swiglu_requant_n<F, FMT, 4, true>(g0, g1, u0, u1, ar, sr, j, lane & 15);
+        // publish: the coherent stores above have completed before the count
+        __builtin_amdgcn_s_waitcnt(0);
+        if (lane == 0)
+          __hip_atomic_fetch_add(done + mt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      // GEMM2 item, m-tile minor
+      const long w2 = w - n1;
+      const int nb = (int)(w2 / n_mt), mt = (int)(w2 % n_mt);
+      const int s0 = wave * S2 / NW, s1 = (wave + 1) * S2 / NW;
+      const int e = uniform(p.mbexp[mt]);
+      const int row0 = uniform(p.offsets[e]) + kMTile * (mt - uniform(p.mtoff[e]));
+      const int nrows = min(kMTile, uniform(p.offsets[e + 1]) - row0);
+      const uint8_t *wt = p.w2p + ((size_t)e * nq2 + nb) * (size_t)S2 * 4096;
+      const uint32_t *wsq = p.w2sp + ((size_t)e * nq2 + nb) * (size_t)S2 * 64;
+      if (tid == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(done + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < NU) {
+          if (++spins > kWaitLimit) {
+            atomicOr(flag, 1);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+        }
+      }
+      __syncthreads();
+      // the m-tile's activation rows through device-coherent buffer loads
+      // (cache policy sc1), from a workgroup-uniform resource at its first row
+      const int r = min(lane & 15, nrows - 1);
+      const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+          p.a2c + (size_t)row0 * a2row, (short)0, (int)(kMTile * a2row), kBufferFlags);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          p.a2s + (size_t)row0 * (p.I / 32), (short)0, kMTile * (p.I / 32), kBufferFlags);
+      const int aoff = r * (int)a2row + 16 * g, soff = r * (p.I / 32) + g;
+      v4f acc[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
+      // four K steps per unrolled group, as in mma_4tiles
+      for (int s4 = s0; s4 < s1; s4 += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int st = s4 + u;
+          if (st < s1) {
+            v8i a;
+            const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(
+                ra, aoff + (FMT == 0 ? 128 : 64) * st, 0, kCoherent);
+            a[0] = (int)lo[0]; a[1] = (int)lo[1]; a[2] = (int)lo[2]; a[3] = (int)lo[3];
+            if (FMT == 0) {
+              const u32x4 hi =
+                  __builtin_amdgcn_raw_buffer_load_b128(ra, aoff + 128 * st + 64, 0, kCoherent);
+              a[4] = (int)hi[0]; a[5] = (int)hi[1]; a[6] = (int)hi[2]; a[7] = (int)hi[3];
+            } else {
+              a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
+            }
+            const int sa = (int)__builtin_amdgcn_raw_buffer_load_b8(rs, soff + 4 * st, 0, kCoherent);
+            const int sb = (int)wsq[(size_t)st * 64 + lane];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const u32x4 bq = *reinterpret_cast<const u32x4 *>(wt + (size_t)st * 4096 +
+                                                               q * 1024 + lane * 16);
+              v8i b;
+              b[0] = (int)bq[0]; b[1] = (int)bq[1]; b[2] = (int)bq[2]; b[3] = (int)bq[3];
+              b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
+              acc[q] = mfma_q<FMT>(q, a, b, acc[q], sa, sb);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) red[wave][4 * q + rr][lane] = acc[q][rr];
+      __syncthreads();
+      if (wave == 0) {
+        size_t prow[4];
+        float t[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int m = min(4 * g + rr, nrows - 1);
+          const float wt_a = p.wts[row0 + m];
+          prow[rr] = (size_t)(row0 + m);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = 4 * q + rr;
+            float o = red[0][i][lane];
+#pragma unroll
+            for (int u = 1; u < NW; ++u) o += red[u][i][lane];
+            t[rr][q] = wt_a * o;
+          }
+        }
+        stage_store_n<4>(p, prow, 64 * nb, lane & 15, t);
+      }
+    }
+    __syncthreads();  // red is free again
+  }
+}
+
 // how the four waves of a tiled workgroup split a BM x 256 item: 1 = all rows
 // x one quad each, 2 = half the rows x two quads each
 constexpr int kTiledSplit = 1;
@@ -208,7 +380,33 @@ static unsigned persistent_grid(long items_upper, int num_cus) {
   return (unsigned)(items_upper < cap ? items_upper : cap);
 }
 
+// GEMM2 weight steps a wave of a fused workgroup loads before its wait
+// The grid never exceeds the workgroups the device holds at once (the
+// waits rely on it: see fused_kernel).
+template <int FMT, int NW>
+static hipError_t launch_fused_w(const GemmArgs &a, const KArgs &k, hipStream_t s) {
+  static int per_cu = 0;  // resident workgroups per CU, a property of the kernel
+  if (per_cu == 0) {
+    int n = 0;
+    const hipError_t e =
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fused_kernel<FMT, NW>, 64 * NW, 0);
+    if (e != hipSuccess) return e;
+    per_cu = n > 0 ? n : 1;
+  }
+  const long items = a.max_mtiles * (a.I / 32 + a.H / 64);
+  const long cap = (long)per_cu * a.num_cus;
+  fused_kernel<FMT, NW><<<(unsigned)(items < cap ? items : cap), 64 * NW, 0, s>>>(k);
+  return hipGetLastError();
+}
+
+static hipError_t launch_fused(const GemmArgs &a, hipStream_t s) {
+  const KArgs k = make_args(a, false);
+  return a.act == MOE_ACT_MXFP8_E4M3 ? launch_fused_w<0, 4>(a, k, s)
+                                     : launch_fused_w<4, 4>(a, k, s);
+}
+
 hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s) {
+  if (a.plan.fused) return launch_fused(a, s);
   const KArgs k = make_args(a, false);
   if (a.plan.tiled) return launch_tiled_gemm1(a, k, s);
   const long items = a.max_mtiles * (a.I / 32);
@@ -225,6 +423,7 @@ hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s) {
+  if (a.plan.fused) return hipSuccess;  // launch_gemm1 ran both GEMMs
   const KArgs k = make_args(a, true);
   if (a.plan.tiled) return launch_tiled_gemm2(a, k, s);
   const long items = a.max_mtiles * (a.H / 64);

@@ -46,11 +46,16 @@ __device__ __forceinline__ void barrier_keep_copies() {
   __builtin_amdgcn_s_barrier();
 }
 // LDS of the tiled kernel: a ring of NA activation stages (the BM rows of
-// one K step and their scale dwords) and a ring of NB weight stages (the
+// one K step and their scale dwords) and a ring of NB = 4 weight stages (the
 // four weight quads' 1 KiB fragments and scale dwords).  Weights stream from
 // HBM and are fetched NB - 1 steps ahead, activations come from L2 and are
-// fetched NA - 1 = 2 steps ahead.  (Weight rings deeper than 4 fit in
-// 160 KiB but measured slower on the 7168 x 3072 layer.)
+// fetched NA - 1 steps ahead.  The waits count copy groups in order, so NA
+// also sets how many groups stay in flight across a step boundary (NA - 2):
+// GEMM1 takes NA = 4 (weights and activations of a step in one group, two
+// groups in flight), GEMM2 NA = 3 (weights one step ahead of activations,
+// one group in flight); on the 7168 x 3072 and 5120 x 640 layers these
+// measured 1-4% faster than the other choice for each GEMM.  (Weight rings
+// deeper than 4 fit in 160 KiB but measured slower.)
 //
 // Waves tile the item's BM x 256 outputs as RS row splits x (4 / QPW) quad
 // groups: a wave owns MT / RS m-tiles and QPW weight quads.  RS = 1, QPW = 1
@@ -61,7 +66,7 @@ __device__ __forceinline__ void barrier_keep_copies() {
 // do not divide evenly a wave repeats a copy another wave makes (same bytes
 // to the same LDS address), so every wave issues the same number and one
 // wait count fits all.
-template <int FMT, int MT, int RS, int QPW>
+template <int FMT, int MT, int RS, int QPW, int NA_>
 struct TileShape {
   static constexpr int NWV = RS * 4 / QPW;           // waves per workgroup
   static constexpr int MTW = MT / RS;                // m-tiles per wave
@@ -80,7 +85,7 @@ struct TileShape {
   static constexpr int A_STAGE = OFF_AS + NWV * 256;
   static constexpr int OFF_BS = 4 * 4096;            // after [4 quads][4 tiles] fragments
   static constexpr int B_STAGE = OFF_BS + 4 * 256;   // + [4 quads][64 lanes] scale dwords
-  static constexpr int NA = 3;
+  static constexpr int NA = NA_;
   static constexpr int NB_FIT = (160 * 1024 - NA * A_STAGE) / B_STAGE;
   static constexpr int NB = NB_FIT < 4 ? NB_FIT : 4;
   static constexpr int D = NB - NA;                  // weight lead over activations, in steps
@@ -89,7 +94,7 @@ struct TileShape {
   static_assert(MT % RS == 0 && 4 % QPW == 0 && 16 % NWV == 0, "even split");
   static_assert(A_BYTES % 1024 == 0, "activation tile must fill whole copies");
   static_assert(RPW <= 64, "scale rows per wave");
-  static_assert(D >= 1, "weights must lead activations");
+  static_assert(D >= 0, "weights never trail activations");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert((NA - 1) * CA + (NB - 1) * CB < 64, "vmcnt range");
   // LDS slot of row r's scale dword
@@ -99,7 +104,7 @@ struct TileShape {
 template <int FMT, int MT, int RS, int QPW, bool SECOND>
 __global__ __launch_bounds__(64 * RS * 4 / QPW, 1) void tiled_kernel(KArgs p) {
   using F = typename ActFmt<FMT>::F;
-  using TS = TileShape<FMT, MT, RS, QPW>;
+  using TS = TileShape<FMT, MT, RS, QPW, SECOND ? 3 : 4>;
   constexpr int NA = TS::NA, NB = TS::NB, D = TS::D, MTW = TS::MTW;
   constexpr int BM = TS::BM, ROWB = TS::ROWB, CH = TS::CH;
   __shared__ __attribute__((aligned(16))) uint8_t lds[TS::LDS];
@@ -344,7 +349,7 @@ static hipError_t launch_tiled_w(const GemmArgs &a, const KArgs &k, hipStream_t 
 #define TILED(F_, MT_)                                                                 \
   case MT_:                                                                            \
     tiled_kernel<F_, MT_, RS, QPW, SECOND>                                             \
-        <<<grid, 64 * TileShape<F_, MT_, RS, QPW>::NWV, 0, s>>>(k);                    \
+        <<<grid, 64 * TileShape<F_, MT_, RS, QPW, 3>::NWV, 0, s>>>(k);                 \
     break;
   if (a.act == MOE_ACT_MXFP8_E4M3) {
     switch (a.plan.mt) {

@@ -11,6 +11,9 @@ namespace moe {
 constexpr int kSortBlock = 256;  // tokens per sort workgroup
 constexpr int kFrontMaxT = 16;   // largest T routed/sorted/quantised by one fused launch
 constexpr int kMTile = 16;       // rows per MFMA m-tile
+// Head of the fused launch's sync region: [0] set when a wait gave up (a
+// guard; never expected), then one GEMM1 completion count per m-tile.
+constexpr int kSyncHead = 1;
 constexpr int kUnit = 32;        // h columns per GEMM1 work unit (one requant block)
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -36,10 +39,11 @@ inline PackDims pack_dims(int R, int K) { return PackDims{R, K, K / 128}; }
 
 struct WsLayout {
   size_t off[MOE_WS_NUM];
-  size_t hist;    // [nb][E] int32 per-sort-block histograms, then bases
+  size_t hist;    // [nb][E] int32 per-sort-block histograms, then bases within the expert
   size_t mtoff;   // [E+1] int32 prefix sum of m-blocks per expert
   size_t mbexp;   // [N/16 + E] int32 expert of each m-block
   size_t wsorted; // [N] fp32 routing weight of sorted row p (assignment perm[p])
+  size_t sync;    // [kSyncHead + N/16 + E + 1] int32 of the fused launch (zeroed before it)
   size_t total;
   int nb;
 };
@@ -60,6 +64,7 @@ inline WsLayout ws_layout(int T, int top_k, int E, int H, int I, int act) {
   L.mbexp = take((N / kMTile + E + 1) * 4);
   L.hist = take((size_t)L.nb * E * 4);
   L.wsorted = take(N * 4);
+  L.sync = take((kSyncHead + N / kMTile + E + 1) * 4);
   L.off[MOE_WS_PERM] = take(N * 4);
   L.off[MOE_WS_A1_CODES] = take((size_t)T * a1row);
   L.off[MOE_WS_A1_SCALES] = take((size_t)T * (H / 32));
@@ -95,15 +100,18 @@ hipError_t launch_route(const float *logits, int T, int E, int top_k, int32_t *i
 hipError_t launch_sort_hist(const int32_t *ids, int T, int E, int top_k, int32_t *hist, int nb,
                             hipStream_t s);
 hipError_t launch_sort_scan(int32_t *hist, int nb, int E, int32_t *counts, int32_t *offsets,
-                            int32_t *mtoff, int32_t *mbexp, int bm, hipStream_t s);
+                            int32_t *mtoff, int32_t *mbexp, int bm, int32_t *sync, int nsync,
+                            hipStream_t s);
 hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, const int32_t *hist,
-                               int32_t *perm, int32_t *inv, const float *w, float *wsorted,
-                               hipStream_t s);
+                               const int32_t *offsets, int32_t *perm, int32_t *inv,
+                               const float *w, float *wsorted, hipStream_t s);
 // Fused route + sort + quant for T <= kSortBlock (same outputs as the
 // separate kernels; hist is not used).
 struct FrontArgs {
+  int32_t *sync;  // [nsync] zeroed (the fused GEMM launch's counters), or nsync 0
+  int nsync;
   const float *logits;
-  const uint16_t *x;
+  const uint16_t *x;  // null: no quantisation (the caller's codes feed GEMM1)
   int T, E, top_k, H, act, bm;
   int32_t *ids;
   float *wts;
@@ -126,6 +134,7 @@ struct GemmPlan {
   bool tiled;
   int mt;   // 16-row MFMA tiles per work item (1 for stream)
   int split;  // tiled: 1 = each wave all BM rows x one quad, 2 = BM/2 rows x two quads
+  bool fused = false;  // stream only: GEMM1 and GEMM2 items in one persistent launch
   int bm() const { return 16 * mt; }
 };
 GemmPlan choose_plan(int T, int top_k, int E, int act);
@@ -147,6 +156,7 @@ struct GemmArgs {
   const uint8_t *w13p, *w13sp, *w2p, *w2sp;
   float *rows;  // [N][H] weighted GEMM2 rows (layout by combine)
   int combine;  // moe_combine transport of the rows
+  int32_t *sync;  // fused launch: work counter, wait flag, per-m-tile counts (zeroed)
 };
 hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s);

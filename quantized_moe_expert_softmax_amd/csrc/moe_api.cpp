@@ -172,7 +172,8 @@ namespace {
 GemmPlan plan_for(const moe_layer *L, int T, int top_k, int act) {
   for (const moe_plan &p : L->plans)
     if (p.act == act && p.top_k == top_k && T <= p.t_max)
-      return p.variant == MOE_PLAN_STREAM ? GemmPlan{false, 1, 1} : GemmPlan{true, p.rows / 16, 1};
+      return p.variant == MOE_PLAN_TILED ? GemmPlan{true, p.rows / 16, 1}
+                                         : GemmPlan{false, 1, 1, p.variant == MOE_PLAN_FUSED};
   return choose_plan(T, top_k, L->E, act);
 }
 
@@ -189,8 +190,9 @@ moe_status moe_set_plans(moe_layer_t L, const moe_plan *plans, int n) {
     if (p.top_k < 1 || p.top_k > 8 || p.top_k > L->E)
       return fail(MOE_ERR_INVALID_ARG, "plan %d: top_k %d", i, p.top_k);
     if (p.t_max < 1) return fail(MOE_ERR_INVALID_ARG, "plan %d: t_max %d", i, p.t_max);
-    if (p.variant == MOE_PLAN_STREAM) {
-      if (p.rows != 16) return fail(MOE_ERR_INVALID_ARG, "plan %d: stream rows must be 16", i);
+    if (p.variant == MOE_PLAN_STREAM || p.variant == MOE_PLAN_FUSED) {
+      if (p.rows != 16)
+        return fail(MOE_ERR_INVALID_ARG, "plan %d: stream and fused rows must be 16", i);
     } else if (p.variant == MOE_PLAN_TILED) {
       if (p.rows % 16 != 0 || !tiled_mt_built(p.act, p.rows / 16))
         return fail(MOE_ERR_INVALID_ARG, "plan %d: no tiled kernel with %d rows for act %d", i,
@@ -208,7 +210,8 @@ moe_status moe_get_plan(moe_layer_t L, int T, int top_k, moe_act_dtype act, moe_
   if (st != MOE_OK) return st;
   if (!out) return fail(MOE_ERR_INVALID_ARG, "null output");
   const GemmPlan g = plan_for(L, T, top_k, act);
-  *out = moe_plan{(int32_t)act, top_k, T, g.tiled ? MOE_PLAN_TILED : MOE_PLAN_STREAM,
+  *out = moe_plan{(int32_t)act, top_k, T,
+                  g.tiled ? MOE_PLAN_TILED : (g.fused ? MOE_PLAN_FUSED : MOE_PLAN_STREAM),
                   g.tiled ? 16 * g.mt : 16};
   return MOE_OK;
 }
@@ -218,19 +221,26 @@ moe_status moe_forward(moe_layer_t L, const void *x, const float *logits, int T,
   return moe_forward_ex(L, x, logits, T, top_k, act, 0u, y, ws, ws_bytes, s);
 }
 
-moe_status moe_forward_ex(moe_layer_t L, const void *x, const float *logits, int T, int top_k,
-                          moe_act_dtype act, uint32_t flags, void *y, void *ws, size_t ws_bytes,
-                          hipStream_t s) {
+// The whole layer, from bf16 rows x (quantised here) or, when prequant, from
+// the caller's MX codes xq and scales xqs.
+static moe_status forward_impl(moe_layer_t L, bool prequant, const void *x, const uint8_t *xq,
+                               const uint8_t *xqs, const float *logits, int T, int top_k,
+                               moe_act_dtype act, uint32_t flags, void *y, void *ws,
+                               size_t ws_bytes, hipStream_t s) {
   moe_status st = check_call(L, T, top_k, act);
   if (st != MOE_OK) return st;
   if (flags != MOE_COMBINE_FP32 && flags != MOE_COMBINE_BF16 && flags != MOE_COMBINE_FP8)
     return fail(MOE_ERR_INVALID_ARG, "flags 0x%x: not a moe_combine value", flags);
   if (T == 0) return MOE_OK;
-  if (!x || !logits || !y || !ws) return fail(MOE_ERR_INVALID_ARG, "null data pointer");
-  if (misaligned(x, 16) || misaligned(y, 16) || misaligned(logits, 4))
-    return fail(MOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned, logits 4-byte aligned");
+  if ((prequant ? (!xq || !xqs) : !x) || !logits || !y || !ws)
+    return fail(MOE_ERR_INVALID_ARG, "null data pointer");
+  if (misaligned(y, 16) || misaligned(logits, 4))
+    return fail(MOE_ERR_INVALID_ARG, "y must be 16-byte aligned, logits 4-byte aligned");
+  if (prequant ? (misaligned(xq, 16) || misaligned(xqs, 4)) : misaligned(x, 16))
+    return fail(MOE_ERR_INVALID_ARG,
+                "x must be 16-byte aligned (codes 16-byte, scales 4-byte aligned)");
   if (misaligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (x == y) return fail(MOE_ERR_INVALID_ARG, "y must not alias x");
+  if (!prequant && x == y) return fail(MOE_ERR_INVALID_ARG, "y must not alias x");
   const WsLayout W = ws_layout(T, top_k, L->E, L->H, L->I, act);
   if (ws_bytes < W.total)
     return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, W.total);
@@ -246,6 +256,8 @@ moe_status moe_forward_ex(moe_layer_t L, const void *x, const float *logits, int
   int32_t *perm = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_PERM]);
   uint8_t *a1c = base + W.off[MOE_WS_A1_CODES];
   uint8_t *a1s = base + W.off[MOE_WS_A1_SCALES];
+  // GEMM1 reads the activation codes from here
+  const uint8_t *g1c = prequant ? xq : a1c, *g1s = prequant ? xqs : a1s;
   uint8_t *a2c = base + W.off[MOE_WS_A2_CODES];
   uint8_t *a2s = base + W.off[MOE_WS_A2_SCALES];
   float *rows = reinterpret_cast<float *>(base + W.off[MOE_WS_ROWS]);
@@ -260,11 +272,14 @@ moe_status moe_forward_ex(moe_layer_t L, const void *x, const float *logits, int
     g.max_mtiles = (N + g.plan.bm() - 1) / g.plan.bm() + (N < L->E ? N : L->E);
   }
   g.num_cus = L->num_cus;
-  g.a1c = a1c; g.a1s = a1s; g.a2c = a2c; g.a2s = a2s;
+  g.a1c = g1c; g.a1s = g1s; g.a2c = a2c; g.a2s = a2s;
   g.perm = perm; g.offsets = offsets; g.mtoff = mtoff; g.mbexp = mbexp; g.wts = wsorted;
   g.w13p = L->w13p; g.w13sp = L->w13sp; g.w2p = L->w2p; g.w2sp = L->w2sp;
   g.rows = rows;
   g.combine = (int)flags;
+  // the fused launch's counters, zeroed by the route/sort launch before it
+  g.sync = reinterpret_cast<int32_t *>(base + W.sync);
+  const int nsync = g.plan.fused ? (int)(kSyncHead + g.max_mtiles) : 0;
 
   const bool prof = L->profiling && L->prof_calls < L->prof_max;
   hipEvent_t *ev = prof ? &L->events[(size_t)L->prof_calls * (MOE_K_NUM + 1)] : nullptr;
@@ -286,6 +301,8 @@ moe_status moe_forward_ex(moe_layer_t L, const void *x, const float *logits, int
     f.ids = ids; f.wts = wts; f.counts = counts; f.offsets = offsets; f.mtoff = mtoff;
     f.mbexp = mbexp; f.perm = perm; f.inv = inv; f.wsorted = wsorted; f.codes = a1c;
     f.scales = a1s;
+    f.sync = g.sync;
+    f.nsync = nsync;
     if (e == hipSuccess) e = launch_front(f, s);
     for (int i = 0; i < 5; ++i) mark();
   } else {
@@ -294,12 +311,13 @@ moe_status moe_forward_ex(moe_layer_t L, const void *x, const float *logits, int
     if (e == hipSuccess) e = launch_sort_hist(ids, T, L->E, top_k, hist, W.nb, s);
     mark();
     if (e == hipSuccess)
-      e = launch_sort_scan(hist, W.nb, L->E, counts, offsets, mtoff, mbexp, g.plan.bm(), s);
+      e = launch_sort_scan(hist, W.nb, L->E, counts, offsets, mtoff, mbexp, g.plan.bm(), g.sync,
+                           nsync, s);
     mark();
     if (e == hipSuccess)
-      e = launch_sort_scatter(ids, T, L->E, top_k, hist, perm, inv, wts, wsorted, s);
+      e = launch_sort_scatter(ids, T, L->E, top_k, hist, offsets, perm, inv, wts, wsorted, s);
     mark();
-    if (e == hipSuccess)
+    if (e == hipSuccess && !prequant)
       e = launch_quant(static_cast<const uint16_t *>(x), T, L->H, act, a1c, a1s, s);
     mark();
   }
@@ -313,6 +331,21 @@ moe_status moe_forward_ex(moe_layer_t L, const void *x, const float *logits, int
   if (e != hipSuccess) return hip_fail(e, "moe_forward launch");
   if (prof) ++L->prof_calls;
   return MOE_OK;
+}
+
+moe_status moe_forward_ex(moe_layer_t L, const void *x, const float *logits, int T, int top_k,
+                          moe_act_dtype act, uint32_t flags, void *y, void *ws, size_t ws_bytes,
+                          hipStream_t s) {
+  return forward_impl(L, false, x, nullptr, nullptr, logits, T, top_k, act, flags, y, ws,
+                      ws_bytes, s);
+}
+
+moe_status moe_forward_prequant(moe_layer_t L, const uint8_t *x_codes, const uint8_t *x_scales,
+                                const float *logits, int T, int top_k, moe_act_dtype act,
+                                uint32_t flags, void *y, void *ws, size_t ws_bytes,
+                                hipStream_t s) {
+  return forward_impl(L, true, nullptr, x_codes, x_scales, logits, T, top_k, act, flags, y, ws,
+                      ws_bytes, s);
 }
 
 moe_status moe_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w,
@@ -354,9 +387,10 @@ moe_status moe_sort(const int32_t *ids, int T, int E, int top_k, int32_t *counts
   const int nb = ceil_div(T, kSortBlock);
   hipError_t e = hipSuccess;
   if (nb > 0) e = launch_sort_hist(ids, T, E, top_k, hist, nb, s);
-  if (e == hipSuccess) e = launch_sort_scan(hist, nb, E, counts, offsets, mtoff, mbexp, kMTile, s);
+  if (e == hipSuccess)
+    e = launch_sort_scan(hist, nb, E, counts, offsets, mtoff, mbexp, kMTile, nullptr, 0, s);
   if (e == hipSuccess && nb > 0)
-    e = launch_sort_scatter(ids, T, E, top_k, hist, perm, inv, nullptr, nullptr, s);
+    e = launch_sort_scatter(ids, T, E, top_k, hist, offsets, perm, inv, nullptr, nullptr, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "sort launch");
 }
 

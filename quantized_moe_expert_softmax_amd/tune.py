@@ -18,13 +18,13 @@ import json
 import sys
 import time
 
-from . import (MOE_ACT_MXFP8_E4M3, MOE_PLAN_STREAM, MOE_PLAN_TILED, alloc_workspace,
-               moe_forward, moe_get_plan, moe_set_plans)
+from . import (MOE_ACT_MXFP8_E4M3, MOE_PLAN_FUSED, MOE_PLAN_STREAM, MOE_PLAN_TILED,
+               alloc_workspace, moe_forward, moe_get_plan, moe_set_plans)
 
 
 def candidates(act: int):
     rows = (32, 64, 96, 128, 160) if act == MOE_ACT_MXFP8_E4M3 else (64, 128)
-    return [(MOE_PLAN_STREAM, 16)] + [(MOE_PLAN_TILED, r) for r in rows]
+    return [(MOE_PLAN_STREAM, 16), (MOE_PLAN_FUSED, 16)] + [(MOE_PLAN_TILED, r) for r in rows]
 
 
 def _time(layer, x, lgs, top_k, act, y, ws, steps, warmup):

@@ -69,6 +69,8 @@ def test_forward_rejects_null_handle(lib):
     assert st == moe.MOE_ERR_INVALID_ARG and "handle" in _err(lib)
     st = lib.moe_forward_ex(None, p, p, 4, 2, 0, 1, p, p, 1 << 20, None)
     assert st == moe.MOE_ERR_INVALID_ARG and "handle" in _err(lib)
+    st = lib.moe_forward_prequant(None, p, p, p, 4, 2, 0, 0, p, p, 1 << 20, None)
+    assert st == moe.MOE_ERR_INVALID_ARG and "handle" in _err(lib)
     assert lib.moe_workspace_bytes(None, 4, 2, 0) == 0
     offs = (ctypes.c_size_t * moe.MOE_WS_NUM)()
     assert lib.moe_workspace_offsets(None, 4, 2, 0, offs) == moe.MOE_ERR_INVALID_ARG

@@ -58,8 +58,9 @@ def test_table_lookup_order_and_fallback():
 
 
 @pytest.mark.parametrize("bad", [
-    dict(rows=48), dict(rows=160, act=1), dict(variant=2), dict(act=5), dict(top_k=0),
+    dict(rows=48), dict(rows=160, act=1), dict(variant=3), dict(act=5), dict(top_k=0),
     dict(top_k=9), dict(t_max=0), dict(variant=moe.MOE_PLAN_STREAM, rows=32),
+    dict(variant=moe.MOE_PLAN_FUSED, rows=32),
 ])
 def test_invalid_plans_rejected(bad):
     w, _, _ = _small(16, 256, 128, 8, 2, seed=13)
@@ -91,3 +92,34 @@ def test_tuner_installs_a_valid_table():
     y, _ = _run(layer, x, lg, k, 0)
     assert_output_close(y, oracle.forward(x, lg, *w, k, 0), "tuned")
     torch.cuda.synchronize()
+
+
+# the fused launch over both front paths (T <= 16 fused front kernel, else the
+# separate route/sort kernels), ragged m-tiles, one expert, E > 256 items
+FUSED_CASES = [(1, 256, 128, 8, 2), (16, 256, 128, 8, 2), (37, 384, 256, 5, 3),
+               (3, 128, 128, 1, 1), (130, 512, 640, 32, 8), (1, 1024, 1152, 64, 6),
+               (300, 256, 256, 16, 4), (17, 256, 128, 1024, 8)]
+
+
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("T,H,I,E,k", FUSED_CASES)
+def test_fused_plan(T, H, I, E, k, act):
+    """The fused launch matches the oracle, writes the same first-stage bytes,
+    and repeated calls on one workspace agree bit for bit (its counters are
+    cleared by every call's routing launch)."""
+    w, x, lg = _small(T, H, I, E, k, seed=T + H + E)
+    layer = _layer(*w)
+    moe.moe_set_plans(layer, [dict(act=act, top_k=k, t_max=T, variant=moe.MOE_PLAN_FUSED,
+                                   rows=16)])
+    ref, a2c, a2s = oracle.forward(x, lg, *w, k, act, want_a2=True)
+    y, ws = _run(layer, x, lg, k, act)
+    assert_output_close(y, ref, "fused T=%d H=%d I=%d E=%d k=%d act=%d" % (T, H, I, E, k, act))
+    mism, smism = _check_workspace(layer, ws, x, lg, k, act, (a2c, a2s))
+    assert mism < 1e-2 and smism < 1e-2, (mism, smism)
+    import torch
+    xd, ld = bf16_dev(x), dev(lg)
+    for _ in range(3):
+        y2 = moe.moe_forward(layer, xd, ld, k, act, ws=ws)
+    torch.cuda.synchronize()
+    from tests.gpu_util import bf16_host_bits
+    assert np.array_equal(bf16_host_bits(y2), y)
