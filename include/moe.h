@@ -85,6 +85,49 @@ moe_status moe_prepare_weights(int E, int H, int I, const void *w13, const void 
                                const void *w2, const void *w2_scale, hipStream_t s,
                                moe_layer_t *out);
 
+/* ---- weight sets owned by the caller, swapped per layer -------------------
+ * The pages run one fused MoE object for every layer of the model and swap
+ * its stage-1 weight pointers per layer ("FlyDSL MegaMoE fused EP-MoE
+ * integration", summary: the per-layer weight swap targets the fused
+ * kernel's runtime weight pointers).  Here: weights packed once into device
+ * memory the caller owns, and a handle (plan table, device properties) whose
+ * forward calls read the weight set last bound to it. */
+typedef struct {
+    void *w13;        /* packed gate/up codes,  bytes[0] of moe_packed_weight_bytes */
+    void *w13_scale;  /* packed gate/up scales, bytes[1]                            */
+    void *w2;         /* packed down codes,     bytes[2]                            */
+    void *w2_scale;   /* packed down scales,    bytes[3]                            */
+} moe_packed_weights;
+
+/* Host out bytes[4]: the sizes of the four packed buffers of an (E, H, I)
+ * expert set (equal to the canonical buffers' sizes).  MOE_ERR_INVALID_ARG on
+ * dimensions moe_prepare_weights rejects. */
+moe_status moe_packed_weight_bytes(int E, int H, int I, size_t bytes[4]);
+
+/* Repack canonical weights (layouts as in moe_prepare_weights) into the
+ * caller's device buffers dst (16-byte aligned, sizes from
+ * moe_packed_weight_bytes, not overlapping the sources).  Enqueue only: no
+ * allocation, no synchronisation; the sources must stay valid until the
+ * repack on s has run. */
+moe_status moe_pack_weights(int E, int H, int I, const void *w13, const void *w13_scale,
+                            const void *w2, const void *w2_scale, const moe_packed_weights *dst,
+                            hipStream_t s);
+
+/* A handle for (E, H, I) layers that owns no weights: forward calls fail
+ * with MOE_ERR_INVALID_ARG until moe_bind_weights has given it a set.
+ * Allocates no device memory. */
+moe_status moe_create_layer(int E, int H, int I, moe_layer_t *out);
+
+/* Point the handle's later calls at the packed set w (device pointers,
+ * copied into the handle; the memory stays the caller's and must outlive
+ * the calls that read it).  w == NULL returns a handle made by
+ * moe_prepare_weights to its own weights (and unbinds a moe_create_layer
+ * handle).  A forward call reads the pointers bound when it is enqueued, so
+ * rebinding between calls on one stream, or between HIP-graph captures, is
+ * safe; it mutates the handle, so it is not concurrent with calls enqueuing
+ * on the same handle from other threads. */
+moe_status moe_bind_weights(moe_layer_t layer, const moe_packed_weights *w);
+
 /* Release a handle and its device memory (synchronises the device first).
  * NULL is ignored. */
 void moe_destroy(moe_layer_t layer);

@@ -40,7 +40,8 @@ KERNELS = ("route", "sort_hist", "sort_scan", "sort_scatter", "quant", "gemm1", 
 MOE_K_NUM = len(KERNELS)
 
 EXPORTS = ("moe_prepare_weights", "moe_destroy", "moe_workspace_bytes", "moe_forward",
-           "moe_forward_ex", "moe_forward_prequant",
+           "moe_forward_ex", "moe_forward_prequant", "moe_packed_weight_bytes",
+           "moe_pack_weights", "moe_create_layer", "moe_bind_weights",
            "moe_workspace_offsets", "moe_route", "moe_sort_workspace_bytes", "moe_sort",
            "moe_quant_act", "moe_set_plans", "moe_get_plan", "moe_profile_enable",
            "moe_profile_read", "moe_status_str", "moe_last_error")
@@ -92,6 +93,10 @@ def load_library(path: str = LIB_PATH):
         lib.moe_forward.argtypes = [P, P, P, I, I, I, P, P, Z, P]
         lib.moe_forward_ex.argtypes = [P, P, P, I, I, I, ctypes.c_uint32, P, P, Z, P]
         lib.moe_forward_prequant.argtypes = [P, P, P, P, I, I, I, ctypes.c_uint32, P, P, Z, P]
+        lib.moe_packed_weight_bytes.argtypes = [I, I, I, P]
+        lib.moe_pack_weights.argtypes = [I, I, I, P, P, P, P, P, P]
+        lib.moe_create_layer.argtypes = [I, I, I, ctypes.POINTER(P)]
+        lib.moe_bind_weights.argtypes = [P, P]
         lib.moe_workspace_offsets.argtypes = [P, I, I, I, P]
         lib.moe_route.argtypes = [P, I, I, I, P, P, P]
         lib.moe_sort_workspace_bytes.argtypes = [I, I, I]
@@ -107,7 +112,8 @@ def load_library(path: str = LIB_PATH):
         lib.moe_last_error.argtypes = []
         lib.moe_last_error.restype = ctypes.c_char_p
         for name in ("moe_prepare_weights", "moe_forward", "moe_forward_ex",
-                     "moe_forward_prequant", "moe_workspace_offsets", "moe_route",
+                     "moe_forward_prequant", "moe_packed_weight_bytes", "moe_pack_weights",
+                     "moe_create_layer", "moe_bind_weights", "moe_workspace_offsets", "moe_route",
                      "moe_sort", "moe_quant_act", "moe_set_plans", "moe_get_plan",
                      "moe_profile_enable", "moe_profile_read"):
             getattr(lib, name).restype = I
@@ -176,6 +182,54 @@ def moe_prepare_weights(E, H, I, w13, w13_scale, w2, w2_scale, stream=None) -> M
     _check(lib.moe_prepare_weights(E, H, I, _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
                                    _stream(stream), ctypes.byref(h)))
     return MoeLayer(h, E, H, I)
+
+
+class PackedWeights(ctypes.Structure):
+    """moe_packed_weights: device pointers of one packed weight set."""
+    _fields_ = [("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
+
+
+def moe_packed_weight_bytes(E: int, H: int, I: int):
+    """Sizes of the four packed buffers (w13, w13_scale, w2, w2_scale) in bytes."""
+    out = (ctypes.c_size_t * 4)()
+    _check(load_library().moe_packed_weight_bytes(E, H, I, out))
+    return list(out)
+
+
+def moe_pack_weights(E, H, I, w13, w13_scale, w2, w2_scale, stream=None):
+    """Repack canonical weights into four new uint8 device tensors (the caller
+    owns them; keep them alive while a layer is bound to them).  Enqueue only."""
+    import torch
+    lib = load_library()
+    _require(w13, 1, (E, 2 * I, H // 2), "w13")
+    _require(w13_scale, 1, (E, 2 * I, H // 32), "w13_scale")
+    _require(w2, 1, (E, H, I // 2), "w2")
+    _require(w2_scale, 1, (E, H, I // 32), "w2_scale")
+    bufs = [torch.empty(n, dtype=torch.uint8, device=w13.device)
+            for n in moe_packed_weight_bytes(E, H, I)]
+    dst = PackedWeights(*(b.data_ptr() for b in bufs))
+    _check(lib.moe_pack_weights(E, H, I, _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+                                ctypes.byref(dst), _stream(stream)))
+    return bufs
+
+
+def moe_create_layer(E: int, H: int, I: int) -> MoeLayer:
+    """A handle with no weights of its own (bind a packed set before calling)."""
+    h = ctypes.c_void_p()
+    _check(load_library().moe_create_layer(E, H, I, ctypes.byref(h)))
+    return MoeLayer(h, E, H, I)
+
+
+def moe_bind_weights(layer: MoeLayer, packed=None):
+    """Point the layer's later calls at a packed set (the four tensors from
+    moe_pack_weights), or back to its own weights with None."""
+    lib = load_library()
+    if packed is None:
+        _check(lib.moe_bind_weights(layer.handle, None))
+        return
+    w = PackedWeights(*(b.data_ptr() for b in packed))
+    _check(lib.moe_bind_weights(layer.handle, ctypes.byref(w)))
 
 
 def moe_workspace_bytes(layer: MoeLayer, T: int, top_k: int, act: int) -> int:

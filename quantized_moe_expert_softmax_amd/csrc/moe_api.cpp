@@ -16,7 +16,8 @@ struct moe_layer {
   int E, H, I;
   int device;
   int num_cus;
-  uint8_t *w13p, *w13sp, *w2p, *w2sp;
+  uint8_t *w13p, *w13sp, *w2p, *w2sp;  // the weight set forward calls read (null: none bound)
+  uint8_t *own[4];                     // packed weights the handle allocated (moe_prepare_weights)
   std::vector<moe_plan> plans;  // per-layer plan table (moe_set_plans)
   // kernel timing (benchmarks only)
   bool profiling;
@@ -117,10 +118,11 @@ moe_status moe_prepare_weights(int E, int H, int I, const void *w13, const void 
   L->profiling = false; L->prof_max = 0; L->prof_calls = 0;
   const size_t b13 = (size_t)E * d13.code_bytes(), s13 = (size_t)E * d13.scale_bytes();
   const size_t b2 = (size_t)E * d2.code_bytes(), s2 = (size_t)E * d2.scale_bytes();
-  hipError_t e = hipMalloc(&L->w13p, b13);
-  if (e == hipSuccess) e = hipMalloc(&L->w13sp, s13);
-  if (e == hipSuccess) e = hipMalloc(&L->w2p, b2);
-  if (e == hipSuccess) e = hipMalloc(&L->w2sp, s2);
+  hipError_t e = hipMalloc(&L->own[0], b13);
+  if (e == hipSuccess) e = hipMalloc(&L->own[1], s13);
+  if (e == hipSuccess) e = hipMalloc(&L->own[2], b2);
+  if (e == hipSuccess) e = hipMalloc(&L->own[3], s2);
+  L->w13p = L->own[0]; L->w13sp = L->own[1]; L->w2p = L->own[2]; L->w2sp = L->own[3];
   if (e != hipSuccess) {
     (void)hipGetLastError();
     moe_destroy(L);
@@ -145,11 +147,79 @@ void moe_destroy(moe_layer_t L) {
   if (!L) return;
   (void)hipDeviceSynchronize();
   for (hipEvent_t ev : L->events) (void)hipEventDestroy(ev);
-  if (L->w13p) (void)hipFree(L->w13p);
-  if (L->w13sp) (void)hipFree(L->w13sp);
-  if (L->w2p) (void)hipFree(L->w2p);
-  if (L->w2sp) (void)hipFree(L->w2sp);
+  for (uint8_t *p : L->own)
+    if (p) (void)hipFree(p);
   delete L;
+}
+
+moe_status moe_packed_weight_bytes(int E, int H, int I, size_t bytes[4]) {
+  std::string why;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "null output array");
+  if (bad_dims(E, H, I, &why)) return fail(MOE_ERR_INVALID_ARG, "%s", why.c_str());
+  const PackDims d13 = pack_dims(2 * I, H), d2 = pack_dims(H, I);
+  bytes[0] = (size_t)E * d13.code_bytes();
+  bytes[1] = (size_t)E * d13.scale_bytes();
+  bytes[2] = (size_t)E * d2.code_bytes();
+  bytes[3] = (size_t)E * d2.scale_bytes();
+  return MOE_OK;
+}
+
+moe_status moe_pack_weights(int E, int H, int I, const void *w13, const void *w13_scale,
+                            const void *w2, const void *w2_scale, const moe_packed_weights *dst,
+                            hipStream_t s) {
+  std::string why;
+  if (bad_dims(E, H, I, &why)) return fail(MOE_ERR_INVALID_ARG, "%s", why.c_str());
+  if (!w13 || !w13_scale || !w2 || !w2_scale || !dst) return fail(MOE_ERR_INVALID_ARG, "null pointer");
+  if (!dst->w13 || !dst->w13_scale || !dst->w2 || !dst->w2_scale)
+    return fail(MOE_ERR_INVALID_ARG, "null packed weight pointer");
+  if (misaligned(w13, 16) || misaligned(w2, 16))
+    return fail(MOE_ERR_INVALID_ARG, "weight code buffers must be 16-byte aligned");
+  if (misaligned(dst->w13, 16) || misaligned(dst->w13_scale, 16) || misaligned(dst->w2, 16) ||
+      misaligned(dst->w2_scale, 16))
+    return fail(MOE_ERR_INVALID_ARG, "packed weight buffers must be 16-byte aligned");
+  moe_status st = check_device(nullptr, nullptr);
+  if (st != MOE_OK) return st;
+  hipError_t e = launch_prepack(static_cast<const uint8_t *>(w13),
+                                static_cast<const uint8_t *>(w13_scale), E, 2 * I, H, true,
+                                static_cast<uint8_t *>(dst->w13),
+                                static_cast<uint8_t *>(dst->w13_scale), s);
+  if (e == hipSuccess)
+    e = launch_prepack(static_cast<const uint8_t *>(w2), static_cast<const uint8_t *>(w2_scale), E,
+                       H, I, false, static_cast<uint8_t *>(dst->w2),
+                       static_cast<uint8_t *>(dst->w2_scale), s);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "weight repack");
+}
+
+moe_status moe_create_layer(int E, int H, int I, moe_layer_t *out) {
+  std::string why;
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "null output handle pointer");
+  *out = nullptr;
+  if (bad_dims(E, H, I, &why)) return fail(MOE_ERR_INVALID_ARG, "%s", why.c_str());
+  int dev = 0, cus = 0;
+  moe_status st = check_device(&dev, &cus);
+  if (st != MOE_OK) return st;
+  moe_layer *L = new moe_layer();
+  L->E = E; L->H = H; L->I = I; L->device = dev; L->num_cus = cus;
+  *out = L;
+  return MOE_OK;
+}
+
+moe_status moe_bind_weights(moe_layer_t L, const moe_packed_weights *w) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "null layer handle");
+  if (!w) {
+    L->w13p = L->own[0]; L->w13sp = L->own[1]; L->w2p = L->own[2]; L->w2sp = L->own[3];
+    return MOE_OK;
+  }
+  if (!w->w13 || !w->w13_scale || !w->w2 || !w->w2_scale)
+    return fail(MOE_ERR_INVALID_ARG, "null packed weight pointer");
+  if (misaligned(w->w13, 16) || misaligned(w->w13_scale, 16) || misaligned(w->w2, 16) ||
+      misaligned(w->w2_scale, 16))
+    return fail(MOE_ERR_INVALID_ARG, "packed weight buffers must be 16-byte aligned");
+  L->w13p = static_cast<uint8_t *>(w->w13);
+  L->w13sp = static_cast<uint8_t *>(w->w13_scale);
+  L->w2p = static_cast<uint8_t *>(w->w2);
+  L->w2sp = static_cast<uint8_t *>(w->w2_scale);
+  return MOE_OK;
 }
 
 size_t moe_workspace_bytes(moe_layer_t L, int T, int top_k, moe_act_dtype act) {
@@ -232,6 +302,7 @@ static moe_status forward_impl(moe_layer_t L, bool prequant, const void *x, cons
   if (flags != MOE_COMBINE_FP32 && flags != MOE_COMBINE_BF16 && flags != MOE_COMBINE_FP8)
     return fail(MOE_ERR_INVALID_ARG, "flags 0x%x: not a moe_combine value", flags);
   if (T == 0) return MOE_OK;
+  if (!L->w13p) return fail(MOE_ERR_INVALID_ARG, "no weights bound to the layer");
   if ((prequant ? (!xq || !xqs) : !x) || !logits || !y || !ws)
     return fail(MOE_ERR_INVALID_ARG, "null data pointer");
   if (misaligned(y, 16) || misaligned(logits, 4))

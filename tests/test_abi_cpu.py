@@ -128,3 +128,32 @@ def test_plan_calls_validate(lib):
     assert lib.moe_set_plans(None, entry, 1) == moe.MOE_ERR_INVALID_ARG and "handle" in _err(lib)
     out = moe.MoePlan()
     assert lib.moe_get_plan(None, 4, 2, 0, ctypes.byref(out)) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_packed_weight_bytes_equal_canonical_sizes(lib):
+    """The packed layout holds exactly the canonical bytes (host-only call)."""
+    for E, H, I in ((8, 256, 128), (384, 7168, 3072), (1, 128, 128), (128, 5120, 640)):
+        assert moe.moe_packed_weight_bytes(E, H, I) == [
+            E * 2 * I * H // 2, E * 2 * I * H // 32, E * H * I // 2, E * H * I // 32]
+    out = (ctypes.c_size_t * 4)()
+    for E, H, I in ((0, 256, 128), (8, 100, 128), (8, 256, 96)):
+        assert lib.moe_packed_weight_bytes(E, H, I, out) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_packed_weight_bytes(8, 256, 128, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_weight_binding_calls_validate(lib):
+    p = ctypes.c_void_p(256)
+    h = ctypes.c_void_p()
+    assert lib.moe_create_layer(0, 256, 128, ctypes.byref(h)) == moe.MOE_ERR_INVALID_ARG
+    assert h.value is None
+    assert lib.moe_create_layer(8, 256, 128, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_bind_weights(None, None) == moe.MOE_ERR_INVALID_ARG
+    dst = moe.PackedWeights(256, 256, 0, 256)
+    st = lib.moe_pack_weights(8, 256, 128, p, p, p, p, ctypes.byref(dst), None)
+    assert st == moe.MOE_ERR_INVALID_ARG and "null" in _err(lib)
+    dst = moe.PackedWeights(256, 256, 264, 256)
+    st = lib.moe_pack_weights(8, 256, 128, p, p, p, p, ctypes.byref(dst), None)
+    assert st == moe.MOE_ERR_INVALID_ARG and "aligned" in _err(lib)
+    assert lib.moe_pack_weights(8, 256, 128, p, p, p, p, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_pack_weights(8, 100, 128, p, p, p, p, ctypes.byref(dst), None) == \
+        moe.MOE_ERR_INVALID_ARG
