@@ -339,10 +339,6 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(KArgs p) {
   }
 }
 
-// how the four waves of a tiled workgroup split a BM x 256 item: 1 = all rows
-// x one quad each, 2 = half the rows x two quads each
-constexpr int kTiledSplit = 1;
-
 GemmPlan choose_plan(int T, int top_k, int E, int act) {
   // The average rows per expert decides between weight streaming (fewer than
   // 2 rows) and the pipelined tiled kernel, whose BM covers the mean plus 1.5

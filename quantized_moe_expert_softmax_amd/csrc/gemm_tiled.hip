@@ -101,6 +101,54 @@ struct TileShape {
   static __device__ __forceinline__ int sslot(int r) { return (r / RPW) * 64 + (r % RPW); }
 };
 
+// Epilogue of one weight quad u of a work item (output tiles 4u .. 4u+3 of
+// acc; tile0 the quad's first 16-row weight tile): GEMM1 SwiGLU + requant to
+// the A2 rows, GEMM2 weighted rows to the staging buffer.  A padded row
+// (loaded from the last valid row) stores the same values as that row, so
+// every store is unconditional.
+template <class F, int FMT, int MTW, int NT, bool SECOND>
+__device__ __forceinline__ void store_item(const KArgs &p, const v4f (&acc)[MTW][NT], int u,
+                                           int tile0, int mw0, int row0, int nrows, int g,
+                                           int r16, size_t a2row) {
+  if (!SECOND) {
+    const int j = tile0 / 4;  // unit: h columns [32j, 32j + 32)
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
+      float g0[4], g1[4], u0[4], u1[4];
+      uint8_t *ar[4], *sr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int mrow = 16 * (mw0 + m) + 4 * g + r;
+        const size_t prow = (size_t)(row0 + min(mrow, nrows - 1));
+        g0[r] = acc[m][4 * u][r]; g1[r] = acc[m][4 * u + 1][r];
+        u0[r] = acc[m][4 * u + 2][r]; u1[r] = acc[m][4 * u + 3][r];
+        ar[r] = p.a2c + prow * a2row;
+        sr[r] = p.a2s + prow * (p.I / 32);
+      }
+      swiglu_requant_n<F, FMT, 4>(g0, g1, u0, u1, ar, sr, j, r16);
+    }
+  } else {
+    float wa[MTW][4];
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        wa[m][r] = p.wts[row0 + min(16 * (mw0 + m) + 4 * g + r, nrows - 1)];
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
+      size_t prow[4];
+      float t[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        prow[r] = (size_t)(row0 + min(16 * (mw0 + m) + 4 * g + r, nrows - 1));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[r][q] = wa[m][r] * acc[m][4 * u + q][r];
+      }
+      stage_store_n<4>(p, prow, 16 * tile0, r16, t);
+    }
+  }
+}
+
 template <int FMT, int MT, int RS, int QPW, bool SECOND>
 __global__ __launch_bounds__(64 * RS * 4 / QPW, 1) void tiled_kernel(KArgs p) {
   using F = typename ActFmt<FMT>::F;
@@ -343,6 +391,196 @@ __global__ __launch_bounds__(64 * RS * 4 / QPW, 1) void tiled_kernel(KArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Producer/consumer form of the tiled kernel.  The copy waits count a wave's
+// own copies in issue order, so in the form above, where every wave copies
+// both operands, a step's weights (HBM) and activations (L2) share one
+// deadline.  Here waves 0-3 each copy only their own weight quad (four 1 KiB
+// fragments and its scale dword) into a ring of NB weight stages, NB - 1
+// steps ahead, and wait only for those; wave 4 copies the activation tile
+// and its scales into the NA-stage activation ring and waits only for
+// those.  Copies past the last K step re-read the last step (cache hits)
+// into a ring slot no later step reads.  One barrier per step.
+// ---------------------------------------------------------------------------
+template <int FMT, int MT>
+struct PcShape {
+  static constexpr int BM = 16 * MT;
+  static constexpr int ROWB = FMT == 0 ? 128 : 64;    // activation bytes per row per K step
+  static constexpr int CH = ROWB / 16;
+  static constexpr int A_BYTES = BM * ROWB;
+  static constexpr int A_CHUNKS = A_BYTES / 1024;     // 1 KiB copies per stage
+  static constexpr int SC = (BM + 63) / 64;           // scale copies per stage (64 rows each)
+  static constexpr int CA = A_CHUNKS + SC;            // producer copies per step
+  static constexpr int OFF_AS = A_BYTES;              // [BM] scale dwords
+  static constexpr int A_STAGE = A_BYTES + 1024;
+  static constexpr int CB = 5;                        // consumer copies per step
+  static constexpr int OFF_BS = 4 * 4096;
+  static constexpr int B_STAGE = OFF_BS + 4 * 256;
+  static constexpr int NA = 3;
+  static constexpr int NB_FIT = (160 * 1024 - NA * A_STAGE) / B_STAGE;
+  static constexpr int NB = NB_FIT < 5 ? NB_FIT : 5;
+  static constexpr int B_BASE = NA * A_STAGE;
+  static constexpr int LDS = B_BASE + NB * B_STAGE;
+  static_assert(A_BYTES % 1024 == 0, "activation tile must fill whole copies");
+  static_assert(BM <= 256, "scale slots");
+  static_assert(NB >= 3, "weight ring");
+  static_assert((NA - 1) * CA < 64 && (NB - 1) * CB < 64, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <int FMT, int MT, bool SECOND>
+__global__ __launch_bounds__(320, 1) void pc_kernel(KArgs p) {
+  using F = typename ActFmt<FMT>::F;
+  using PS = PcShape<FMT, MT>;
+  constexpr int NA = PS::NA, NB = PS::NB, BM = PS::BM, ROWB = PS::ROWB, CH = PS::CH;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[PS::LDS];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool producer = uniform(wave) == 4;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int K = SECOND ? p.I : p.H;
+  const int S = K / 128;
+  const int ntiles = (SECOND ? p.H : 2 * p.I) / 16;
+  const int NBLK = (ntiles + 15) / 16;
+  const int n_mb = uniform(p.mtoff[p.E]);
+  const long total = (long)n_mb * NBLK;
+  const size_t arow = FMT == 0 ? (size_t)K : (size_t)K / 2;
+  const size_t srow = (size_t)K / 32;
+  const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
+  const size_t quad_bytes = (size_t)S * 4096, quad_dwords = (size_t)S * 64;
+  const uint8_t *__restrict__ A = SECOND ? p.a2c : p.a1c;
+  const uint8_t *__restrict__ As = SECOND ? p.a2s : p.a1s;
+  const int G = gridDim.x;
+  const int L = (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8);
+  const int swz = (FMT == 0) ? (r16 & 7) : (r16 & 3);
+  const int aoff_lo = r16 * ROWB + 16 * (g ^ swz);
+  const int aoff_hi = r16 * ROWB + 16 * ((4 + g) ^ swz);
+
+  for (long w = L; w < total; w += G) {
+    const int gmb = (int)(w / NBLK), nb = (int)(w % NBLK);
+    const int e = uniform(p.mbexp[gmb]);
+    const int mb = gmb - uniform(p.mtoff[e]);
+    const int row0 = uniform(p.offsets[e]) + BM * mb;
+    const int nrows = min(BM, uniform(p.offsets[e + 1]) - row0);
+
+    if (producer) {
+      const uint8_t *asrc[PS::A_CHUNKS];
+#pragma unroll
+      for (int k = 0; k < PS::A_CHUNKS; ++k) {
+        const int ci = k * 64 + lane;  // 16-byte LDS chunk this lane fills
+        const int row = ci / CH, slot = ci % CH;
+        const int rr = min(row, nrows - 1);
+        const size_t ridx = SECOND ? (size_t)(row0 + rr) : (size_t)(p.perm[row0 + rr] / p.top_k);
+        asrc[k] = A + ridx * arow + 16 * (slot ^ (row & (CH - 1)));
+      }
+      const uint8_t *ssrc[PS::SC];
+#pragma unroll
+      for (int j = 0; j < PS::SC; ++j) {
+        const int rr = min(min(64 * j + lane, BM - 1), nrows - 1);
+        const size_t ridx = SECOND ? (size_t)(row0 + rr) : (size_t)(p.perm[row0 + rr] / p.top_k);
+        ssrc[j] = As + ridx * srow;
+      }
+      auto issue_a = [&](int st) __attribute__((always_inline)) {
+        const int sr = min(st, S - 1);
+        uint8_t *stg = lds + (st % NA) * PS::A_STAGE;
+#pragma unroll
+        for (int k = 0; k < PS::A_CHUNKS; ++k)
+          copy16_to_lds(asrc[k] + (size_t)ROWB * sr, stg + k * 1024);
+#pragma unroll
+        for (int j = 0; j < PS::SC; ++j) copy4_to_lds(ssrc[j] + 4 * sr, stg + PS::OFF_AS + 256 * j);
+      };
+#pragma unroll
+      for (int st = 0; st < NA - 1; ++st) issue_a(st);
+      wait_vm<(NA - 2) * PS::CA>();  // step 0 has landed
+      barrier_keep_copies();
+      for (int s = 0; s < S; ++s) {
+        issue_a(s + NA - 1);
+        wait_vm<(NA - 2) * PS::CA>();  // step s+1 has landed
+        barrier_keep_copies();
+      }
+      wait_vm<0>();
+    } else {
+      const int qd = wave;  // the weight quad this wave computes and copies
+      const int t0 = 16 * nb + 4 * qd;  // quads past the last tile read quad 0
+      const size_t qb = (size_t)e * (ntiles / 4) + (t0 < ntiles ? t0 / 4 : 0);
+      const uint8_t *wsrc = p.wp + qb * quad_bytes + (size_t)lane * 16;
+      const uint32_t *wssrc = p.wsp + qb * quad_dwords + lane;
+      auto issue_b = [&](int st, int i) __attribute__((always_inline)) {
+        const int sr = min(st, S - 1);
+        uint8_t *sw = lds + PS::B_BASE + (st % NB) * PS::B_STAGE;
+        if (i < 4)
+          copy16_to_lds(wsrc + (size_t)sr * 4096 + i * 1024, sw + (4 * qd + i) * 1024);
+        else
+          copy4_to_lds(wssrc + (size_t)sr * 64, sw + PS::OFF_BS + qd * 256);
+      };
+      auto read_a = [&](const uint8_t *st, int m) __attribute__((always_inline)) {
+        v8i a;
+        const uint8_t *base = st + m * 16 * ROWB;
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(base + aoff_lo);
+        a[0] = (int)lo[0]; a[1] = (int)lo[1]; a[2] = (int)lo[2]; a[3] = (int)lo[3];
+        if (FMT == 0) {
+          const u32x4 hi = *reinterpret_cast<const u32x4 *>(base + aoff_hi);
+          a[4] = (int)hi[0]; a[5] = (int)hi[1]; a[6] = (int)hi[2]; a[7] = (int)hi[3];
+        } else {
+          a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
+        }
+        return a;
+      };
+      auto read_sa = [&](const uint8_t *st, int m) __attribute__((always_inline)) {
+        return (int)st[PS::OFF_AS + 4 * (16 * m + r16) + g];
+      };
+#pragma unroll
+      for (int st = 0; st < NB - 1; ++st)
+#pragma unroll
+        for (int i = 0; i < PS::CB; ++i) issue_b(st, i);
+      wait_vm<(NB - 2) * PS::CB>();  // step 0 has landed
+      barrier_keep_copies();
+
+      v4f acc[MT][4];
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[m][q] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < S; ++s) {
+        const uint8_t *st = lds + (s % NA) * PS::A_STAGE;
+        const uint8_t *sw = lds + PS::B_BASE + (s % NB) * PS::B_STAGE;
+        const int sb = *reinterpret_cast<const int *>(sw + PS::OFF_BS + qd * 256 + lane * 4);
+        v8i b[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(sw + qd * 4096 + q * 1024 + lane * 16);
+          b[q][0] = (int)v[0]; b[q][1] = (int)v[1]; b[q][2] = (int)v[2]; b[q][3] = (int)v[3];
+          b[q][4] = 0; b[q][5] = 0; b[q][6] = 0; b[q][7] = 0;
+        }
+        v8i acur = read_a(st, 0);
+        int sacur = read_sa(st, 0);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+          for (int i = m * PS::CB / MT; i < (m + 1) * PS::CB / MT; ++i) issue_b(s + NB - 1, i);
+          v8i anext = acur;
+          int sanext = sacur;
+          if (m + 1 < MT) {
+            anext = read_a(st, m + 1);
+            sanext = read_sa(st, m + 1);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[m][q] = mfma_q<FMT>(q, acur, b[q], acc[m][q], sacur, sb);
+          __builtin_amdgcn_sched_barrier(0);
+          acur = anext;
+          sacur = sanext;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<(NB - 2) * PS::CB>();  // step s+1's weights have landed
+        barrier_keep_copies();
+      }
+      wait_vm<0>();
+      if (t0 < ntiles) store_item<F, FMT, MT, 4, SECOND>(p, acc, 0, t0, 0, row0, nrows, g, r16, a2row);
+    }
+  }
+}
+
 template <int RS, int QPW, bool SECOND>
 static hipError_t launch_tiled_w(const GemmArgs &a, const KArgs &k, hipStream_t s) {
   const unsigned grid = (unsigned)(a.num_cus / 8 * 8);  // one workgroup per CU
@@ -366,11 +604,38 @@ static hipError_t launch_tiled_w(const GemmArgs &a, const KArgs &k, hipStream_t 
   return hipGetLastError();
 }
 
-// Only the one-row-split form is built: the 2 x 2 and eight-wave forms
-// (launch_tiled_w<2, 2> / <2, 1>) measured no faster on the 7168 x 3072 layer.
+template <bool SECOND>
+static hipError_t launch_pc(const GemmArgs &a, const KArgs &k, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.num_cus / 8 * 8);  // one workgroup per CU
+#define PC(F_, MT_)                                          \
+  case MT_:                                                  \
+    pc_kernel<F_, MT_, SECOND><<<grid, 320, 0, s>>>(k);      \
+    break;
+  if (a.act == MOE_ACT_MXFP8_E4M3) {
+    switch (a.plan.mt) {
+      PC(0, 2) PC(0, 4) PC(0, 6) PC(0, 8) PC(0, 10)
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.plan.mt) {
+      PC(4, 4) PC(4, 8)
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef PC
+  return hipGetLastError();
+}
+
+// Of the form-1 wave splits only the one-row split is built: the 2 x 2 and
+// eight-wave forms (launch_tiled_w<2, 2> / <2, 1>) measured no faster on the
+// 7168 x 3072 layer.
 template <bool SECOND>
 static hipError_t launch_tiled(const GemmArgs &a, const KArgs &k, hipStream_t s) {
-  if (a.plan.split != 1) return hipErrorInvalidValue;
+  // split 2: GEMM1 in the producer/consumer form, 7-8% faster than form 1 on
+  // the 7168 x 3072 and 5120 x 640 layers at T >= 8192 (GEMM2's staging
+  // epilogue does not fit the register budget of two waves on one SIMD)
+  if (a.plan.split == 2 && !SECOND) return launch_pc<SECOND>(a, k, s);
+  if (a.plan.split != 1 && a.plan.split != 2) return hipErrorInvalidValue;
   return launch_tiled_w<1, 1, SECOND>(a, k, s);
 }
 

@@ -130,10 +130,15 @@ hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int E, in
 //           go straight from HBM to VGPRs (decode: few rows per expert)
 //   tiled:  bm = 16*MT rows per work item staged in LDS and shared by the
 //           waves, each wave owning 64 weight rows (prefill)
+// Form of the tiled kernels: 1 = four waves that each copy part of both
+// operands; 2 = GEMM1 with four MFMA waves that copy only their own weights
+// and a fifth wave that copies the activations (GEMM2 stays in form 1).
+constexpr int kTiledSplit = 2;
+
 struct GemmPlan {
   bool tiled;
   int mt;   // 16-row MFMA tiles per work item (1 for stream)
-  int split;  // tiled: 1 = each wave all BM rows x one quad, 2 = BM/2 rows x two quads
+  int split;  // tiled kernel form (kTiledSplit)
   bool fused = false;  // stream only: GEMM1 and GEMM2 items in one persistent launch
   int bm() const { return 16 * mt; }
 };

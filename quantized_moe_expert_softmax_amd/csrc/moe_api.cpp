@@ -242,7 +242,7 @@ namespace {
 GemmPlan plan_for(const moe_layer *L, int T, int top_k, int act) {
   for (const moe_plan &p : L->plans)
     if (p.act == act && p.top_k == top_k && T <= p.t_max)
-      return p.variant == MOE_PLAN_TILED ? GemmPlan{true, p.rows / 16, 1}
+      return p.variant == MOE_PLAN_TILED ? GemmPlan{true, p.rows / 16, kTiledSplit}
                                          : GemmPlan{false, 1, 1, p.variant == MOE_PLAN_FUSED};
   return choose_plan(T, top_k, L->E, act);
 }
