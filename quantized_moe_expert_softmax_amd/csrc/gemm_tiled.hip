@@ -128,12 +128,8 @@ __device__ __forceinline__ void store_item(const KArgs &p, const v4f (&acc)[MTW]
       swiglu_requant_n<F, FMT, 4>(g0, g1, u0, u1, ar, sr, j, r16);
     }
   } else {
-    float wa[MTW][4];
-#pragma unroll
-    for (int m = 0; m < MTW; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        wa[m][r] = p.wts[row0 + min(16 * (mw0 + m) + 4 * g + r, nrows - 1)];
+    // the routing weights are loaded per m-tile (all of them at once do not
+    // fit the register budget of the producer/consumer form)
 #pragma unroll
     for (int m = 0; m < MTW; ++m) {
       size_t prow[4];
@@ -141,8 +137,9 @@ __device__ __forceinline__ void store_item(const KArgs &p, const v4f (&acc)[MTW]
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         prow[r] = (size_t)(row0 + min(16 * (mw0 + m) + 4 * g + r, nrows - 1));
+        const float wa = p.wts[prow[r]];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) t[r][q] = wa[m][r] * acc[m][4 * u + q][r];
+        for (int q = 0; q < 4; ++q) t[r][q] = wa * acc[m][4 * u + q][r];
       }
       stage_store_n<4>(p, prow, 16 * tile0, r16, t);
     }
@@ -631,11 +628,12 @@ static hipError_t launch_pc(const GemmArgs &a, const KArgs &k, hipStream_t s) {
 // 7168 x 3072 layer.
 template <bool SECOND>
 static hipError_t launch_tiled(const GemmArgs &a, const KArgs &k, hipStream_t s) {
-  // split 2: GEMM1 in the producer/consumer form, 7-8% faster than form 1 on
-  // the 7168 x 3072 and 5120 x 640 layers at T >= 8192 (GEMM2's staging
-  // epilogue does not fit the register budget of two waves on one SIMD)
-  if (a.plan.split == 2 && !SECOND) return launch_pc<SECOND>(a, k, s);
-  if (a.plan.split != 1 && a.plan.split != 2) return hipErrorInvalidValue;
+  // split 2: both GEMMs in the producer/consumer form; on the 7168 x 3072
+  // and 5120 x 640 layers at T >= 8192 it measured 7-8% faster than form 1
+  // for GEMM1 and 2-6% faster for GEMM2 (whose epilogue loads the routing
+  // weights per m-tile to fit two waves on one SIMD)
+  if (a.plan.split == 2) return launch_pc<SECOND>(a, k, s);
+  if (a.plan.split != 1) return hipErrorInvalidValue;
   return launch_tiled_w<1, 1, SECOND>(a, k, s);
 }
 
