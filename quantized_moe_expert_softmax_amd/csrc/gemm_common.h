@@ -113,8 +113,6 @@ __device__ __forceinline__ void row16_max_n(uint32_t (&v)[NR]) {
   for (int i = 0; i < NR; ++i) v[i] = max(v[i], dpp<0x140>(v[i]));
 }
 
-// GEMM1 epilogue for NR accumulator rows at once: for row i, lane c = l%16
-// holds gate/up columns 32j + c (lo) and 32j + 16 + c (hi) of one token row;
 // A byte store; COH: a device-coherent one (an agent-scope relaxed atomic
 // store, which writes through to the level all XCDs share), for data another
 // workgroup of the same launch reads.
@@ -124,6 +122,32 @@ __device__ __forceinline__ void store_u8(uint8_t *p, uint32_t v) {
     __hip_atomic_store(p, (uint8_t)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else
     *p = (uint8_t)v;
+}
+
+// GEMM1 epilogue for NR accumulator rows at once: for row i, lane c = l%16
+// holds gate/up columns 32j + c (lo) and 32j + 16 + c (hi) of one token row.
+// The element codes (clo: column c, chi: column 16 + c) and block exponent
+// of NR rows' h = silu(gate) * up blocks (amax over the 16 lanes of a row).
+template <class F, int NR>
+__device__ __forceinline__ void swiglu_codes_n(const float (&glo)[NR], const float (&ghi)[NR],
+                                               const float (&ulo)[NR], const float (&uhi)[NR],
+                                               uint32_t (&clo)[NR], uint32_t (&chi)[NR],
+                                               int (&X)[NR]) {
+  float hlo[NR], hhi[NR];
+  uint32_t am[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    hlo[i] = silu(glo[i]) * ulo[i];
+    hhi[i] = silu(ghi[i]) * uhi[i];
+    am[i] = max(f32_bits(hlo[i]) & 0x7fffffffu, f32_bits(hhi[i]) & 0x7fffffffu);
+  }
+  row16_max_n<NR>(am);
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    X[i] = block_exponent<F>(am[i]);
+    clo[i] = encode_element<F>(f32_bits(hlo[i]), X[i]);
+    chi[i] = encode_element<F>(f32_bits(hhi[i]), X[i]);
+  }
 }
 
 // h = silu(gate) * up; the 32 h values of the row form one 1x32 block (amax
@@ -136,23 +160,9 @@ __device__ __forceinline__ void swiglu_requant_n(const float (&glo)[NR], const f
                                                  const float (&ulo)[NR], const float (&uhi)[NR],
                                                  uint8_t *const (&a2row)[NR],
                                                  uint8_t *const (&a2srow)[NR], int j, int c) {
-  float hlo[NR], hhi[NR];
-  uint32_t am[NR];
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    hlo[i] = silu(glo[i]) * ulo[i];
-    hhi[i] = silu(ghi[i]) * uhi[i];
-    am[i] = max(f32_bits(hlo[i]) & 0x7fffffffu, f32_bits(hhi[i]) & 0x7fffffffu);
-  }
-  row16_max_n<NR>(am);
   uint32_t clo[NR], chi[NR];
   int X[NR];
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    X[i] = block_exponent<F>(am[i]);
-    clo[i] = encode_element<F>(f32_bits(hlo[i]), X[i]);
-    chi[i] = encode_element<F>(f32_bits(hhi[i]), X[i]);
-  }
+  swiglu_codes_n<F, NR>(glo, ghi, ulo, uhi, clo, chi, X);
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     if (FMT == 0) {
@@ -240,6 +250,39 @@ __device__ __forceinline__ void stage_store_n(const KArgs &p, const size_t (&pro
       }
     }
   }
+}
+
+// 4 x 4 byte transpose across the four lanes of a quad (lanes 4k .. 4k+3;
+// j = lane & 3) by two DPP exchanges (lanes j ^ 2, then j ^ 1): on entry byte
+// r of lane j's dword is M[r][j], on exit M[j][r].
+__device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t d, int j) {
+  const uint32_t x = dpp<0x4E>(d);
+  d = (j & 2) == 0 ? (d & 0xffffu) | (x << 16) : (x >> 16) | (d & 0xffff0000u);
+  const uint32_t y = dpp<0xB1>(d);
+  return (j & 1) == 0 ? (d & 0x00ff00ffu) | ((y & 0x00ff00ffu) << 8)
+                      : ((y >> 8) & 0x00ff00ffu) | (d & 0xff00ff00u);
+}
+
+// GEMM1 epilogue with dword stores (MXFP8 A2): for the four rows 4g + r of
+// a row group, lane c = 4k + jq holds the codes of columns 32 unit + c and
+// 32 unit + 16 + c; after a byte transpose in each quad, lane (k, jq) holds
+// row 4g + jq's codes of columns 4k .. 4k+3 (and 16 + 4k ..), stored as two
+// dwords, plus the row's scale byte (the four lanes of a row write the same
+// byte).  a2row / a2srow: the A2 code and scale rows of the lane's row.
+__device__ __forceinline__ void swiglu_store_f8_t(const float (&glo)[4], const float (&ghi)[4],
+                                                  const float (&ulo)[4], const float (&uhi)[4],
+                                                  uint8_t *a2row, uint8_t *a2srow, int unit,
+                                                  int c) {
+  uint32_t clo[4], chi[4];
+  int X[4];
+  swiglu_codes_n<E4M3, 4>(glo, ghi, ulo, uhi, clo, chi, X);
+  const int jq = c & 3;
+  const uint32_t lo = quad_transpose_bytes(clo[0] | (clo[1] << 8) | (clo[2] << 16) | (clo[3] << 24), jq);
+  const uint32_t hi = quad_transpose_bytes(chi[0] | (chi[1] << 8) | (chi[2] << 16) | (chi[3] << 24), jq);
+  const int Xr = jq == 0 ? X[0] : jq == 1 ? X[1] : jq == 2 ? X[2] : X[3];
+  *reinterpret_cast<uint32_t *>(a2row + 32 * unit + 4 * (c >> 2)) = lo;
+  *reinterpret_cast<uint32_t *>(a2row + 32 * unit + 16 + 4 * (c >> 2)) = hi;
+  a2srow[unit] = (uint8_t)(Xr + 127);
 }
 
 // Tiled (prefill) variant, in gemm_tiled.hip.

@@ -112,6 +112,10 @@ template <class F, int FMT, int MTW, int NT, bool SECOND>
 __device__ __forceinline__ void store_item(const KArgs &p, const v4f (&acc)[MTW][NT], int u,
                                            int tile0, int mw0, int row0, int nrows, int g,
                                            int r16, size_t a2row) {
+  // the row of this lane after a quad transpose (dword-store epilogue)
+  auto trow = [&](int m) __attribute__((always_inline)) {
+    return (size_t)(row0 + min(16 * (mw0 + m) + 4 * g + (r16 & 3), nrows - 1));
+  };
   if (!SECOND) {
     const int j = tile0 / 4;  // unit: h columns [32j, 32j + 32)
 #pragma unroll
@@ -127,7 +131,12 @@ __device__ __forceinline__ void store_item(const KArgs &p, const v4f (&acc)[MTW]
         ar[r] = p.a2c + prow * a2row;
         sr[r] = p.a2s + prow * (p.I / 32);
       }
-      swiglu_requant_n<F, FMT, 4>(g0, g1, u0, u1, ar, sr, j, r16);
+      if (FMT == 0) {
+        const size_t prow = trow(m);
+        swiglu_store_f8_t(g0, g1, u0, u1, p.a2c + prow * a2row, p.a2s + prow * (p.I / 32), j, r16);
+      } else {
+        swiglu_requant_n<F, FMT, 4>(g0, g1, u0, u1, ar, sr, j, r16);
+      }
     }
   } else {
     // the routing weights are loaded per m-tile (all of them at once do not
@@ -143,6 +152,8 @@ __device__ __forceinline__ void store_item(const KArgs &p, const v4f (&acc)[MTW]
 #pragma unroll
         for (int q = 0; q < 4; ++q) t[r][q] = wa * acc[m][4 * u + q][r];
       }
+      // (a quad-transposed form with one 16-byte store per tile measured
+      // 14-22% slower for GEMM2 than these 64-byte row pieces)
       stage_store_n<4>(p, prow, 16 * tile0, r16, t);
     }
   }
@@ -467,6 +478,67 @@ __global__ __launch_bounds__(64 * (4 + kPcProducers), 1) void pc_kernel(KArgs p)
   const int aoff_lo = r16 * ROWB + 16 * (g ^ swz);
   const int aoff_hi = r16 * ROWB + 16 * ((4 + g) ^ swz);
 
+  // Consumer weight stream across items (XITEM): the copies of a step NB - 1
+  // steps ahead run on from an item's last steps into the next item's first
+  // ones (the next item of this workgroup is w + G), so the weights keep
+  // streaming through the epilogue and an item never starts on an empty
+  // ring.  The ring slot of a step is its position in this workgroup's whole
+  // sequence of steps, modulo NB.  Past the last item the copies re-read a
+  // valid step into slots no step reads.  It measured 1.5% faster per call
+  // (A4W4, T = 16384, MT = 8); at MT = 10 its extra live registers spill, so
+  // there each item issues its own first NB - 1 steps and its copies past
+  // the last step re-read that step.
+  constexpr bool XITEM = MT <= 8;
+  const int qd = uniform(wave & 3);  // the weight quad a consumer wave computes and copies
+  const int total_i = (int)total;      // items fit 32 bits (m-blocks x n-blocks)
+  auto quad_of = [&](int wi) __attribute__((always_inline)) {
+    const int ei = uniform(p.mbexp[wi / NBLK]);
+    const int ti = 16 * (wi % NBLK) + 4 * qd;  // quads past the last tile read quad 0
+    return uniform(ei * (ntiles / 4) + (ti < ntiles ? ti / 4 : 0));
+  };
+  int cw = L;         // item of the next copy
+  int cs = 0;         // its step
+  int cslot = 0;      // its ring slot
+  int cqb = L < total_i ? quad_of(L) : 0;
+  int rslot = 0;      // ring slot of the current item's step 0
+  // weight copy i of the cursor's step
+  auto issue_next = [&](int i) __attribute__((always_inline)) {
+    const int sr = cw < total_i ? cs : S - 1;
+    uint8_t *sw = lds + PS::B_BASE + cslot * PS::B_STAGE;
+    // a wave-uniform base plus a 32-bit lane offset (the scalar-base form of
+    // the copy: no 64-bit address per lane)
+    if (i < 4)
+      copy16_to_lds(p.wp + ((size_t)cqb * quad_bytes + (size_t)sr * 4096) +
+                        (uint32_t)(i * 1024 + lane * 16),
+                    sw + (4 * qd + i) * 1024);
+    else
+      copy4_to_lds(reinterpret_cast<const uint8_t *>(p.wsp + (size_t)cqb * quad_dwords +
+                                                     (size_t)sr * 64) +
+                       (uint32_t)(lane * 4),
+                   sw + PS::OFF_BS + qd * 256);
+  };
+  // the cursor moves to the next step once all its copies are issued
+  auto advance = [&]() __attribute__((always_inline)) {
+    cslot = cslot + 1 == NB ? 0 : cslot + 1;
+    if (++cs == S) {
+      if (XITEM) {
+        cs = 0;
+        cw += G;
+        if (cw < total_i) cqb = quad_of(cw);
+      } else {
+        cs = S - 1;  // re-read the last step until the next item starts
+      }
+    }
+  };
+  if (XITEM && !producer) {
+#pragma unroll
+    for (int st = 0; st < NB - 1; ++st) {
+#pragma unroll
+      for (int i = 0; i < PS::CB; ++i) issue_next(i);
+      advance();
+    }
+  }
+
   for (long w = L; w < total; w += G) {
     const int gmb = (int)(w / NBLK), nb = (int)(w % NBLK);
     const int e = uniform(p.mbexp[gmb]);
@@ -523,19 +595,7 @@ __global__ __launch_bounds__(64 * (4 + kPcProducers), 1) void pc_kernel(KArgs p)
         produce(std::integral_constant<int, PS::NP >= 3 ? 2 : 0>{});
       wait_vm<0>();
     } else {
-      const int qd = wave;  // the weight quad this wave computes and copies
-      const int t0 = 16 * nb + 4 * qd;  // quads past the last tile read quad 0
-      const size_t qb = (size_t)e * (ntiles / 4) + (t0 < ntiles ? t0 / 4 : 0);
-      const uint8_t *wsrc = p.wp + qb * quad_bytes + (size_t)lane * 16;
-      const uint32_t *wssrc = p.wsp + qb * quad_dwords + lane;
-      auto issue_b = [&](int st, int i) __attribute__((always_inline)) {
-        const int sr = min(st, S - 1);
-        uint8_t *sw = lds + PS::B_BASE + (st % NB) * PS::B_STAGE;
-        if (i < 4)
-          copy16_to_lds(wsrc + (size_t)sr * 4096 + i * 1024, sw + (4 * qd + i) * 1024);
-        else
-          copy4_to_lds(wssrc + (size_t)sr * 64, sw + PS::OFF_BS + qd * 256);
-      };
+      const int t0 = 16 * nb + 4 * qd;
       auto read_a = [&](const uint8_t *st, int m) __attribute__((always_inline)) {
         v8i a;
         const uint8_t *base = st + m * 16 * ROWB;
@@ -552,10 +612,21 @@ __global__ __launch_bounds__(64 * (4 + kPcProducers), 1) void pc_kernel(KArgs p)
       auto read_sa = [&](const uint8_t *st, int m) __attribute__((always_inline)) {
         return (int)st[PS::OFF_AS + 4 * (16 * m + r16) + g];
       };
+      if (!XITEM) {
+        cw = w;
+        cs = 0;
+        cqb = quad_of(w);
+        rslot = cslot;
 #pragma unroll
-      for (int st = 0; st < NB - 1; ++st)
+        for (int st = 0; st < NB - 1; ++st) {
 #pragma unroll
-        for (int i = 0; i < PS::CB; ++i) issue_b(st, i);
+          for (int i = 0; i < PS::CB; ++i) issue_next(i);
+          advance();
+        }
+      }
+      // step 0's copies were issued NB - 1 steps ago (with XITEM: in the last
+      // steps of the previous item, or before the first; the previous
+      // epilogue's stores, issued after them, also drain here)
       wait_vm<(NB - 2) * PS::CB>();  // step 0 has landed
       barrier_keep_copies();
 
@@ -565,8 +636,8 @@ __global__ __launch_bounds__(64 * (4 + kPcProducers), 1) void pc_kernel(KArgs p)
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[m][q] = v4f{0.f, 0.f, 0.f, 0.f};
       // the weight fragments and scale dword of K step st
-      auto read_b = [&](int st, v8i (&bb)[4], int &sbb) __attribute__((always_inline)) {
-        const uint8_t *sw = lds + PS::B_BASE + (st % NB) * PS::B_STAGE;
+      auto read_b = [&](int slot, v8i (&bb)[4], int &sbb) __attribute__((always_inline)) {
+        const uint8_t *sw = lds + PS::B_BASE + slot * PS::B_STAGE;
         sbb = *reinterpret_cast<const int *>(sw + PS::OFF_BS + qd * 256 + lane * 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -579,13 +650,14 @@ __global__ __launch_bounds__(64 * (4 + kPcProducers), 1) void pc_kernel(KArgs p)
         const uint8_t *st = lds + (s % NA) * PS::A_STAGE;
         int sb;
         v8i b[4];
-        read_b(s, b, sb);
+        read_b(rslot, b, sb);
+        rslot = rslot + 1 == NB ? 0 : rslot + 1;
         v8i acur = read_a(st, 0);
         int sacur = read_sa(st, 0);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
 #pragma unroll
-          for (int i = m * PS::CB / MT; i < (m + 1) * PS::CB / MT; ++i) issue_b(s + NB - 1, i);
+          for (int i = m * PS::CB / MT; i < (m + 1) * PS::CB / MT; ++i) issue_next(i);
           v8i anext = acur;
           int sanext = sacur;
           if (m + 1 < MT) {
@@ -600,13 +672,17 @@ __global__ __launch_bounds__(64 * (4 + kPcProducers), 1) void pc_kernel(KArgs p)
           sacur = sanext;
         }
         __builtin_amdgcn_sched_barrier(0);
+        advance();
         wait_vm<(NB - 2) * PS::CB>();  // step s+1's weights have landed
         barrier_keep_copies();
       }
-      wait_vm<0>();
+      // without XITEM the re-reads past the last step land before the next
+      // item's first copies reuse their slots
+      if (!XITEM) wait_vm<0>();
       if (t0 < ntiles) store_item<F, FMT, MT, 4, SECOND>(p, acc, 0, t0, 0, row0, nrows, g, r16, a2row);
     }
   }
+  wait_vm<0>();  // no copy into this workgroup's LDS outlives it
 }
 
 template <int RS, int QPW, bool SECOND>
