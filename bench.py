@@ -17,10 +17,13 @@ captured per logits set; `ms_per_step_graph`, slower than eager launches on
 this stack), and eager launches with HIP events the library records around
 every kernel (per-kernel times; an event record costs a few microseconds, so
 this pass is not used for the step time).  The roofline
-entry is for the dominant kernel (GEMM1) against HBM bandwidth, with its
-algorithmic bytes per launch: touched experts x gate/up weight bytes (codes
-+ E8M0 scales) + the quantised token rows read + the requantised rows
-written.
+entry is for the dominant kernel (GEMM1), against whichever ceiling leaves
+it less time: HBM bandwidth with its algorithmic bytes per launch (touched
+experts x gate/up weight bytes, codes + E8M0 scales, + the quantised token
+rows read + the requantised rows written; the decode sizes), or the dense
+MFMA peak of its operand formats with its algorithmic FLOPs (4 T top_k H I;
+the large shards at prefill sizes).  layer_mfma_frac is the whole layer's
+6 T top_k H I FLOPs per step against that peak.
 
 cpu_baseline: the CPU oracle (test infrastructure, single-threaded C)
 timed on a bounded sample of the same workload: routing, sort and
@@ -41,6 +44,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+# MI355X dense matrix peaks, TFLOP/s: MXFP8 x MXFP4 runs at the FP8 rate, MXFP4 x MXFP4 at FP4's
+MFMA_PEAK_TFLOPS = {0: 5000.0, 1: 10100.0}
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "quantized_moe_expert_softmax_amd", "csrc")
 # sources that decide the decode GEMM1's memory traffic: its kernel, the weight layout
@@ -131,6 +136,34 @@ def gemm1_bytes(layer, U, T, top_k, act):
     a1 = (H if act == 0 else H // 2) + H // 32
     a2 = (I if act == 0 else I // 2) + I // 32
     return U * (I * H + 2 * I * H // 32) + T * a1 + T * top_k * a2
+
+
+def gemm1_flops(layer, T, top_k):
+    # every assignment row times the expert's 2I gate/up rows over K = H
+    return 2.0 * T * top_k * layer.H * 2 * layer.I
+
+
+def roofline_entry(layer, U, T, top_k, act, g1_ms):
+    """Roofline of GEMM1 (the dominant kernel): its algorithmic bytes against
+    HBM and its algorithmic FLOPs against the dense MFMA peak of its operand
+    formats; `bound` is the ceiling that leaves less time, `achieved` the
+    launch's rate against it (the other ceiling's fraction is kept beside)."""
+    b = gemm1_bytes(layer, U, T, top_k, act)
+    f = gemm1_flops(layer, T, top_k)
+    t = g1_ms * 1e-3
+    gbs, tfs = b / t / 1e9, f / t / 1e12
+    pk = MFMA_PEAK_TFLOPS[act]
+    hbm_bound = b / (HBM_PEAK_GBS * 1e9) >= f / (pk * 1e12)
+    e = {"bound": "hbm" if hbm_bound else "mfma", "kernel": "gemm1",
+         "achieved": round(gbs if hbm_bound else tfs, 1),
+         "peak": HBM_PEAK_GBS if hbm_bound else pk,
+         "unit": "GB/s" if hbm_bound else "TFLOP/s",
+         "frac": round((gbs / HBM_PEAK_GBS) if hbm_bound else (tfs / pk), 4)}
+    if hbm_bound:
+        e["mfma_frac"] = round(tfs / pk, 4)
+    else:
+        e["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+    return e, b
 
 
 def layer_weight_bytes(layer, U):
@@ -276,7 +309,7 @@ def main():
     ncalls = max(r["ncalls"], 1)
     g1_ms = r["kern"]["gemm1"] / ncalls
     U_mean = r["U"]
-    g1_bytes = gemm1_bytes(layer, U_mean, T, wl.top_k, act)
+    roof, g1_bytes = roofline_entry(layer, U_mean, T, wl.top_k, act, g1_ms)
     achieved = g1_bytes / (g1_ms * 1e-3) / 1e9
     kernels_us = {k: round(v / ncalls * 1e3, 2) for k, v in r["kern"].items()}
     log("T=%d: %.1f us/step (eager), %.1f graph, %.0f tokens/s, gemm1 %.1f us (%.0f GB/s), "
@@ -334,11 +367,14 @@ def main():
             ("" if combine == 0 else " combine=" + args.combine) +
             (" prequant" if args.prequant else "")),
             "global_batch": T, "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "kernel": "gemm1", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else int(traffic),
-                     "traffic_source": traffic_src, "bytes_per_launch": int(g1_bytes),
-                     "avg_launch_us": round(g1_ms * 1e3, 2)},
+        "roofline": dict(roof, **{
+            "traffic": None if traffic is None else int(traffic),
+            "traffic_source": traffic_src, "bytes_per_launch": int(g1_bytes),
+            "flops_per_launch": gemm1_flops(layer, T, wl.top_k),
+            "avg_launch_us": round(g1_ms * 1e3, 2)}),
+        # the whole layer's 6 T k H I algorithmic FLOPs per step against the dense MFMA peak
+        "layer_mfma_frac": round(6.0 * T * wl.top_k * wl.H * wl.I / (ms_step * 1e-3) / 1e12 /
+                                 MFMA_PEAK_TFLOPS[act], 4),
         "kernels_us": kernels_us,
         "sweep": sweep,
         "cpu_baseline": cpu,
