@@ -123,3 +123,36 @@ def test_fused_plan(T, H, I, E, k, act):
     torch.cuda.synchronize()
     from tests.gpu_util import bf16_host_bits
     assert np.array_equal(bf16_host_bits(y2), y)
+
+
+# Tiled plans with more items than workgroups (one per CU, 256) and K of 1 or 2
+# steps of 128: a consumer wave's weight copies run NB - 1 = 3 steps ahead,
+# so they reach into the next item and the one after it (MT <= 8), or
+# re-read the last step until the next item issues its own (MT = 10).  The
+# intermediate size is 128 or 512: a row's output depends on I/32 requantised
+# A2 blocks, and where h's block maximum lies on a power of two the kernel's
+# SwiGLU (hardware exp and reciprocal) and the oracle's can pick neighbouring
+# E8M0 scales for one block; at I = 256 (8 blocks) one such block moved a row
+# of the (0, 96, 8192, 128, 256) case by 3.2%, the same bits before and after
+# the cross-item copies, so the per-row bound is checked on shapes where one
+# block weighs less.
+MANY_ITEMS = [
+    (0, 32, 4096, 256, 128, 64, 4),    # MT 2: ~512 GEMM1 items, S = 2 / 1
+    (0, 96, 4096, 128, 512, 64, 4),    # MT 6: ~768 GEMM1 items, S = 1 / 4
+    (0, 160, 16384, 128, 128, 64, 4),  # MT 10: ~450 items, per-item prologue
+    (1, 64, 8192, 256, 128, 64, 4),    # MXFP4 MT 4: ~512 items
+    (1, 128, 16384, 128, 128, 64, 4),  # MXFP4 MT 8: ~512 items, S = 1 / 1
+]
+
+
+@pytest.mark.parametrize("act,rows,T,H,I,E,k", MANY_ITEMS)
+def test_tiled_many_items_per_workgroup(act, rows, T, H, I, E, k):
+    w, x, lg = _small(T, H, I, E, k, seed=rows + T)
+    layer = _layer(*w)
+    moe.moe_set_plans(layer, [dict(act=act, top_k=k, t_max=T, variant=moe.MOE_PLAN_TILED,
+                                   rows=rows)])
+    ref, a2c, a2s = oracle.forward(x, lg, *w, k, act, want_a2=True)
+    y, ws = _run(layer, x, lg, k, act)
+    assert_output_close(y, ref, "tiled rows=%d T=%d H=%d I=%d act=%d" % (rows, T, H, I, act))
+    mism, smism = _check_workspace(layer, ws, x, lg, k, act, (a2c, a2s))
+    assert mism < 1e-2 and smism < 1e-2, (mism, smism)
