@@ -405,12 +405,15 @@ __global__ __launch_bounds__(64 * RS * 4 / QPW, 1) void tiled_kernel(KArgs p) {
 // Producer/consumer form of the tiled kernel.  The copy waits count a wave's
 // own copies in issue order, so in the form above, where every wave copies
 // both operands, a step's weights (HBM) and activations (L2) share one
-// deadline.  Here waves 0-3 each copy only their own weight quad (four 1 KiB
-// fragments and its scale dword) into a ring of NB weight stages, NB - 1
-// steps ahead, and wait only for those; waves 4.. (the producers) copy the
-// activation tile and its scales into the NA-stage activation ring, each an
-// equal share, and wait only for those.  Copies past the last K step re-read the last step (cache hits)
-// into a ring slot no later step reads.  One barrier per step.
+// deadline.  Here the consumer waves (RS per weight quad: wave c computes
+// quad c % 4 on m-tiles [(c / 4) MT / RS, +MT / RS)) copy only their quad's
+// four 1 KiB fragments (a share each) and its scale dword into a ring of NB
+// weight stages, NB - 1 steps ahead, and wait only for those; the producer
+// waves after them copy the activation tile and its scales into the
+// NA-stage activation ring, an equal share each, and wait only for those.
+// The barrier of every step makes each wave's copies visible to the others.
+// Copies past the last K step re-read a valid step (cache hits) into a ring
+// slot no later step reads.
 // ---------------------------------------------------------------------------
 // Producer waves and ring depths: two producer waves (each with its own
 // copy count, so the activation ring can be four stages deep within the
@@ -420,11 +423,19 @@ __global__ __launch_bounds__(64 * RS * 4 / QPW, 1) void tiled_kernel(KArgs p) {
 // T = 16384) and equal on the 5120 x 640 one; three producers with five
 // activation stages, and passing the step barrier before the last m-tile's
 // MFMAs, measured no faster.
-constexpr int kPcProducers = 2, kPcActStages = 4, kPcWStages = 4;
+// Consumer waves: two per weight quad (kPcRowSplit = 2), each with half of
+// the item's m-tiles, so two MFMA waves share a SIMD and one issues while
+// the other waits on LDS or a copy; measured 3% faster per call at A4W4
+// T = 16384 and 2.5% on the 5120 x 640 shard than one wave per quad, equal
+// on the 7168 x 3072 layer at A8W4 T = 4096 and 8192.
+constexpr int kPcProducers = 2, kPcActStages = 4, kPcWStages = 4, kPcRowSplit = 2;
 template <int FMT, int MT>
 struct PcShape {
   static constexpr int NP = kPcProducers;             // producer waves
-  static constexpr int NWAVES = 4 + NP;
+  static constexpr int RS = kPcRowSplit;              // consumer waves per weight quad
+  static constexpr int NC = 4 * RS;                   // consumer waves
+  static constexpr int NWAVES = NC + NP;
+  static constexpr int MTW = MT / RS;                 // m-tiles per consumer wave
   static constexpr int BM = 16 * MT;
   static constexpr int ROWB = FMT == 0 ? 128 : 64;    // activation bytes per row per K step
   static constexpr int CH = ROWB / 16;
@@ -435,7 +446,7 @@ struct PcShape {
   static constexpr int CA = (CA_ALL + NP - 1) / NP;   // per producer wave (the last repeats)
   static constexpr int OFF_AS = A_BYTES;              // [BM] scale dwords
   static constexpr int A_STAGE = A_BYTES + 1024;
-  static constexpr int CB = 5;                        // consumer copies per step
+  static constexpr int CB = 4 / RS + 1;               // consumer copies per step (fragments, scale)
   static constexpr int OFF_BS = 4 * 4096;
   static constexpr int B_STAGE = OFF_BS + 4 * 256;
   static constexpr int NA = kPcActStages;
@@ -444,6 +455,7 @@ struct PcShape {
   static constexpr int B_BASE = NA * A_STAGE;
   static constexpr int LDS = B_BASE + NB * B_STAGE;
   static_assert(A_BYTES % 1024 == 0, "activation tile must fill whole copies");
+  static_assert(MT % RS == 0 && 4 % RS == 0, "even row split");
   static_assert(BM <= 256, "scale slots");
   static_assert(NB >= 3, "weight ring");
   static_assert((NA - 1) * CA < 64 && (NB - 1) * CB < 64, "vmcnt range");
@@ -451,14 +463,14 @@ struct PcShape {
 };
 
 template <int FMT, int MT, bool SECOND>
-__global__ __launch_bounds__(64 * (4 + kPcProducers), 1) void pc_kernel(KArgs p) {
+__global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_kernel(KArgs p) {
   using F = typename ActFmt<FMT>::F;
   using PS = PcShape<FMT, MT>;
   constexpr int NA = PS::NA, NB = PS::NB, BM = PS::BM, ROWB = PS::ROWB, CH = PS::CH;
   __shared__ __attribute__((aligned(16))) uint8_t lds[PS::LDS];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool producer = uniform(wave) >= 4;
+  const bool producer = uniform(wave) >= PS::NC;
   const int g = lane >> 4, r16 = lane & 15;
   const int K = SECOND ? p.I : p.H;
   const int S = K / 128;
@@ -487,9 +499,13 @@ __global__ __launch_bounds__(64 * (4 + kPcProducers), 1) void pc_kernel(KArgs p)
   // valid step into slots no step reads.  It measured 1.5% faster per call
   // (A4W4, T = 16384, MT = 8); at MT = 10 its extra live registers spill, so
   // there each item issues its own first NB - 1 steps and its copies past
-  // the last step re-read that step.
-  constexpr bool XITEM = MT <= 8;
+  // the last step re-read that step.  (With two consumer waves per quad a
+  // wave holds at most 5 m-tiles, and the cross-item stream runs at every
+  // tile height.)
+  constexpr bool XITEM = MT / kPcRowSplit <= 8;
   const int qd = uniform(wave & 3);  // the weight quad a consumer wave computes and copies
+  const int rh = PS::RS == 1 ? 0 : uniform(wave >> 2);  // its share of the copies and m-tiles
+  constexpr int MTW = PS::MTW;
   const int total_i = (int)total;      // items fit 32 bits (m-blocks x n-blocks)
   auto quad_of = [&](int wi) __attribute__((always_inline)) {
     const int ei = uniform(p.mbexp[wi / NBLK]);
@@ -507,10 +523,13 @@ __global__ __launch_bounds__(64 * (4 + kPcProducers), 1) void pc_kernel(KArgs p)
     uint8_t *sw = lds + PS::B_BASE + cslot * PS::B_STAGE;
     // a wave-uniform base plus a 32-bit lane offset (the scalar-base form of
     // the copy: no 64-bit address per lane)
-    if (i < 4)
+    // the 4 / RS fragments of this wave's share, then the quad's scale
+    // dword (each wave of a quad copies it: same bytes, same LDS address)
+    const int f = rh * (4 / PS::RS) + i;
+    if (i < 4 / PS::RS)
       copy16_to_lds(p.wp + ((size_t)cqb * quad_bytes + (size_t)sr * 4096) +
-                        (uint32_t)(i * 1024 + lane * 16),
-                    sw + (4 * qd + i) * 1024);
+                        (uint32_t)(f * 1024 + lane * 16),
+                    sw + (4 * qd + f) * 1024);
     else
       copy4_to_lds(reinterpret_cast<const uint8_t *>(p.wsp + (size_t)cqb * quad_dwords +
                                                      (size_t)sr * 64) +
@@ -587,9 +606,9 @@ __global__ __launch_bounds__(64 * (4 + kPcProducers), 1) void pc_kernel(KArgs p)
           barrier_keep_copies();
         }
       };
-      if (PS::NP == 1 || wave == 4)
+      if (PS::NP == 1 || wave == PS::NC)
         produce(std::integral_constant<int, 0>{});
-      else if (PS::NP == 2 || wave == 5)
+      else if (PS::NP == 2 || wave == PS::NC + 1)
         produce(std::integral_constant<int, PS::NP >= 2 ? 1 : 0>{});
       else
         produce(std::integral_constant<int, PS::NP >= 3 ? 2 : 0>{});
@@ -630,56 +649,65 @@ __global__ __launch_bounds__(64 * (4 + kPcProducers), 1) void pc_kernel(KArgs p)
       wait_vm<(NB - 2) * PS::CB>();  // step 0 has landed
       barrier_keep_copies();
 
-      v4f acc[MT][4];
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[m][q] = v4f{0.f, 0.f, 0.f, 0.f};
-      // the weight fragments and scale dword of K step st
-      auto read_b = [&](int slot, v8i (&bb)[4], int &sbb) __attribute__((always_inline)) {
-        const uint8_t *sw = lds + PS::B_BASE + slot * PS::B_STAGE;
-        sbb = *reinterpret_cast<const int *>(sw + PS::OFF_BS + qd * 256 + lane * 4);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 v = *reinterpret_cast<const u32x4 *>(sw + qd * 4096 + q * 1024 + lane * 16);
-          bb[q][0] = (int)v[0]; bb[q][1] = (int)v[1]; bb[q][2] = (int)v[2]; bb[q][3] = (int)v[3];
-          bb[q][4] = 0; bb[q][5] = 0; bb[q][6] = 0; bb[q][7] = 0;
-        }
-      };
-      for (int s = 0; s < S; ++s) {
-        const uint8_t *st = lds + (s % NA) * PS::A_STAGE;
-        int sb;
-        v8i b[4];
-        read_b(rslot, b, sb);
-        rslot = rslot + 1 == NB ? 0 : rslot + 1;
-        v8i acur = read_a(st, 0);
-        int sacur = read_sa(st, 0);
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-#pragma unroll
-          for (int i = m * PS::CB / MT; i < (m + 1) * PS::CB / MT; ++i) issue_next(i);
-          v8i anext = acur;
-          int sanext = sacur;
-          if (m + 1 < MT) {
-            anext = read_a(st, m + 1);
-            sanext = read_sa(st, m + 1);
+      // the MFMA loop and epilogue of this wave's m-tiles, compiled once per
+      // row half so that the m-tile offset is a constant in every address
+      auto consume = [&](auto rhc) __attribute__((always_inline)) {
+        constexpr int MW0 = decltype(rhc)::value * MTW;
+        v4f acc[MTW][4];
+  #pragma unroll
+        for (int m = 0; m < MTW; ++m)
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) acc[m][q] = v4f{0.f, 0.f, 0.f, 0.f};
+        // the weight fragments and scale dword of K step st
+        auto read_b = [&](int slot, v8i (&bb)[4], int &sbb) __attribute__((always_inline)) {
+          const uint8_t *sw = lds + PS::B_BASE + slot * PS::B_STAGE;
+          sbb = *reinterpret_cast<const int *>(sw + PS::OFF_BS + qd * 256 + lane * 4);
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(sw + qd * 4096 + q * 1024 + lane * 16);
+            bb[q][0] = (int)v[0]; bb[q][1] = (int)v[1]; bb[q][2] = (int)v[2]; bb[q][3] = (int)v[3];
+            bb[q][4] = 0; bb[q][5] = 0; bb[q][6] = 0; bb[q][7] = 0;
           }
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[m][q] = mfma_q<FMT>(q, acur, b[q], acc[m][q], sacur, sb);
+        };
+        for (int s = 0; s < S; ++s) {
+          const uint8_t *st = lds + (s % NA) * PS::A_STAGE;
+          int sb;
+          v8i b[4];
+          read_b(rslot, b, sb);
+          rslot = rslot + 1 == NB ? 0 : rslot + 1;
+          v8i acur = read_a(st, MW0);
+          int sacur = read_sa(st, MW0);
+  #pragma unroll
+          for (int m = 0; m < MTW; ++m) {
+  #pragma unroll
+            for (int i = m * PS::CB / MTW; i < (m + 1) * PS::CB / MTW; ++i) issue_next(i);
+            v8i anext = acur;
+            int sanext = sacur;
+            if (m + 1 < MTW) {
+              anext = read_a(st, MW0 + m + 1);
+              sanext = read_sa(st, MW0 + m + 1);
+            }
+  #pragma unroll
+            for (int q = 0; q < 4; ++q)
+              acc[m][q] = mfma_q<FMT>(q, acur, b[q], acc[m][q], sacur, sb);
+            __builtin_amdgcn_sched_barrier(0);
+            acur = anext;
+            sacur = sanext;
+          }
           __builtin_amdgcn_sched_barrier(0);
-          acur = anext;
-          sacur = sanext;
+          advance();
+          wait_vm<(NB - 2) * PS::CB>();  // step s+1's weights have landed
+          barrier_keep_copies();
         }
-        __builtin_amdgcn_sched_barrier(0);
-        advance();
-        wait_vm<(NB - 2) * PS::CB>();  // step s+1's weights have landed
-        barrier_keep_copies();
-      }
-      // without XITEM the re-reads past the last step land before the next
-      // item's first copies reuse their slots
-      if (!XITEM) wait_vm<0>();
-      if (t0 < ntiles) store_item<F, FMT, MT, 4, SECOND>(p, acc, 0, t0, 0, row0, nrows, g, r16, a2row);
+        // without XITEM the re-reads past the last step land before the next
+        // item's first copies reuse their slots
+        if (!XITEM) wait_vm<0>();
+        if (t0 < ntiles) store_item<F, FMT, MTW, 4, SECOND>(p, acc, 0, t0, MW0, row0, nrows, g, r16, a2row);
+      };
+      if (PS::RS == 1 || rh == 0)
+        consume(std::integral_constant<int, 0>{});
+      else
+        consume(std::integral_constant<int, PS::RS >= 2 ? 1 : 0>{});
     }
   }
   wait_vm<0>();  // no copy into this workgroup's LDS outlives it
