@@ -22,6 +22,9 @@ from . import (MOE_ACT_MXFP8_E4M3, MOE_PLAN_FUSED, MOE_PLAN_STREAM, MOE_PLAN_TIL
                alloc_workspace, moe_forward, moe_get_plan, moe_set_plans)
 
 
+_NAMES = {MOE_PLAN_STREAM: "stream", MOE_PLAN_TILED: "tiled", MOE_PLAN_FUSED: "fused"}
+
+
 def candidates(act: int):
     rows = (32, 64, 96, 128, 160) if act == MOE_ACT_MXFP8_E4M3 else (64, 128)
     return [(MOE_PLAN_STREAM, 16), (MOE_PLAN_FUSED, 16)] + [(MOE_PLAN_TILED, r) for r in rows]
@@ -60,7 +63,7 @@ def tune(layer, inputs, top_k: int, act: int, steps: int = 10, warmup: int = 3,
         pick = best if times[best] < (1.0 - margin) * base else (builtin["variant"], builtin["rows"])
         table.append(dict(act=act, top_k=top_k, t_max=T, variant=pick[0], rows=pick[1]))
         report[T] = {"builtin": [builtin["variant"], builtin["rows"]], "pick": list(pick),
-                     "us": {"%s/%d" % ("tiled" if v else "stream", r): round(t * 1e6, 1)
+                     "us": {"%s/%d" % (_NAMES[v], r): round(t * 1e6, 1)
                             for (v, r), t in times.items()}}
         if log:
             log("T=%d builtin=%s pick=%s %s" % (T, report[T]["builtin"], report[T]["pick"],
