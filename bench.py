@@ -11,12 +11,15 @@ workload (T=1, 2, 8, 32) are timed too and reported under "sweep".
 Between steps the router logits rotate over 8 pre-drawn sets, so successive
 calls touch different experts (the touched weights of one call are larger
 than the MI355X last-level cache at T >= 8, and rotate through ~1.7 GB at
-T = 1).  Each token count is timed three ways over the same calls: eager
+T = 1).  Each token count is timed in passes over the same calls: eager
 launches (this is `value` and `ms_per_step`), HIP-graph replay (one graph
 captured per logits set; `ms_per_step_graph`, slower than eager launches on
 this stack), and eager launches with HIP events the library records around
 every kernel (per-kernel times; an event record costs a few microseconds, so
-this pass is not used for the step time).  The roofline
+this pass is not used for the step time).  A fourth pass times each call on
+its own (HIP events on the launch stream) after a 512 MiB device read that
+evicts the last-level cache: `us_per_call_flushed` gives its p10, median and
+p90.  The roofline
 entry is for the dominant kernel (GEMM1), against whichever ceiling leaves
 it less time: HBM bandwidth with its algorithmic bytes per launch (touched
 experts x gate/up weight bytes, codes + E8M0 scales, + the quantised token
@@ -235,7 +238,28 @@ def time_T(moe, torch, layer, wl, T, act, steps, warmup, combine=0, prequant=Fal
     kern, ncalls = moe.moe_profile_read(layer)
     moe.moe_profile_enable(layer, False)
     U = sum(Us[i % 8] for i in range(ncalls)) / max(ncalls, 1)
-    return {"dt_eager": dt_eager, "dt_graph": dt_graph, "kern": kern, "ncalls": ncalls, "U": U}
+
+    # per-call times with a cold last-level cache: before each call (outside its
+    # events) a 512 MiB device read evicts the 256 MB MALL (a read leaves no dirty
+    # lines to be written back during the call); HIP events on the launch stream
+    # bracket the call alone
+    flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        flush.sum()
+        ev[i][0].record(stream)
+        call(lgs[i % 8], stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    del flush
+
+    def pct(q):
+        return round(per_call[min(len(per_call) - 1, int(q * len(per_call)))], 2)
+    flushed = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}
+    return {"dt_eager": dt_eager, "dt_graph": dt_graph, "kern": kern, "ncalls": ncalls, "U": U,
+            "flushed": flushed}
 
 
 def cpu_baseline(moe, torch, layer_dev_weights, wl, T, act, rows):
@@ -323,6 +347,7 @@ def main():
         return {
             "us_per_call": round(d * 1e6, 2),
             "us_per_call_graph": round(r["dt_graph"] * 1e6 / args.steps, 2),
+            "us_per_call_flushed": r["flushed"],
             "tokens_per_s": round(t / d, 1),
             "touched_experts": round(r["U"], 1),
             "layer_weight_GBps": round(layer_weight_bytes(layer, r["U"]) / d / 1e9, 1),
@@ -357,6 +382,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "ms_per_step_graph": round(r["dt_graph"] * 1e3 / args.steps, 4),
+        # per-call HIP-event times after a 512 MiB cache-evicting read (microseconds)
+        "us_per_call_flushed": r["flushed"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -237,6 +237,7 @@ moe_status moe_workspace_offsets(moe_layer_t L, int T, int top_k, moe_act_dtype 
   return MOE_OK;
 }
 
+extern "C++" {  // internal helpers: C++ linkage inside the C-ABI block
 namespace {
 
 GemmPlan plan_for(const moe_layer *L, int T, int top_k, int act) {
@@ -248,6 +249,7 @@ GemmPlan plan_for(const moe_layer *L, int T, int top_k, int act) {
 }
 
 }  // namespace
+}  // extern "C++"
 
 moe_status moe_set_plans(moe_layer_t L, const moe_plan *plans, int n) {
   if (!L) return fail(MOE_ERR_INVALID_ARG, "null layer handle");
