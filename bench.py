@@ -51,8 +51,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {0: 5000.0, 1: 10100.0}
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "quantized_moe_expert_softmax_amd", "csrc")
-# sources that decide the decode GEMM1's memory traffic: its kernel, the weight layout
-GEMM_SOURCES = ("gemm_common.h", "gemm_stream.hip", "prepack.hip", "mx_device.h", "internal.h")
+# sources that decide GEMM1's memory traffic: its kernels (stream and tiled), the weight layout
+GEMM_SOURCES = ("gemm_common.h", "gemm_stream.hip", "gemm_tiled.hip", "prepack.hip", "mx_device.h",
+                "internal.h")
 
 
 def log(*a):
