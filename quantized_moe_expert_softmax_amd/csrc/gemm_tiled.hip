@@ -8,19 +8,19 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // Tiled variant (prefill): a work item is (expert e, 256 weight rows, BM =
-// 16*MT token rows).  Wave w owns 64 weight rows (GEMM1: one gate/up unit)
-// and MT x 4 accumulator tiles, so every weight fragment is read from HBM
-// once per item and feeds MT MFMAs; the activation tile of a K step is
-// shared by the four waves.  Every operand of a K step -- the BM activation
-// rows (16-byte chunks XOR-swizzled by row), their E8M0 scales, each wave's
-// four 1 KiB weight fragments and their scale dword -- is copied from
-// global memory straight into LDS with global_load_lds (no register
-// staging), NS steps deep, the copies of a later step interleaved with the
-// MFMAs of the current one; the waits count those copies exactly (they are
-// the only vector-memory instructions in the loop and issue in program
-// order).  BM is picked per call so that most experts fit one m-block (each
-// weight panel is then read once).  The logical workgroup index is remapped
-// so consecutive items share an XCD and its L2.
+// 16*MT token rows).  Each 64-row weight quad (GEMM1: one gate/up unit) is
+// computed by its MFMA waves on all the item's rows, so every weight
+// fragment is read from HBM once per item and feeds MT MFMAs; the activation
+// tile of a K step is shared by all waves.  Every operand of a K step -- the
+// BM activation rows (16-byte chunks XOR-swizzled by row), their E8M0
+// scales, each quad's four 1 KiB weight fragments and their scale dword --
+// is copied from global memory straight into LDS with global_load_lds (no
+// register staging), several steps deep, the copies of a later step
+// interleaved with the MFMAs of the current one; the waits count those
+// copies exactly (they are the only vector-memory instructions in the loop
+// and issue in program order).  BM is picked per call so that most experts
+// fit one m-block (each weight panel is then read once).  The logical
+// workgroup index is remapped so consecutive items share an XCD and its L2.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 typedef __attribute__((address_space(1))) void *glb_ptr_t;
@@ -47,62 +47,6 @@ __device__ __forceinline__ void barrier_keep_copies() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
   __builtin_amdgcn_s_barrier();
 }
-// LDS of the tiled kernel: a ring of NA activation stages (the BM rows of
-// one K step and their scale dwords) and a ring of NB = 4 weight stages (the
-// four weight quads' 1 KiB fragments and scale dwords).  Weights stream from
-// HBM and are fetched NB - 1 steps ahead, activations come from L2 and are
-// fetched NA - 1 steps ahead.  The waits count copy groups in order, so NA
-// also sets how many groups stay in flight across a step boundary (NA - 2):
-// GEMM1 takes NA = 4 (weights and activations of a step in one group, two
-// groups in flight), GEMM2 NA = 3 (weights one step ahead of activations,
-// one group in flight); on the 7168 x 3072 and 5120 x 640 layers these
-// measured 1-4% faster than the other choice for each GEMM.  (Weight rings
-// deeper than 4 fit in 160 KiB but measured slower.)
-//
-// Waves tile the item's BM x 256 outputs as RS row splits x (4 / QPW) quad
-// groups: a wave owns MT / RS m-tiles and QPW weight quads.  RS = 1, QPW = 1
-// gives four waves that each read the whole activation tile; RS = QPW = 2
-// gives four waves that each read half of it and two quads (fewer LDS bytes
-// per MFMA); RS = 2, QPW = 1 gives eight waves, two per SIMD.  The copies of
-// a step are spread over all waves independently of that split; where they
-// do not divide evenly a wave repeats a copy another wave makes (same bytes
-// to the same LDS address), so every wave issues the same number and one
-// wait count fits all.
-template <int FMT, int MT, int RS, int QPW, int NA_>
-struct TileShape {
-  static constexpr int NWV = RS * 4 / QPW;           // waves per workgroup
-  static constexpr int MTW = MT / RS;                // m-tiles per wave
-  static constexpr int BM = 16 * MT;
-  static constexpr int ROWB = FMT == 0 ? 128 : 64;   // activation bytes per row per K step
-  static constexpr int CH = ROWB / 16;               // 16-byte chunks per row
-  static constexpr int A_BYTES = BM * ROWB;
-  static constexpr int A_CHUNKS = A_BYTES / 1024;    // 1 KiB copies per stage
-  static constexpr int A_COPIES = (A_CHUNKS + NWV - 1) / NWV;  // per wave
-  static constexpr int RPW = (BM + NWV - 1) / NWV;   // scale rows copied per wave
-  static constexpr int FPW = 16 / NWV;              // weight fragments copied per wave
-  static constexpr int CA = A_COPIES + 1;            // activation copies per wave per step
-  static constexpr int CB = FPW + 1;                 // weight copies per wave per step
-  static constexpr int C = CA + CB;
-  static constexpr int OFF_AS = A_BYTES;             // [NWV waves][64 slots] dwords
-  static constexpr int A_STAGE = OFF_AS + NWV * 256;
-  static constexpr int OFF_BS = 4 * 4096;            // after [4 quads][4 tiles] fragments
-  static constexpr int B_STAGE = OFF_BS + 4 * 256;   // + [4 quads][64 lanes] scale dwords
-  static constexpr int NA = NA_;
-  static constexpr int NB_FIT = (160 * 1024 - NA * A_STAGE) / B_STAGE;
-  static constexpr int NB = NB_FIT < 4 ? NB_FIT : 4;
-  static constexpr int D = NB - NA;                  // weight lead over activations, in steps
-  static constexpr int B_BASE = NA * A_STAGE;
-  static constexpr int LDS = B_BASE + NB * B_STAGE;
-  static_assert(MT % RS == 0 && 4 % QPW == 0 && 16 % NWV == 0, "even split");
-  static_assert(A_BYTES % 1024 == 0, "activation tile must fill whole copies");
-  static_assert(RPW <= 64, "scale rows per wave");
-  static_assert(D >= 0, "weights never trail activations");
-  static_assert(LDS <= 160 * 1024, "LDS");
-  static_assert((NA - 1) * CA + (NB - 1) * CB < 64, "vmcnt range");
-  // LDS slot of row r's scale dword
-  static __device__ __forceinline__ int sslot(int r) { return (r / RPW) * 64 + (r % RPW); }
-};
-
 // Epilogue of one weight quad u of a work item (output tiles 4u .. 4u+3 of
 // acc; tile0 the quad's first 16-row weight tile): GEMM1 SwiGLU + requant to
 // the A2 rows, GEMM2 weighted rows to the staging buffer.  A padded row
@@ -159,253 +103,12 @@ __device__ __forceinline__ void store_item(const KArgs &p, const v4f (&acc)[MTW]
   }
 }
 
-template <int FMT, int MT, int RS, int QPW, bool SECOND>
-__global__ __launch_bounds__(64 * RS * 4 / QPW, 1) void tiled_kernel(KArgs p) {
-  using F = typename ActFmt<FMT>::F;
-  using TS = TileShape<FMT, MT, RS, QPW, SECOND ? 3 : 4>;
-  constexpr int NA = TS::NA, NB = TS::NB, D = TS::D, MTW = TS::MTW;
-  constexpr int BM = TS::BM, ROWB = TS::ROWB, CH = TS::CH;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[TS::LDS];
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int qd0 = (wave % (4 / QPW)) * QPW;  // first weight quad of this wave
-  const int mw0 = (wave / (4 / QPW)) * MTW;  // first m-tile of this wave
-  const int g = lane >> 4, r16 = lane & 15;
-  const int K = SECOND ? p.I : p.H;
-  const int S = K / 128;
-  const int ntiles = (SECOND ? p.H : 2 * p.I) / 16;
-  const int NBLK = (ntiles + 15) / 16;  // n-blocks of 256 weight rows
-  const int n_mb = uniform(p.mtoff[p.E]);
-  const long total = (long)n_mb * NBLK;
-  const size_t arow = FMT == 0 ? (size_t)K : (size_t)K / 2;
-  const size_t srow = (size_t)K / 32;
-  const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
-  const size_t quad_bytes = (size_t)S * 4096, quad_dwords = (size_t)S * 64;
-  const uint8_t *__restrict__ A = SECOND ? p.a2c : p.a1c;
-  const uint8_t *__restrict__ As = SECOND ? p.a2s : p.a1s;
-  const int G = gridDim.x;
-  const int L = (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8);
-  // per-lane constant LDS offsets of the swizzled activation fragments
-  const int swz = (FMT == 0) ? (r16 & 7) : (r16 & 3);
-  const int aoff_lo = r16 * ROWB + 16 * (g ^ swz);
-  const int aoff_hi = r16 * ROWB + 16 * ((4 + g) ^ swz);
-
-  for (long w = L; w < total; w += G) {
-    // item w = (global m-block, n-block), n-block minor: consecutive items
-    // (neighbouring CUs of one XCD) share the activation tile through L2
-    const int gmb = (int)(w / NBLK), nb = (int)(w % NBLK);
-    const int e = uniform(p.mbexp[gmb]);
-    const int mb = gmb - uniform(p.mtoff[e]);
-    const int row0 = uniform(p.offsets[e]) + BM * mb;
-    const int nrows = min(BM, uniform(p.offsets[e + 1]) - row0);
-
-    // global sources of this lane's copies (the K-step offset is added later);
-    // activation chunk k of a stage is LDS bytes [1024 k, +1024)
-    const uint8_t *asrc[TS::A_COPIES];
-    int adst[TS::A_COPIES];
-#pragma unroll
-    for (int i = 0; i < TS::A_COPIES; ++i) {
-      const int k = (wave * TS::A_COPIES + i) % TS::A_CHUNKS;
-      const int ci = k * 64 + lane;  // 16-byte LDS chunk this lane fills
-      const int row = ci / CH, slot = ci % CH;
-      const int rr = min(row, nrows - 1);
-      const size_t ridx = SECOND ? (size_t)(row0 + rr) : (size_t)(p.perm[row0 + rr] / p.top_k);
-      asrc[i] = A + ridx * arow + 16 * (slot ^ (row & (CH - 1)));
-      adst[i] = k * 1024;
-    }
-    const uint8_t *ssrc;
-    {
-      const int row = min(wave * TS::RPW + (lane % TS::RPW), BM - 1);
-      const int rr = min(row, nrows - 1);
-      const size_t ridx = SECOND ? (size_t)(row0 + rr) : (size_t)(p.perm[row0 + rr] / p.top_k);
-      ssrc = As + ridx * srow;
-    }
-    // copies: this wave's weight fragments f0 .. f0+FPW-1 of the item's 16
-    // (quad f/4, tile f%4) and the scale dword of quad wave % 4
-    const int f0 = wave * TS::FPW;
-    const int cq = f0 / 4, cs = wave % 4;
-    auto quad_base = [&](int q) __attribute__((always_inline)) {
-      const int t0 = 16 * nb + 4 * q;  // quads past the last tile read quad 0
-      return (size_t)e * (ntiles / 4) + (t0 < ntiles ? t0 / 4 : 0);
-    };
-    const uint8_t *wsrc = p.wp + quad_base(cq) * quad_bytes + (size_t)lane * 16;
-    const uint32_t *wssrc = p.wsp + quad_base(cs) * quad_dwords + lane;
-    static_assert(TS::FPW <= 4, "a wave's fragments lie in one quad");
-
-    // Copy group p = the weight copies of K step p + D (the weights run D
-    // steps further ahead), then the activation copies of step p.  Copies of
-    // a step past the last are issued from one fixed address (every lane
-    // reads the same 16 bytes) into a ring slot no step reads any more, so
-    // every group has C copies and one wait count fits all.  Copies retire
-    // in issue order, so "at most N outstanding" names exactly what landed;
-    // the weight copies (from HBM) go first.
-    const uint8_t *dummy = p.wp + quad_base(cq) * quad_bytes;
-    // weight copy i (0 <= i < CB) of K step sb: this wave's fragments, then
-    // a quad's scale dword (repeated by every wave with the same wave % 4)
-    auto issue_b = [&](int sb, int i) __attribute__((always_inline)) {
-      const bool real = sb < S;
-      uint8_t *sw = lds + TS::B_BASE + (sb % NB) * TS::B_STAGE;
-      if (i < TS::FPW)
-        copy16_to_lds(real ? wsrc + (size_t)sb * 4096 + ((f0 + i) % 4) * 1024 : dummy,
-                      sw + (f0 + i) * 1024);
-      else
-        copy4_to_lds(real ? (const void *)(wssrc + (size_t)sb * 64) : (const void *)dummy,
-                     sw + TS::OFF_BS + cs * 256);
-    };
-    // copy i (0 <= i < C) of group p: the weight copies, the activation
-    // chunks, the activation scale dword
-    auto issue_one = [&](int pg, int i) __attribute__((always_inline)) {
-      if (i < TS::CB) {
-        issue_b(pg + D, i);
-      } else {
-        const int ia = i - TS::CB;
-        const bool real = pg < S;
-        uint8_t *st = lds + (pg % NA) * TS::A_STAGE;
-        if (ia < TS::A_COPIES)
-          copy16_to_lds(real ? asrc[ia] + (size_t)ROWB * pg : dummy, st + adst[ia]);
-        else
-          copy4_to_lds(real ? ssrc + 4 * pg : dummy, st + TS::OFF_AS + wave * 256);
-      }
-    };
-
-    constexpr int NT = 4 * QPW;  // accumulator tiles per m-tile (weight tiles of this wave)
-    v4f acc[MTW][NT];
-#pragma unroll
-    for (int m = 0; m < MTW; ++m)
-#pragma unroll
-      for (int q = 0; q < NT; ++q) acc[m][q] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // activation fragment of this wave's m-tile m
-    auto read_a = [&](const uint8_t *st, int m) __attribute__((always_inline)) {
-      v8i a;
-      const uint8_t *base = st + (mw0 + m) * 16 * ROWB;
-      const u32x4 lo = *reinterpret_cast<const u32x4 *>(base + aoff_lo);
-      a[0] = (int)lo[0]; a[1] = (int)lo[1]; a[2] = (int)lo[2]; a[3] = (int)lo[3];
-      if (FMT == 0) {
-        const u32x4 hi = *reinterpret_cast<const u32x4 *>(base + aoff_hi);
-        a[4] = (int)hi[0]; a[5] = (int)hi[1]; a[6] = (int)hi[2]; a[7] = (int)hi[3];
-      } else {
-        a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
-      }
-      return a;
-    };
-    // the scale operands are read as single bytes, so the MFMA takes the load
-    // result as it is and no VALU op waits on the read inside the sequence
-    auto read_sa = [&](const uint8_t *st, int m) __attribute__((always_inline)) {
-      return (int)st[TS::OFF_AS + 4 * TS::sslot(16 * (mw0 + m) + r16) + g];
-    };
-
-    // prologue: the weight lead (steps 0 .. D-1), then groups 0 .. NA-2
-#pragma unroll
-    for (int sb = 0; sb < D; ++sb)
-#pragma unroll
-      for (int i = 0; i < TS::CB; ++i) issue_b(sb, i);
-#pragma unroll
-    for (int pg = 0; pg < NA - 1; ++pg)
-#pragma unroll
-      for (int i = 0; i < TS::C; ++i) issue_one(pg, i);
-    // step 0 has landed: what may still be in flight is issued after its
-    // activation copies (groups 1 .. NA-2)
-    wait_vm<(NA - 2) * TS::C>();
-    __syncthreads();
-
-    for (int s = 0; s < S; ++s) {
-      // the copies of group s + NA - 1 are spread over the MFMA sequence of
-      // step s, so the wave never stalls on a full memory queue with the
-      // matrix cores idle
-      {  // inactive waves (past the last weight tile) compute on valid data and never store
-        const uint8_t *st = lds + (s % NA) * TS::A_STAGE;
-        const uint8_t *sw = lds + TS::B_BASE + (s % NB) * TS::B_STAGE;
-        v8i b[NT];
-        int sb[QPW];
-#pragma unroll
-        for (int u = 0; u < QPW; ++u)
-          sb[u] = *reinterpret_cast<const int *>(sw + TS::OFF_BS + (qd0 + u) * 256 + lane * 4);
-#pragma unroll
-        for (int q = 0; q < NT; ++q) {
-          const u32x4 v = *reinterpret_cast<const u32x4 *>(sw + qd0 * 4096 + q * 1024 +
-                                                          lane * 16);
-          b[q][0] = (int)v[0]; b[q][1] = (int)v[1]; b[q][2] = (int)v[2]; b[q][3] = (int)v[3];
-          b[q][4] = 0; b[q][5] = 0; b[q][6] = 0; b[q][7] = 0;
-        }
-        // activation fragment m+1 is read from LDS while the MFMAs of m run
-        v8i acur = read_a(st, 0);
-        int sacur = read_sa(st, 0);
-#pragma unroll
-        for (int m = 0; m < MTW; ++m) {
-#pragma unroll
-          for (int i = m * TS::C / MTW; i < (m + 1) * TS::C / MTW; ++i) issue_one(s + NA - 1, i);
-          v8i anext = acur;
-          int sanext = sacur;
-          if (m + 1 < MTW) {
-            anext = read_a(st, m + 1);
-            sanext = read_sa(st, m + 1);
-          }
-#pragma unroll
-          for (int q = 0; q < NT; ++q)
-            acc[m][q] = mfma_q<FMT>(q & 3, acur, b[q], acc[m][q], sacur, sb[q / 4]);
-          __builtin_amdgcn_sched_barrier(0);
-          acur = anext;
-          sacur = sanext;
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vm<(NA - 2) * TS::C>();  // step s+1 has landed
-      barrier_keep_copies();
-    }
-
-#pragma unroll
-    for (int u = 0; u < QPW; ++u) {
-      const int tile0 = 16 * nb + 4 * (qd0 + u);
-      if (tile0 >= ntiles) continue;  // past the last weight tile: computed, never stored
-      if (!SECOND) {
-        const int j = tile0 / 4;  // unit: h columns [32j, 32j + 32)
-#pragma unroll
-        for (int m = 0; m < MTW; ++m) {
-          float g0[4], g1[4], u0[4], u1[4];
-          uint8_t *ar[4], *sr[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int mrow = 16 * (mw0 + m) + 4 * g + r;
-            const size_t prow = (size_t)(row0 + min(mrow, nrows - 1));
-            g0[r] = acc[m][4 * u][r]; g1[r] = acc[m][4 * u + 1][r];
-            u0[r] = acc[m][4 * u + 2][r]; u1[r] = acc[m][4 * u + 3][r];
-            ar[r] = p.a2c + prow * a2row;
-            sr[r] = p.a2s + prow * (p.I / 32);
-          }
-          swiglu_requant_n<F, FMT, 4>(g0, g1, u0, u1, ar, sr, j, r16);
-        }
-      } else {
-        // a padded row (loaded from the last valid row) stores the same
-        // values as that row, so every store is unconditional
-        float wa[MTW][4];
-#pragma unroll
-        for (int m = 0; m < MTW; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            wa[m][r] = p.wts[row0 + min(16 * (mw0 + m) + 4 * g + r, nrows - 1)];
-#pragma unroll
-        for (int m = 0; m < MTW; ++m) {
-          size_t prow[4];
-          float t[4][4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            prow[r] = (size_t)(row0 + min(16 * (mw0 + m) + 4 * g + r, nrows - 1));
-#pragma unroll
-            for (int q = 0; q < 4; ++q) t[r][q] = wa[m][r] * acc[m][4 * u + q][r];
-          }
-          stage_store_n<4>(p, prow, 16 * tile0, r16, t);
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Producer/consumer form of the tiled kernel.  The copy waits count a wave's
-// own copies in issue order, so in the form above, where every wave copies
-// both operands, a step's weights (HBM) and activations (L2) share one
-// deadline.  Here the consumer waves (RS per weight quad: wave c computes
+// The tiled kernel, in producer/consumer form.  Copy waits count a wave's
+// own copies in issue order, so a wave that copied both operands would give
+// a step's weights (HBM) and activations (L2) one deadline (an earlier form
+// did, and measured 7-8% slower for GEMM1 and 2-6% for GEMM2).  Here the
+// consumer waves (RS per weight quad: wave c computes
 // quad c % 4 on m-tiles [(c / 4) MT / RS, +MT / RS)) copy only their quad's
 // four 1 KiB fragments (a share each) and its scale dword into a ring of NB
 // weight stages, NB - 1 steps ahead, and wait only for those; the producer
@@ -713,29 +416,6 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
   wait_vm<0>();  // no copy into this workgroup's LDS outlives it
 }
 
-template <int RS, int QPW, bool SECOND>
-static hipError_t launch_tiled_w(const GemmArgs &a, const KArgs &k, hipStream_t s) {
-  const unsigned grid = (unsigned)(a.num_cus / 8 * 8);  // one workgroup per CU
-#define TILED(F_, MT_)                                                                 \
-  case MT_:                                                                            \
-    tiled_kernel<F_, MT_, RS, QPW, SECOND>                                             \
-        <<<grid, 64 * TileShape<F_, MT_, RS, QPW, 3>::NWV, 0, s>>>(k);                 \
-    break;
-  if (a.act == MOE_ACT_MXFP8_E4M3) {
-    switch (a.plan.mt) {
-      TILED(0, 2) TILED(0, 4) TILED(0, 6) TILED(0, 8) TILED(0, 10)
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (a.plan.mt) {
-      TILED(4, 4) TILED(4, 8)
-      default: return hipErrorInvalidValue;
-    }
-  }
-#undef TILED
-  return hipGetLastError();
-}
-
 template <bool SECOND>
 static hipError_t launch_pc(const GemmArgs &a, const KArgs &k, hipStream_t s) {
   const unsigned grid = (unsigned)(a.num_cus / 8 * 8);  // one workgroup per CU
@@ -758,18 +438,10 @@ static hipError_t launch_pc(const GemmArgs &a, const KArgs &k, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Of the form-1 wave splits only the one-row split is built: the 2 x 2 and
-// eight-wave forms (launch_tiled_w<2, 2> / <2, 1>) measured no faster on the
-// 7168 x 3072 layer.
 template <bool SECOND>
 static hipError_t launch_tiled(const GemmArgs &a, const KArgs &k, hipStream_t s) {
-  // split 2: both GEMMs in the producer/consumer form; on the 7168 x 3072
-  // and 5120 x 640 layers at T >= 8192 it measured 7-8% faster than form 1
-  // for GEMM1 and 2-6% faster for GEMM2 (whose epilogue loads the routing
-  // weights per m-tile to fit two waves on one SIMD)
-  if (a.plan.split == 2) return launch_pc<SECOND>(a, k, s);
-  if (a.plan.split != 1) return hipErrorInvalidValue;
-  return launch_tiled_w<1, 1, SECOND>(a, k, s);
+  if (a.plan.split != kTiledSplit) return hipErrorInvalidValue;
+  return launch_pc<SECOND>(a, k, s);
 }
 
 hipError_t launch_tiled_gemm1(const GemmArgs &a, const KArgs &k, hipStream_t s) {

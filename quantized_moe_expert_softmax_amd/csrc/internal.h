@@ -129,10 +129,9 @@ hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int E, in
 //   stream: 16-row m-tiles, the four waves of a workgroup split K, weights
 //           go straight from HBM to VGPRs (decode: few rows per expert)
 //   tiled:  bm = 16*MT rows per work item staged in LDS and shared by the
-//           waves, each wave owning 64 weight rows (prefill)
-// Form of the tiled kernels: 1 = four waves that each copy part of both
-// operands; 2 = GEMM1 with four MFMA waves that copy only their own weights
-// and a fifth wave that copies the activations (GEMM2 stays in form 1).
+//           waves, two MFMA waves per 64 weight rows (prefill)
+// Form of the tiled kernels (the only one built): MFMA waves that copy only
+// their own weights, producer waves that copy the activations.
 constexpr int kTiledSplit = 2;
 
 struct GemmPlan {
