@@ -30,7 +30,9 @@ the large shards at prefill sizes).  layer_mfma_frac is the whole layer's
 
 cpu_baseline: the CPU oracle (test infrastructure, single-threaded C)
 timed on a bounded sample of the same workload: routing, sort and
-quantisation of all T tokens plus the expert FFN of a few sampled tokens.
+quantisation of all T tokens plus the expert FFN of a few sampled tokens;
+cpu_baseline_all_cores: the same oracle over token partitions, one thread
+per host core (up to 16), on 2 sampled tokens per thread.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
 """
@@ -294,9 +296,56 @@ def cpu_baseline(moe, torch, layer_dev_weights, wl, T, act, rows):
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
+        "front_s_per_token": t_front / T,
         "sample": ("route+sort+quant of all %d tokens (%.3f s) + expert FFN of %d sampled tokens "
                    "(%.2f s); value = 1 / (front time per token + FFN time per sampled token)"
                    % (T, t_front, len(sample), t_ffn)),
+    }
+
+
+def cpu_baseline_all_cores(torch, layer_dev_weights, wl, T, act, single):
+    """The same oracle over token partitions, one thread per host core (its C
+    entry points keep no state between calls; ctypes releases the GIL), on a
+    bounded sample of 2 tokens per thread.  `single` is the single-thread
+    result, whose routing/sort/quant time per token is reused."""
+    import concurrent.futures
+    import platform
+    import numpy as np
+    import oracle
+    w13, w13s, w2, w2s = layer_dev_weights
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    x = wl.x(T)
+    lg = wl.logits(T, 0)
+    n = min(T, 2 * cores)
+    sample = np.unique(np.linspace(0, T - 1, num=n).astype(np.int64))
+    cache = {}
+    sel, _ = oracle.route(lg[sample], wl.top_k)
+    for e in sorted(set(int(v) for v in sel.reshape(-1))):
+        cache[e] = tuple(a[e].cpu().numpy() for a in (w13, w13s, w2, w2s))
+    parts = [p for p in np.array_split(sample, cores) if len(p)]
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(parts)) as ex:
+        list(ex.map(lambda part: oracle.forward_rows(x, lg, part, cache.__getitem__, wl.top_k, act),
+                    parts))
+    t_ffn = time.perf_counter() - t0
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    per_token = single["front_s_per_token"] + t_ffn / len(sample)
+    return {
+        "value": 1.0 / per_token,
+        "unit": "tokens/s",
+        "cores": len(parts),
+        "kind": "oracle",
+        "sample": ("expert FFN of %d sampled tokens in %d threads (%.2f s wall) + the single-thread "
+                   "route+sort+quant time per token; host %s" % (len(sample), len(parts), t_ffn,
+                                                                 model)),
     }
 
 
@@ -367,10 +416,12 @@ def main():
             log("T=%d: %s" % (t, sweep[str(t)]))
     sweep[str(T)] = entry(T, r)
 
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         cpu = cpu_baseline(moe, torch, w, wl, T, act, args.cpu_rows)
+        cpu_all = cpu_baseline_all_cores(torch, w, wl, T, act, cpu)
+        cpu.pop("front_s_per_token")
     traffic, traffic_src = measured_traffic(wl.name, T, act)
     dtype = "mxfp8xmxfp4" if act == 0 else "mxfp4xmxfp4"
     line = {
@@ -406,6 +457,8 @@ def main():
         "kernels_us": kernels_us,
         "sweep": sweep,
         "cpu_baseline": cpu,
+        # the same oracle over token partitions on all host cores (a baseline, not the target)
+        "cpu_baseline_all_cores": cpu_all,
     }
     print(json.dumps(line), flush=True)
     layer.close()
