@@ -105,6 +105,21 @@ def gemm_source_hash():
     return h.hexdigest()[:16]
 
 
+def build_info(torch):
+    """What produced the numbers: a hash of the library's HIP sources (the GPU
+    box's copy of the tree has no git metadata), the GEMM-source hash the
+    traffic figures are keyed by, and the torch / HIP runtime and device."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return {"csrc_sha256": h.hexdigest()[:16], "gemm_source_hash": gemm_source_hash(),
+            "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+            "device": torch.cuda.get_device_name(0)}
+
+
 def measured_traffic(workload, T, act):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 --pmc summary
     (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by what the
@@ -459,6 +474,7 @@ def main():
         "cpu_baseline": cpu,
         # the same oracle over token partitions on all host cores (a baseline, not the target)
         "cpu_baseline_all_cores": cpu_all,
+        "build": build_info(torch),
     }
     print(json.dumps(line), flush=True)
     layer.close()
