@@ -367,7 +367,7 @@ def cpu_baseline_all_cores(torch, layer_dev_weights, wl, T, act, single):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (the layer's "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (a layer's "
               "experts all fit one MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
