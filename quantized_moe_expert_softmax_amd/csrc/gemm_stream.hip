@@ -66,8 +66,11 @@ __global__ __launch_bounds__(64 * NW) void gemm1_kernel(KArgs p) {
   const size_t a1row = FMT == 0 ? (size_t)p.H : (size_t)p.H / 2;
   const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
   const size_t nquads = (size_t)(2 * p.I) / 64;
+  // items m-tile major: consecutive workgroups stream consecutive quads of one
+  // expert's weights (measured 2-3% faster at T = 8..64 than unit-major,
+  // where they read the same quad of different experts)
   for (long w = blockIdx.x; w < total; w += gridDim.x) {
-    const int j = (int)(w / n_mt), mt = (int)(w % n_mt);
+    const int mt = (int)(w / NU), j = (int)(w % NU);
     const int e = uniform(p.mbexp[mt]);
     const int row0 = uniform(p.offsets[e]) + kMTile * (mt - uniform(p.mtoff[e]));
     const int nrows = min(kMTile, uniform(p.offsets[e + 1]) - row0);
@@ -123,8 +126,8 @@ __global__ __launch_bounds__(64 * NW) void gemm2_kernel(KArgs p) {
   const int s0 = wave * S / NW, s1 = (wave + 1) * S / NW;
   const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
   const size_t nquads = (size_t)p.H / 64;
-  for (long w = blockIdx.x; w < total; w += gridDim.x) {
-    const int nb = (int)(w / n_mt), mt = (int)(w % n_mt);
+  for (long w = blockIdx.x; w < total; w += gridDim.x) {  // m-tile major, as in GEMM1
+    const int mt = (int)(w / NB), nb = (int)(w % NB);
     const int e = uniform(p.mbexp[mt]);
     const int row0 = uniform(p.offsets[e]) + kMTile * (mt - uniform(p.mtoff[e]));
     const int nrows = min(kMTile, uniform(p.offsets[e + 1]) - row0);
