@@ -361,19 +361,22 @@ GemmPlan choose_plan(int T, int top_k, int E, int act) {
     int mt = (int)ceil(want / 16.0);
     mt = mt + (mt & 1);
     if (mt > 10) {
-      // Experts span several m-blocks at any tile height: of BM = 128 and 160
-      // take the one with fewer expected padded rows, E[ceil(M / BM)] * BM
-      // for a load M ~ N(avg, avg) (ties: 160, fewer weight re-reads).  On
-      // the 5120 x {640, 1152} shards the tuner's pick matches this at
-      // T = 16384 and 32768 (BM = 128 up to 3.8% faster at mean loads of
-      // 384 and 512 rows, 160 faster at 256 and 768).
+      // Experts span several m-blocks at any tile height: of BM = 128, 160
+      // and 192 take the one with the fewest expected padded rows,
+      // E[ceil(M / BM)] * BM for a load M ~ N(avg, avg); within 1% of the
+      // fewest, the largest BM (fewer m-blocks, fewer weight re-reads).  On
+      // the 5120 x {640, 1152} shards at T = 16384 and 32768 this picks what
+      // the tuner measured fastest: 128 at a mean load of 384 rows, 192 at
+      // 512 (4-6% ahead of 128 and 160), 160 at 256 and 768.
       auto padded = [&](double bm) {
         double blocks = 0.0;
         for (int j = 0; j < 64; ++j)  // P(M > j bm), summed: E[ceil(M / bm)]
           blocks += 0.5 * erfc((j * bm - avg) / sqrt(2.0 * avg));
         return blocks * bm;
       };
-      mt = padded(128.0) < padded(160.0) - 0.5 ? 8 : 10;
+      const double p8 = padded(128.0), p10 = padded(160.0), p12 = padded(192.0);
+      const double best = fmin(p8, fmin(p10, p12));
+      mt = p12 <= 1.01 * best ? 12 : (p10 <= 1.01 * best ? 10 : 8);
     }
     return GemmPlan{true, mt < 2 ? 2 : mt, kTiledSplit};
   }

@@ -152,7 +152,9 @@ struct PcShape {
   static constexpr int CB = 4 / RS + 1;               // consumer copies per step (fragments, scale)
   static constexpr int OFF_BS = 4 * 4096;
   static constexpr int B_STAGE = OFF_BS + 4 * 256;
-  static constexpr int NA = kPcActStages;
+  // a 192-row MXFP8 tile (24 KiB a stage) keeps three activation stages so
+  // that four weight stages still fit
+  static constexpr int NA = A_BYTES > 20 * 1024 ? 3 : kPcActStages;
   static constexpr int NB_FIT = (160 * 1024 - NA * A_STAGE) / B_STAGE;
   static constexpr int NB = NB_FIT < kPcWStages ? NB_FIT : kPcWStages;
   static constexpr int B_BASE = NA * A_STAGE;
@@ -203,9 +205,10 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
   // (A4W4, T = 16384, MT = 8); at MT = 10 its extra live registers spill, so
   // there each item issues its own first NB - 1 steps and its copies past
   // the last step re-read that step.  (With two consumer waves per quad a
-  // wave holds at most 5 m-tiles, and the cross-item stream runs at every
-  // tile height.)
-  constexpr bool XITEM = MT / kPcRowSplit <= 8;
+  // wave holds MT / 2 m-tiles, and the cross-item stream runs at every tile
+  // height up to 160 rows; at 192 rows (6 m-tiles a wave) its registers
+  // would spill, so there each item issues its own first steps.)
+  constexpr bool XITEM = MT / kPcRowSplit <= 5;
   const int qd = uniform(wave & 3);  // the weight quad a consumer wave computes and copies
   const int rh = PS::RS == 1 ? 0 : uniform(wave >> 2);  // its share of the copies and m-tiles
   constexpr int MTW = PS::MTW;
@@ -425,7 +428,7 @@ static hipError_t launch_pc(const GemmArgs &a, const KArgs &k, hipStream_t s) {
     break;
   if (a.act == MOE_ACT_MXFP8_E4M3) {
     switch (a.plan.mt) {
-      PC(0, 2) PC(0, 4) PC(0, 6) PC(0, 8) PC(0, 10)
+      PC(0, 2) PC(0, 4) PC(0, 6) PC(0, 8) PC(0, 10) PC(0, 12)
       default: return hipErrorInvalidValue;
     }
   } else {

@@ -144,7 +144,7 @@ struct GemmPlan {
 GemmPlan choose_plan(int T, int top_k, int E, int act);
 // tiled m-tiles per item built for an activation format
 inline bool tiled_mt_built(int act, int mt) {
-  if (act == MOE_ACT_MXFP8_E4M3) return mt == 2 || mt == 4 || mt == 6 || mt == 8 || mt == 10;
+  if (act == MOE_ACT_MXFP8_E4M3) return mt == 2 || mt == 4 || mt == 6 || mt == 8 || mt == 10 || mt == 12;
   return mt == 4 || mt == 8;
 }
 

@@ -26,7 +26,7 @@ _NAMES = {MOE_PLAN_STREAM: "stream", MOE_PLAN_TILED: "tiled", MOE_PLAN_FUSED: "f
 
 
 def candidates(act: int):
-    rows = (32, 64, 96, 128, 160) if act == MOE_ACT_MXFP8_E4M3 else (64, 128)
+    rows = (32, 64, 96, 128, 160, 192) if act == MOE_ACT_MXFP8_E4M3 else (64, 128)
     return [(MOE_PLAN_STREAM, 16), (MOE_PLAN_FUSED, 16)] + [(MOE_PLAN_TILED, r) for r in rows]
 
 

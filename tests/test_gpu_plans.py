@@ -139,7 +139,8 @@ def test_fused_plan(T, H, I, E, k, act):
 MANY_ITEMS = [
     (0, 32, 4096, 256, 128, 64, 4),    # MT 2: ~512 GEMM1 items, S = 2 / 1
     (0, 96, 4096, 128, 512, 64, 4),    # MT 6: ~768 GEMM1 items, S = 1 / 4
-    (0, 160, 16384, 128, 128, 64, 4),  # MT 10: ~450 items, per-item prologue
+    (0, 160, 16384, 128, 128, 64, 4),  # MT 10: ~450 items
+    (0, 192, 16384, 128, 128, 64, 4),  # MT 12: ~380 items, per-item prologue
     (1, 64, 8192, 256, 128, 64, 4),    # MXFP4 MT 4: ~512 items
     (1, 128, 16384, 128, 128, 64, 4),  # MXFP4 MT 8: ~512 items, S = 1 / 1
 ]
