@@ -280,8 +280,8 @@ typedef struct {
     int32_t variant; /* moe_plan_variant                                          */
     int32_t rows;    /* token rows per work item: 16 for MOE_PLAN_STREAM and
                         MOE_PLAN_FUSED; for
-                        MOE_PLAN_TILED 32, 64, 96, 128, 160 or 192 (MXFP8) and 64
-                        or 128 (MXFP4)                                            */
+                        MOE_PLAN_TILED 32, 64, 96, 128, 160 or 192 (both
+                        activation formats)                                       */
 } moe_plan;
 
 /* Replace the layer's table with plans[0 .. n-1] (host array, copied; at most

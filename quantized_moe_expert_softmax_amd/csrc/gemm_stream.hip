@@ -347,9 +347,11 @@ GemmPlan choose_plan(int T, int top_k, int E, int act) {
   // 2 rows) and the pipelined tiled kernel, whose BM covers the mean plus 1.5
   // standard deviations of a binomial expert load (under uniform routing
   // most experts are then one m-block and their weights are read once).  An
-  // activation tile must fill whole 1 KiB copies per wave (MXFP8: MT even;
-  // MXFP4: MT a multiple of 4) and MT <= 10 keeps the accumulators in
-  // registers.  Both thresholds follow the plan tuner's measurements on the
+  // activation tile fills whole 1 KiB copies and splits over two MFMA waves
+  // per quad (MT even), and MT <= 12 keeps the accumulators in registers;
+  // both activation formats take the same rule (MXFP4 had only 64 and 128
+  // rows before, so at a mean load of 128 rows half its experts read their
+  // weights twice).  Both thresholds follow the plan tuner's measurements on the
   // 7168 x 3072 (E = 384, top_k = 6) and 5120 x {640, 1152} (E = 384 x 6 and
   // 128 x 3) layers: its pick matches this rule wherever the two differ by
   // more than ~2%.
@@ -357,7 +359,7 @@ GemmPlan choose_plan(int T, int top_k, int E, int act) {
   const double avg = (double)N / E;
   if (avg < 2.0) return GemmPlan{false, 1, 1};
   const double want = avg + 1.5 * sqrt(avg);
-  if (act == MOE_ACT_MXFP8_E4M3) {
+  {
     int mt = (int)ceil(want / 16.0);
     mt = mt + (mt & 1);
     if (mt > 10) {
@@ -378,9 +380,9 @@ GemmPlan choose_plan(int T, int top_k, int E, int act) {
       const double best = fmin(p8, fmin(p10, p12));
       mt = p12 <= 1.01 * best ? 12 : (p10 <= 1.01 * best ? 10 : 8);
     }
+    (void)act;
     return GemmPlan{true, mt < 2 ? 2 : mt, kTiledSplit};
   }
-  return GemmPlan{true, want <= 64.0 ? 4 : 8, kTiledSplit};
 }
 
 // Waves per stream workgroup (each takes 1/NW of the K steps).  Measured on

@@ -433,7 +433,7 @@ static hipError_t launch_pc(const GemmArgs &a, const KArgs &k, hipStream_t s) {
     }
   } else {
     switch (a.plan.mt) {
-      PC(4, 4) PC(4, 8)
+      PC(4, 2) PC(4, 4) PC(4, 6) PC(4, 8) PC(4, 10) PC(4, 12)
       default: return hipErrorInvalidValue;
     }
   }

@@ -142,10 +142,10 @@ struct GemmPlan {
   int bm() const { return 16 * mt; }
 };
 GemmPlan choose_plan(int T, int top_k, int E, int act);
-// tiled m-tiles per item built for an activation format
+// tiled m-tiles per item built (both activation formats)
 inline bool tiled_mt_built(int act, int mt) {
-  if (act == MOE_ACT_MXFP8_E4M3) return mt == 2 || mt == 4 || mt == 6 || mt == 8 || mt == 10 || mt == 12;
-  return mt == 4 || mt == 8;
+  (void)act;
+  return mt == 2 || mt == 4 || mt == 6 || mt == 8 || mt == 10 || mt == 12;
 }
 
 struct GemmArgs {

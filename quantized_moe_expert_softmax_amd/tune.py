@@ -18,7 +18,7 @@ import json
 import sys
 import time
 
-from . import (MOE_ACT_MXFP8_E4M3, MOE_PLAN_FUSED, MOE_PLAN_STREAM, MOE_PLAN_TILED,
+from . import (MOE_PLAN_FUSED, MOE_PLAN_STREAM, MOE_PLAN_TILED,
                alloc_workspace, moe_forward, moe_get_plan, moe_set_plans)
 
 
@@ -26,7 +26,7 @@ _NAMES = {MOE_PLAN_STREAM: "stream", MOE_PLAN_TILED: "tiled", MOE_PLAN_FUSED: "f
 
 
 def candidates(act: int):
-    rows = (32, 64, 96, 128, 160, 192) if act == MOE_ACT_MXFP8_E4M3 else (64, 128)
+    rows = (32, 64, 96, 128, 160, 192)  # both activation formats
     return [(MOE_PLAN_STREAM, 16), (MOE_PLAN_FUSED, 16)] + [(MOE_PLAN_TILED, r) for r in rows]
 
 

@@ -58,7 +58,7 @@ def test_table_lookup_order_and_fallback():
 
 
 @pytest.mark.parametrize("bad", [
-    dict(rows=48), dict(rows=160, act=1), dict(variant=3), dict(act=5), dict(top_k=0),
+    dict(rows=48), dict(rows=224, act=1), dict(variant=3), dict(act=5), dict(top_k=0),
     dict(top_k=9), dict(t_max=0), dict(variant=moe.MOE_PLAN_STREAM, rows=32),
     dict(variant=moe.MOE_PLAN_FUSED, rows=32),
 ])
