@@ -380,8 +380,13 @@ GemmPlan choose_plan(int T, int top_k, int E, int act) {
       const double best = fmin(p8, fmin(p10, p12));
       mt = p12 <= 1.01 * best ? 12 : (p10 <= 1.01 * best ? 10 : 8);
     }
+    // at least 64 rows: under uniform loads 64 costs 0.2-0.4% against 32 where
+    // the rule would pick 32 (T = 128 .. 1024 on the 7168 x 3072 layer), and
+    // under skewed loads (a fixed per-expert bias, half the experts empty,
+    // which the mean over all experts hides) it is 10-15% faster at
+    // T = 512 and 1024
     (void)act;
-    return GemmPlan{true, mt < 2 ? 2 : mt, kTiledSplit};
+    return GemmPlan{true, mt < 4 ? 4 : mt, kTiledSplit};
   }
 }
 
