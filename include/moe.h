@@ -256,7 +256,7 @@ moe_status moe_quant_act(const void *x, int T, int H, moe_act_dtype act, uint8_t
  * transport support to MegaMoE", Technical Details: BM profiles chosen by
  * token count).  A layer starts with an empty table; calls no entry matches
  * use the built-in choice (stream below 2 rows per expert, else tiled with
- * BM from the expected expert load).  Every plan computes the same result
+ * BM from the expected expert load, at least 64 rows).  Every plan computes the same result
  * (parity is tested per plan); plans differ only in speed. */
 typedef enum {
     MOE_PLAN_STREAM = 0, /* 16-row m-tiles, K split over the waves, weights to VGPRs */
