@@ -42,3 +42,17 @@ def test_shapes_and_distributions():
     ids = synth.expert_ids(T, E, 4, 3)
     assert ids.shape == (T, 4)
     assert all(len(set(r)) == 4 for r in ids)  # k distinct experts per token
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message before any
+    device work."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
