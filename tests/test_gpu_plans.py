@@ -57,6 +57,40 @@ def test_table_lookup_order_and_fallback():
     assert moe.moe_get_plan(layer, 4, k, 0) == builtin_4
 
 
+# The built-in choice on the layer shapes it was measured on (7168 x 3072 with
+# E = 384, top_k = 6; the 5120 x {640, 1152} shards with E = 384 x 6 and
+# 128 x 3): weight streaming below 2 rows per expert, tiled at least 64 rows,
+# BM covering the mean plus 1.5 sigma up to 160 rows, and above that the tile
+# with the fewest expected padded rows.  It depends on T, top_k and E only.
+BUILTIN = [
+    # (E, top_k, T, variant, rows)
+    (384, 6, 1, moe.MOE_PLAN_STREAM, 16),
+    (384, 6, 127, moe.MOE_PLAN_STREAM, 16),    # 1.98 rows per expert
+    (384, 6, 128, moe.MOE_PLAN_TILED, 64),     # 2 rows: tiled, at the 64-row minimum
+    (384, 6, 1024, moe.MOE_PLAN_TILED, 64),
+    (384, 6, 2048, moe.MOE_PLAN_TILED, 64),    # mean 32 + 1.5 sigma -> 48 -> even MT
+    (384, 6, 4096, moe.MOE_PLAN_TILED, 96),    # mean 64 -> 76 rows
+    (384, 6, 8192, moe.MOE_PLAN_TILED, 160),   # mean 128 -> 145 rows
+    (384, 6, 16384, moe.MOE_PLAN_TILED, 160),  # mean 256: fewest padded rows at 160
+    (384, 6, 24576, moe.MOE_PLAN_TILED, 128),  # mean 384: at 128
+    (384, 6, 32768, moe.MOE_PLAN_TILED, 192),  # mean 512: at 192
+    (128, 3, 16384, moe.MOE_PLAN_TILED, 128),  # mean 384
+    (128, 3, 32768, moe.MOE_PLAN_TILED, 160),  # mean 768
+]
+
+
+@pytest.mark.parametrize("E,k", sorted({(c[0], c[1]) for c in BUILTIN}))
+def test_builtin_plan_choices(E, k):
+    w, _, _ = _small(1, 128, 128, E, k, seed=13)
+    layer = _layer(*w)
+    for e_, k_, T, variant, rows in BUILTIN:
+        if (e_, k_) != (E, k):
+            continue
+        for act in (0, 1):  # both activation formats take the same rule
+            got = moe.moe_get_plan(layer, T, k, act)
+            assert (got["variant"], got["rows"]) == (variant, rows), (E, k, T, act, got)
+
+
 @pytest.mark.parametrize("bad", [
     dict(rows=48), dict(rows=224, act=1), dict(variant=3), dict(act=5), dict(top_k=0),
     dict(top_k=9), dict(t_max=0), dict(variant=moe.MOE_PLAN_STREAM, rows=32),
