@@ -87,17 +87,8 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   // all rows and banks enabled: every lane is written, so no old value is kept
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
-// maximum over the 16 lanes of a row: quad_perm [1,0,3,2], [2,3,0,1], then
-// row_half_mirror and row_mirror
-__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
-  v = max(v, dpp<0xB1>(v));
-  v = max(v, dpp<0x4E>(v));
-  v = max(v, dpp<0x141>(v));
-  v = max(v, dpp<0x140>(v));
-  return v;
-}
-
-// 16-lane row maximum of NR independent values, the NR chains advanced in
+// 16-lane row maximum of NR independent values (quad_perm [1,0,3,2],
+// [2,3,0,1], then row_half_mirror and row_mirror), the NR chains advanced in
 // lock-step so that each DPP read follows other chains' work instead of
 // waiting out its own producer (a DPP operand written by the previous VALU
 // op needs wait states).
