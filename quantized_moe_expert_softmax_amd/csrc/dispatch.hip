@@ -352,11 +352,13 @@ hipError_t launch_quant(const uint16_t *x, long rows, int K, int act, uint8_t *c
 }
 
 // ---------------------------------------------------------------------------
-// Steps 1-3 in one launch for T <= kSortBlock tokens (the forward uses it up
-// to kFrontMaxT), where separate launches would cost more than the work: workgroup 0 routes every
-// token (one wave per token) and sorts the assignments exactly as the
-// hist/scan/scatter kernels do for a single sort block; workgroups 1.. quantise
-// the token rows.  The outputs are the same as those kernels' outputs.
+// Steps 1-3 in one launch for T <= kSortBlock tokens, where separate launches
+// would cost more than the work: workgroup 0 routes every token (one wave per
+// token; the forward does so up to kFrontMaxT tokens) or, with null logits,
+// takes the ids and weights the router kernel wrote, and sorts the
+// assignments exactly as the hist/scan/scatter kernels do for a single sort
+// block; workgroups 1.. quantise the token rows.  The outputs are the same as
+// those kernels' outputs.
 // ---------------------------------------------------------------------------
 template <int NV>
 __global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
@@ -383,23 +385,33 @@ __global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
     cnt[e] = 0;
     masks[0][e] = 0ull; masks[1][e] = 0ull; masks[2][e] = 0ull; masks[3][e] = 0ull;
   }
-  // wave w routes tokens w, w + 16, ...; the logits of four of them are
-  // loaded before the first is routed
-  for (int t0 = wave; t0 < T; t0 += 64) {
-    float v[4][NV];
+  if (p.logits) {
+    // wave w routes tokens w, w + 16, ...; the logits of four of them are
+    // loaded before the first is routed
+    for (int t0 = wave; t0 < T; t0 += 64) {
+      float v[4][NV];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (t0 + 16 * u < T) load_logits<NV>(p.logits + (long)(t0 + 16 * u) * E, E, lane, v[u]);
+      for (int u = 0; u < 4; ++u)
+        if (t0 + 16 * u < T) load_logits<NV>(p.logits + (long)(t0 + 16 * u) * E, E, lane, v[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = t0 + 16 * u;
-      if (t < T) route_values<NV>(v[u], E, k, lane, sid + t * k, sw + t * k);
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + 16 * u;
+        if (t < T) route_values<NV>(v[u], E, k, lane, sid + t * k, sw + t * k);
+      }
+    }
+  } else {
+    // routed by the router kernel earlier on the stream
+    for (int a = tid; a < N; a += 1024) {
+      sid[a] = p.ids[a];
+      sw[a] = p.wts[a];
     }
   }
   __syncthreads();
   for (int a = tid; a < N; a += 1024) {
-    p.ids[a] = sid[a];
-    p.wts[a] = sw[a];
+    if (p.logits) {
+      p.ids[a] = sid[a];
+      p.wts[a] = sw[a];
+    }
     atomicAdd(&cnt[sid[a]], 1);
   }
   __syncthreads();

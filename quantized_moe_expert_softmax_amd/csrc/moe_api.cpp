@@ -363,21 +363,34 @@ static moe_status forward_impl(moe_layer_t L, bool prequant, const void *x, cons
     ++stage;
   };
   mark();
-  if (T <= kFrontMaxT) {
-    // small decode batches: route, sort and quantisation in one launch (its
-    // time is recorded as the route stage; the sort and quant stages record
-    // ~0).  One workgroup routes every token there, which is slower than
-    // the separate kernels beyond a few tens of tokens.
+  // the fused front launch's arguments; routed_logits null: the router
+  // kernel has already written ids and wts
+  auto front_args = [&](const float *routed_logits) {
     FrontArgs f{};
-    f.logits = logits; f.x = static_cast<const uint16_t *>(x);
+    f.logits = routed_logits; f.x = static_cast<const uint16_t *>(x);
     f.T = T; f.E = L->E; f.top_k = top_k; f.H = L->H; f.act = act; f.bm = g.plan.bm();
     f.ids = ids; f.wts = wts; f.counts = counts; f.offsets = offsets; f.mtoff = mtoff;
     f.mbexp = mbexp; f.perm = perm; f.inv = inv; f.wsorted = wsorted; f.codes = a1c;
     f.scales = a1s;
     f.sync = g.sync;
     f.nsync = nsync;
-    if (e == hipSuccess) e = launch_front(f, s);
+    return f;
+  };
+  if (T <= kFrontMaxT) {
+    // small decode batches: route, sort and quantisation in one launch (its
+    // time is recorded as the route stage; the sort and quant stages record
+    // ~0).  One workgroup routes every token there, which is slower than
+    // the separate kernels beyond a few tens of tokens.
+    if (e == hipSuccess) e = launch_front(front_args(logits), s);
     for (int i = 0; i < 5; ++i) mark();
+  } else if (T <= kSortBlock) {
+    // up to one sort block: the router kernel, then sort and quantisation in
+    // one launch (recorded as the sort_hist stage; the scan, scatter and
+    // quant stages record ~0)
+    if (e == hipSuccess) e = launch_route(logits, T, L->E, top_k, ids, wts, s);
+    mark();
+    if (e == hipSuccess) e = launch_front(front_args(nullptr), s);
+    for (int i = 0; i < 4; ++i) mark();
   } else {
     if (e == hipSuccess) e = launch_route(logits, T, L->E, top_k, ids, wts, s);
     mark();
