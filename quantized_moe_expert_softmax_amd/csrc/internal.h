@@ -110,7 +110,7 @@ hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, cons
 struct FrontArgs {
   int32_t *sync;  // [nsync] zeroed (the fused GEMM launch's counters), or nsync 0
   int nsync;
-  const float *logits;  // null: ids and wts already hold the routing (router kernel)
+  const float *logits;
   const uint16_t *x;  // null: no quantisation (the caller's codes feed GEMM1)
   int T, E, top_k, H, act, bm;
   int32_t *ids;
