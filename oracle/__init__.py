@@ -61,9 +61,13 @@ def _load():
         lib.oracle_sort.argtypes = [P, i32, i32, i32, P, P, P]
         lib.oracle_forward.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, P, P, i32,
                                        i32, P, P, P, P, P]
+        lib.oracle_gemm1_rows.argtypes = [P, P, i64, i32, i32, i32, P, P, P, P, P]
+        lib.oracle_gemm2_rows.argtypes = [P, P, i64, i32, i32, i32, P, P, P, P, P]
+        lib.oracle_combine.argtypes = [P, i64, i32, i32, i32, P, P]
         for f in (lib.oracle_mx_quantize, lib.oracle_mx_quantize_bf16, lib.oracle_mx_dequantize,
                   lib.oracle_float_to_bf16, lib.oracle_route, lib.oracle_sort,
-                  lib.oracle_forward):
+                  lib.oracle_forward, lib.oracle_gemm1_rows, lib.oracle_gemm2_rows,
+                  lib.oracle_combine):
             f.restype = None
         _lib = lib
         return lib
@@ -224,3 +228,71 @@ def forward_rows(x_bits, logits, rows, weights_for, top_k: int, fmt: int,
     w2s = np.stack([p[3] for p in parts])
     return forward(np.asarray(x_bits)[rows], lg, w13, w13s, w2, w2s, top_k, fmt,
                    acc_double=acc_double, expert_map=emap, combine=combine)
+
+
+# ---- the layer's steps on their own (FP32 evaluation, as oracle_forward runs
+# them), for checking a device's intermediate results row by row ----
+
+def gemm1_rows(a1_codes, a1_scales, slab, w13, w13s, fmt: int):
+    """Steps 3-5 (GEMM1, SwiGLU, requantisation) on n given rows.
+
+    a1_codes [n, H or H/2], a1_scales [n, H/32]: the quantised token row of
+    each assignment; slab [n]: its expert's index into w13 [S, 2I, H/2] /
+    w13s [S, 2I, H/32].  Returns the A2 rows (codes [n, I or I/2], scales
+    [n, I/32]).
+    """
+    a1c = _c(a1_codes, np.uint8)
+    a1s = _c(a1_scales, np.uint8)
+    sl = _c(slab, np.int32).reshape(-1)
+    w13 = _c(w13, np.uint8)
+    w13s = _c(w13s, np.uint8)
+    n = sl.size
+    I = w13.shape[1] // 2
+    H = w13.shape[2] * 2
+    assert a1c.shape == (n, code_bytes_per_row(H, fmt)) and a1s.shape == (n, H // 32)
+    assert sl.size == 0 or (sl.min() >= 0 and sl.max() < w13.shape[0])
+    a2c = np.zeros((n, code_bytes_per_row(I, fmt)), np.uint8)
+    a2s = np.zeros((n, I // 32), np.uint8)
+    _load().oracle_gemm1_rows(_ptr(a1c), _ptr(a1s), n, H, I, fmt, _ptr(sl), _ptr(w13), _ptr(w13s),
+                              _ptr(a2c), _ptr(a2s))
+    return a2c, a2s
+
+
+def gemm2_rows(a2_codes, a2_scales, slab, wts, w2, w2s, fmt: int):
+    """Step 6 before the transport on n given rows: the weighted FP32 GEMM2 row
+    wts[r] * (A2 row r times every down row of expert slab[r]).
+
+    a2_codes [n, I or I/2], a2_scales [n, I/32], slab [n], wts [n] fp32,
+    w2 [S, H, I/2], w2s [S, H, I/32].  Returns rows [n, H] fp32.
+    """
+    a2c = _c(a2_codes, np.uint8)
+    a2s = _c(a2_scales, np.uint8)
+    sl = _c(slab, np.int32).reshape(-1)
+    wt = _c(wts, np.float32).reshape(-1)
+    w2 = _c(w2, np.uint8)
+    w2s = _c(w2s, np.uint8)
+    n = sl.size
+    H = w2.shape[1]
+    I = w2.shape[2] * 2
+    assert a2c.shape == (n, code_bytes_per_row(I, fmt)) and a2s.shape == (n, I // 32)
+    assert wt.size == n and (n == 0 or (sl.min() >= 0 and sl.max() < w2.shape[0]))
+    rows = np.zeros((n, H), np.float32)
+    _load().oracle_gemm2_rows(_ptr(a2c), _ptr(a2s), n, H, I, fmt, _ptr(sl), _ptr(wt), _ptr(w2),
+                              _ptr(w2s), _ptr(rows))
+    return rows
+
+
+def combine(rows, top_k: int, mode: int = COMBINE_FP32, want_f32: bool = False):
+    """The transport and FP32 slot-order sum of the weighted rows, then BF16.
+
+    rows [T*top_k, H] fp32 by assignment a = t*top_k + j.  Returns y [T, H]
+    as bf16 bit patterns (and the FP32 sums when want_f32).
+    """
+    r = _c(rows, np.float32)
+    n, H = r.shape
+    assert n % top_k == 0 and mode in (COMBINE_FP32, COMBINE_BF16, COMBINE_FP8)
+    T = n // top_k
+    y = np.zeros((T, H), np.uint16)
+    yf = np.zeros((T, H), np.float32) if want_f32 else None
+    _load().oracle_combine(_ptr(r), T, top_k, H, mode, _ptr(y), _ptr(yf))
+    return (y, yf) if want_f32 else y

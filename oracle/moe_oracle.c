@@ -39,8 +39,12 @@
  * sort invariants against a library stable sort, dense brute force, token
  * permutation invariance, the identity-expert construction, E=1/k=1
  * reduction to a dense quantised SwiGLU MLP, the unquantised-FP32 error
- * band).  GEMM/SwiGLU values at the large shapes are covered only by those
- * invariants (parity otherwise unpinned at those sizes).
+ * band, closed forms of the per-term combine transports at top_k > 1).
+ * GEMM/SwiGLU values at the large shapes are covered only by those
+ * invariants (parity otherwise unpinned at those sizes).  The per-step entry
+ * points (oracle_gemm1_rows, oracle_gemm2_rows, oracle_combine) run the same
+ * static functions as oracle_forward, and a test checks that composing them
+ * reproduces oracle_forward bit for bit.
  */
 #include <math.h>
 #include <stdint.h>
@@ -174,11 +178,17 @@ static void mx_quantize_rows_d(const double *v, long rows, int K, int fmt,
     }
 }
 
+/* Value of a code.  In OCP E4M3FN the all-ones magnitude (0x7F, 0xFF) is
+ * NaN, not a number: the quantiser never produces it, and a caller's code
+ * with it makes every value that depends on it NaN. */
 static double decode_code(int fmt, unsigned code)
 {
     fmt_desc d = describe(fmt);
     unsigned sign = code >> (d.nbits - 1);
-    double m = code_magnitude(fmt, code & ((1u << (d.nbits - 1)) - 1u));
+    unsigned mag = code & ((1u << (d.nbits - 1)) - 1u);
+    if (fmt == FMT_E4M3 && mag == 0x7Fu)
+        return NAN;
+    double m = code_magnitude(fmt, mag);
     return sign ? -m : m;
 }
 
@@ -361,6 +371,139 @@ void oracle_sort(const int32_t *ids, int T, int E, int top_k,
 }
 
 /* ------------------------------------------------------------------ */
+/* The layer, one assignment at a time                                 */
+/* ------------------------------------------------------------------ */
+
+/* Working rows of one evaluation (sized for H, I). */
+typedef struct {
+    double *wrow;  /* one dequantised weight row, max(H, I)          */
+    double *gu;    /* [2I] gate then up accumulators                 */
+    double *hbuf;  /* [I] SwiGLU output before requantisation        */
+    double *hdq;   /* [I] dequantised A2 row                         */
+    double *tdq;   /* [H] a weighted row in double (FP8 transport)   */
+    uint8_t *tq;   /* [H] its E4M3 codes                             */
+    uint8_t *ts;   /* [H/32] its scales                              */
+} scratch_rows;
+
+static scratch_rows scratch_alloc(int H, int I)
+{
+    scratch_rows s;
+    int KM = H > I ? H : I;
+    s.wrow = (double *)malloc(sizeof(double) * (size_t)KM);
+    s.gu = (double *)malloc(sizeof(double) * 2 * (size_t)I);
+    s.hbuf = (double *)malloc(sizeof(double) * (size_t)I);
+    s.hdq = (double *)malloc(sizeof(double) * (size_t)I);
+    s.tdq = (double *)malloc(sizeof(double) * (size_t)H);
+    s.tq = (uint8_t *)malloc((size_t)H + 1);
+    s.ts = (uint8_t *)malloc((size_t)H / 32 + 1);
+    return s;
+}
+
+static void scratch_free(scratch_rows *s)
+{
+    free(s->wrow); free(s->gu); free(s->hbuf); free(s->hdq); free(s->tdq); free(s->tq); free(s->ts);
+}
+
+/*
+ * GEMM1, SwiGLU and requantisation of one assignment ("add A4W4 and FP8 P2P
+ * transport support to MegaMoE", Technical Details: GEMM1 on the quantised
+ * activations, SwiGLU, A2 activations and scales emitted for GEMM2; "feat(moe):
+ * FlyDSL MegaMoE fused EP-MoE integration", summary: gate and up rows paired).
+ *   xdq     [H] the token's dequantised activation row
+ *   slab    the expert's index into w13/w13s
+ *   ha, hs  out: A2 codes (I or I/2 bytes) and I/32 scales
+ * gate n = sum over k ascending of xdq[k] * W13[n][k] (rows n < I), up = the
+ * same over rows I + n; h = silu(gate) * up with silu(g) = g / (1 + exp(-g));
+ * h quantised along I in 1x32 blocks.  FP32 products and sums (no FMA), or
+ * double when acc_double.
+ */
+static void gemm1_swiglu_requant(const double *xdq, long slab, int H, int I, int fmt,
+                                 const uint8_t *w13, const uint8_t *w13s, int acc_double,
+                                 scratch_rows *s, uint8_t *ha, uint8_t *hs)
+{
+    for (int n = 0; n < 2 * I; ++n) {
+        long row = slab * 2 * I + n;
+        dequant_row(w13 + row * (H / 2), w13s + row * (H / 32), H, FMT_E2M1, s->wrow);
+        if (acc_double) {
+            double acc = 0.0;
+            for (int k = 0; k < H; ++k)
+                acc += xdq[k] * s->wrow[k];
+            s->gu[n] = acc;
+        } else {
+            float acc = 0.0f;
+            for (int k = 0; k < H; ++k) {
+                float prod = (float)xdq[k] * (float)s->wrow[k];
+                acc = acc + prod;
+            }
+            s->gu[n] = (double)acc;
+        }
+    }
+    for (int i = 0; i < I; ++i) {
+        if (acc_double) {
+            double g = s->gu[i], u = s->gu[I + i];
+            s->hbuf[i] = g / (1.0 + exp(-g)) * u;
+        } else {
+            float g = (float)s->gu[i], u = (float)s->gu[I + i];
+            float sg = g / (1.0f + expf(-g));
+            s->hbuf[i] = (double)(sg * u);
+        }
+    }
+    mx_quantize_rows_d(s->hbuf, 1, I, fmt, ha, hs);
+}
+
+/*
+ * GEMM2 of one assignment times its routing weight (same page: GEMM2 on the
+ * A2 activations, weighted GEMM2 rows): o[h] = sum over i ascending of
+ * hdq[i] * W2[h][i]; the row is wj * o[h], in FP32 (trow) or, when
+ * acc_double, in double (trow_d).
+ */
+static void gemm2_weighted(const double *hdq, long slab, int H, int I, const uint8_t *w2,
+                           const uint8_t *w2s, float wj, int acc_double, scratch_rows *s,
+                           float *trow, double *trow_d)
+{
+    for (int hh = 0; hh < H; ++hh) {
+        long row = slab * H + hh;
+        dequant_row(w2 + row * (I / 2), w2s + row * (I / 32), I, FMT_E2M1, s->wrow);
+        if (acc_double) {
+            double acc = 0.0;
+            for (int i = 0; i < I; ++i)
+                acc += hdq[i] * s->wrow[i];
+            trow_d[hh] = (double)wj * acc;
+        } else {
+            float acc = 0.0f;
+            for (int i = 0; i < I; ++i) {
+                float prod = (float)hdq[i] * (float)s->wrow[i];
+                acc = acc + prod;
+            }
+            trow[hh] = wj * acc;
+        }
+    }
+}
+
+/*
+ * The transport of one weighted FP32 row to the combine (same page: the
+ * combine payload is BF16 or fp8 1x32 blockwise): 0 leaves it as it is; 1
+ * rounds each element to BF16 (nearest even); 2 quantises the row along H to
+ * MXFP8 (E4M3, one E8M0 scale per 32 elements, the activation rule) and
+ * dequantises it.  Each of the top_k rows of a token is transported on its
+ * own, before the sum.
+ */
+static void transport_row(float *trow, int H, int combine, scratch_rows *s)
+{
+    if (combine == 1) {
+        for (int hh = 0; hh < H; ++hh)
+            trow[hh] = bf16_to_float(float_to_bf16(trow[hh]));
+    } else if (combine == 2) {
+        for (int hh = 0; hh < H; ++hh)
+            s->tdq[hh] = (double)trow[hh];
+        mx_quantize_rows_d(s->tdq, 1, H, FMT_E4M3, s->tq, s->ts);
+        dequant_row(s->tq, s->ts, H, FMT_E4M3, s->tdq);
+        for (int hh = 0; hh < H; ++hh)
+            trow[hh] = (float)s->tdq[hh];
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* The layer                                                            */
 /* ------------------------------------------------------------------ */
 
@@ -373,12 +516,8 @@ void oracle_sort(const int32_t *ids, int T, int E, int top_k,
  * acc_double  0: FP32 evaluation (products and sums in float, ascending
  *             K, no contraction); 1: the same steps in double.
  * combine  how each weighted GEMM2 row w_j * o_j (FP32, length H) reaches the
- *             FP32 top-k sum: 0 as it is; 1 rounded to BF16 (nearest even);
- *             2 quantised to MXFP8 (E4M3 with one E8M0 scale per 1x32 block
- *             along H, the activation rule) and dequantised.  Modes 1 and 2
- *             are the compressed combine transports of "add A4W4 and FP8 P2P
- *             transport support to MegaMoE" (Technical Details: BF16 or
- *             fp8 1x32 blockwise combine payloads); they need acc_double = 0.
+ *             FP32 top-k sum (transport_row): 0 as it is, 1 BF16, 2 MXFP8.
+ *             Modes 1 and 2 need acc_double = 0.
  * y        [T][H] bf16 (round to nearest even of the FP32 combine)
  * y_f32    optional [T][H] fp32 combine before the bf16 rounding
  * a2_codes / a2_scales  optional [T*top_k][I or I/2] / [T*top_k][I/32]
@@ -396,24 +535,18 @@ void oracle_forward(const uint16_t *x, const float *logits, int T, int H, int I,
 {
     long a1_row = (fmt == FMT_E4M3) ? H : H / 2;
     long a2_row = (fmt == FMT_E4M3) ? I : I / 2;
-    int KM = H > I ? H : I;
     int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * ((size_t)T * top_k + 1));
     float *wts = (float *)malloc(sizeof(float) * ((size_t)T * top_k + 1));
     uint8_t *xa = (uint8_t *)malloc((size_t)a1_row + 1);
     uint8_t *xs = (uint8_t *)malloc((size_t)H / 32 + 1);
     double *xdq = (double *)malloc(sizeof(double) * (size_t)H);
-    double *wrow = (double *)malloc(sizeof(double) * (size_t)KM);
-    double *gu = (double *)malloc(sizeof(double) * 2 * (size_t)I); /* gate, then up */
-    double *hbuf = (double *)malloc(sizeof(double) * (size_t)I);
     uint8_t *ha = (uint8_t *)malloc((size_t)a2_row + 1);
     uint8_t *hs = (uint8_t *)malloc((size_t)I / 32 + 1);
-    double *hdq = (double *)malloc(sizeof(double) * (size_t)I);
     float *cf = (float *)malloc(sizeof(float) * (size_t)H);
     double *cd = (double *)malloc(sizeof(double) * (size_t)H);
     float *trow = (float *)malloc(sizeof(float) * (size_t)H);   /* weighted row */
-    double *tdq = (double *)malloc(sizeof(double) * (size_t)H);
-    uint8_t *tq = (uint8_t *)malloc((size_t)H + 1);
-    uint8_t *ts = (uint8_t *)malloc((size_t)H / 32 + 1);
+    double *trow_d = (double *)malloc(sizeof(double) * (size_t)H);
+    scratch_rows s = scratch_alloc(H, I);
 
     init_tables();
 
@@ -431,75 +564,21 @@ void oracle_forward(const uint16_t *x, const float *logits, int T, int H, int I,
         for (int j = 0; j < top_k; ++j) {
             long a = (long)t * top_k + j;
             int e = ids[a];
-            float wj = wts[a];
             long slab = expert_map ? (long)expert_map[e] : (long)e;
-            /* step 3: GEMM1, the token row against every gate and up row of e */
-            for (int n = 0; n < 2 * I; ++n) {
-                long row = slab * 2 * I + n;
-                dequant_row(w13 + row * (H / 2), w13s + row * (H / 32), H, FMT_E2M1, wrow);
-                if (acc_double) {
-                    double acc = 0.0;
-                    for (int k = 0; k < H; ++k)
-                        acc += xdq[k] * wrow[k];
-                    gu[n] = acc;
-                } else {
-                    float acc = 0.0f;
-                    for (int k = 0; k < H; ++k) {
-                        float prod = (float)xdq[k] * (float)wrow[k];
-                        acc = acc + prod;
-                    }
-                    gu[n] = (double)acc;
-                }
-            }
-            /* step 4: SwiGLU h = silu(gate) * up, silu(g) = g / (1 + exp(-g)) */
-            for (int i = 0; i < I; ++i) {
-                if (acc_double) {
-                    double g = gu[i], u = gu[I + i];
-                    hbuf[i] = g / (1.0 + exp(-g)) * u;
-                } else {
-                    float g = (float)gu[i], u = (float)gu[I + i];
-                    float s = g / (1.0f + expf(-g));
-                    hbuf[i] = (double)(s * u);
-                }
-            }
-            /* step 5: requantise h along I in 1x32 blocks */
-            mx_quantize_rows_d(hbuf, 1, I, fmt, ha, hs);
+            /* steps 3-5: GEMM1, SwiGLU, requantisation */
+            gemm1_swiglu_requant(xdq, slab, H, I, fmt, w13, w13s, acc_double, &s, ha, hs);
             if (a2_codes)
                 memcpy(a2_codes + a * a2_row, ha, (size_t)a2_row);
             if (a2_scales)
                 memcpy(a2_scales + a * (long)(I / 32), hs, (size_t)I / 32);
-            dequant_row(ha, hs, I, fmt, hdq);
-            /* step 6: GEMM2 and the weighted FP32 combine in slot order */
-            for (int hh = 0; hh < H; ++hh) {
-                long row = slab * H + hh;
-                dequant_row(w2 + row * (I / 2), w2s + row * (I / 32), I, FMT_E2M1, wrow);
-                if (acc_double) {
-                    double acc = 0.0;
-                    for (int i = 0; i < I; ++i)
-                        acc += hdq[i] * wrow[i];
-                    cd[hh] += (double)wj * acc;
-                } else {
-                    float acc = 0.0f;
-                    for (int i = 0; i < I; ++i) {
-                        float prod = (float)hdq[i] * (float)wrow[i];
-                        acc = acc + prod;
-                    }
-                    trow[hh] = wj * acc;
-                }
-            }
-            if (!acc_double) {
-                /* the row's transport to the combine, then the FP32 slot-order sum */
-                if (combine == 1) {
-                    for (int hh = 0; hh < H; ++hh)
-                        trow[hh] = bf16_to_float(float_to_bf16(trow[hh]));
-                } else if (combine == 2) {
-                    for (int hh = 0; hh < H; ++hh)
-                        tdq[hh] = (double)trow[hh];
-                    mx_quantize_rows_d(tdq, 1, H, FMT_E4M3, tq, ts);
-                    dequant_row(tq, ts, H, FMT_E4M3, tdq);
-                    for (int hh = 0; hh < H; ++hh)
-                        trow[hh] = (float)tdq[hh];
-                }
+            dequant_row(ha, hs, I, fmt, s.hdq);
+            /* step 6: the weighted GEMM2 row, its transport, the FP32 slot-order sum */
+            gemm2_weighted(s.hdq, slab, H, I, w2, w2s, wts[a], acc_double, &s, trow, trow_d);
+            if (acc_double) {
+                for (int hh = 0; hh < H; ++hh)
+                    cd[hh] += trow_d[hh];
+            } else {
+                transport_row(trow, H, combine, &s);
                 for (int hh = 0; hh < H; ++hh)
                     cf[hh] = cf[hh] + trow[hh];
             }
@@ -512,7 +591,82 @@ void oracle_forward(const uint16_t *x, const float *logits, int T, int H, int I,
             y[(long)t * H + hh] = float_to_bf16(c);
         }
     }
-    free(ids); free(wts); free(xa); free(xs); free(xdq); free(wrow); free(gu);
-    free(hbuf); free(ha); free(hs); free(hdq); free(cf); free(cd);
-    free(trow); free(tdq); free(tq); free(ts);
+    free(ids); free(wts); free(xa); free(xs); free(xdq); free(ha); free(hs);
+    free(cf); free(cd); free(trow); free(trow_d);
+    scratch_free(&s);
+}
+
+/* ------------------------------------------------------------------ */
+/* The steps on their own (FP32 evaluation), for checking a device's    */
+/* intermediate results: each is the step oracle_forward runs, applied  */
+/* to rows the caller gives.                                            */
+/* ------------------------------------------------------------------ */
+
+/* Steps 3-5 for n assignments: row r of a1c/a1s is the quantised token row
+ * of assignment r (H or H/2 code bytes, H/32 scales), slab[r] its expert's
+ * weight slab; writes A2 row r (I or I/2 code bytes, I/32 scales). */
+void oracle_gemm1_rows(const uint8_t *a1c, const uint8_t *a1s, long n, int H, int I, int fmt,
+                       const int32_t *slab, const uint8_t *w13, const uint8_t *w13s,
+                       uint8_t *a2c, uint8_t *a2s)
+{
+    long a1_row = (fmt == FMT_E4M3) ? H : H / 2;
+    long a2_row = (fmt == FMT_E4M3) ? I : I / 2;
+    double *xdq = (double *)malloc(sizeof(double) * (size_t)H);
+    scratch_rows s = scratch_alloc(H, I);
+    init_tables();
+    for (long r = 0; r < n; ++r) {
+        dequant_row(a1c + r * a1_row, a1s + r * (long)(H / 32), H, fmt, xdq);
+        gemm1_swiglu_requant(xdq, (long)slab[r], H, I, fmt, w13, w13s, 0, &s,
+                             a2c + r * a2_row, a2s + r * (long)(I / 32));
+    }
+    free(xdq);
+    scratch_free(&s);
+}
+
+/* Step 6 before the transport for n assignments: row r of a2c/a2s is an A2
+ * row, slab[r] its expert's weight slab, wts[r] its routing weight; writes
+ * the weighted FP32 row r of rows [n][H]. */
+void oracle_gemm2_rows(const uint8_t *a2c, const uint8_t *a2s, long n, int H, int I, int fmt,
+                       const int32_t *slab, const float *wts, const uint8_t *w2,
+                       const uint8_t *w2s, float *rows)
+{
+    long a2_row = (fmt == FMT_E4M3) ? I : I / 2;
+    scratch_rows s = scratch_alloc(H, I);
+    init_tables();
+    for (long r = 0; r < n; ++r) {
+        dequant_row(a2c + r * a2_row, a2s + r * (long)(I / 32), I, fmt, s.hdq);
+        gemm2_weighted(s.hdq, (long)slab[r], H, I, w2, w2s, wts[r], 0, &s, rows + r * (long)H,
+                       NULL);
+    }
+    scratch_free(&s);
+}
+
+/* The rest of step 6 and step 7 for T tokens: rows [T*top_k][H] are the
+ * weighted FP32 rows by assignment a = t*top_k + j; each is transported
+ * (transport_row) and added in slot order j = 0..top_k-1 in FP32, then
+ * rounded to BF16.  y [T][H] bf16, y_f32 optional [T][H]. */
+void oracle_combine(const float *rows, long T, int top_k, int H, int combine, uint16_t *y,
+                    float *y_f32)
+{
+    float *cf = (float *)malloc(sizeof(float) * (size_t)H);
+    float *trow = (float *)malloc(sizeof(float) * (size_t)H);
+    scratch_rows s = scratch_alloc(H, 32);
+    init_tables();
+    for (long t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h)
+            cf[h] = 0.0f;
+        for (int j = 0; j < top_k; ++j) {
+            memcpy(trow, rows + (t * top_k + j) * (long)H, sizeof(float) * (size_t)H);
+            transport_row(trow, H, combine, &s);
+            for (int h = 0; h < H; ++h)
+                cf[h] = cf[h] + trow[h];
+        }
+        for (int h = 0; h < H; ++h) {
+            if (y_f32)
+                y_f32[t * H + h] = cf[h];
+            y[t * H + h] = float_to_bf16(cf[h]);
+        }
+    }
+    free(cf); free(trow);
+    scratch_free(&s);
 }

@@ -11,7 +11,12 @@
   about) destroys the output;
 * the error against an unquantised FP32 evaluation sits in the bands the
   pages report (A8W4 a few percent, A4W4 around ten percent);
-* the FP32 evaluation stays within a small bound of the double evaluation.
+* the FP32 evaluation stays within a small bound of the double evaluation;
+* the per-step entry points (GEMM1 rows, GEMM2 rows, combine) compose to the
+  whole-layer evaluation bit for bit;
+* the compressed combine transports round each top-k term on its own (a
+  closed form at top_k = 2 with distinct identity experts);
+* E4M3 codes 0x7F / 0xFF decode to NaN (OCP E4M3FN).
 """
 import numpy as np
 import pytest
@@ -287,3 +292,99 @@ def test_combine_transport_error_bounds():
     d8 = np.abs(f8.astype(np.float64) - f32)
     assert np.all(d8 <= 2.0 ** -3 * blk * 1.001 + slack)
     assert d8.max() > db.max()  # coarser than BF16
+
+
+# ---- the per-step entry points and the per-term placement of the transport ----
+
+@pytest.mark.parametrize("fmt", [E4M3, E2M1])
+def test_steps_compose_to_forward(fmt):
+    """oracle_gemm1_rows -> oracle_gemm2_rows -> oracle_combine, fed the
+    quantised token rows and the routing, reproduce oracle_forward bit for bit
+    (A2 bytes, the FP32 combine and y) for every transport, so every pin of
+    oracle_forward also pins the per-step entry points."""
+    x, lg, w13, w13s, w2, w2s, k = _small_case(T=10, k=3, seed=31)
+    T = x.shape[0]
+    ids, w = oracle.route(lg, k)
+    xc, xs = oracle.mx_quantize_bf16(x, fmt)
+    tok = np.repeat(np.arange(T), k)  # assignment a = t*k + j belongs to token t
+    a2c, a2s = oracle.gemm1_rows(xc[tok], xs[tok], ids.reshape(-1), w13, w13s, fmt)
+    rows = oracle.gemm2_rows(a2c, a2s, ids.reshape(-1), w.reshape(-1), w2, w2s, fmt)
+    for mode in (oracle.COMBINE_FP32, oracle.COMBINE_BF16, oracle.COMBINE_FP8):
+        y, yf, rc, rs = oracle.forward(x, lg, w13, w13s, w2, w2s, k, fmt, want_f32=True,
+                                       want_a2=True, combine=mode)
+        assert np.array_equal(rc, a2c) and np.array_equal(rs, a2s)
+        y2, yf2 = oracle.combine(rows, k, mode, want_f32=True)
+        assert np.array_equal(yf2, yf) and np.array_equal(y2, y)
+
+
+def _bf16_round(f32):
+    """Nearest-even BF16 of float32 values, by torch's cast (independent of the oracle)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(f32, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E2M1])
+def test_combine_transport_rounds_each_term(fmt):
+    """top_k = 2 with distinct identity experts: GEMM2 row j of a token is
+    exactly o_j[h] = xq[t, c_j(tau_j(h))] (one non-zero product), so the
+    weighted term is the single FP32 product w_j * o_j[h].  The pages' combine
+    payload (BF16, or MXFP8 1x32 blockwise) is a property of each row sent to
+    the combine, so each term is rounded (or quantised along H) on its own and
+    the rounded terms are summed in FP32 in slot order.  The closed form
+    below (numpy FP32 products and sums, torch's BF16 cast, the brute-force
+    MX quantiser) must equal the oracle bit for bit, and must differ from the
+    reading that rounds the FP32 sum instead."""
+    H, I, E, T, k = 256, 128, 8, 16, 2
+    w13, w13s, w2, w2s, cmap, tau = identity_experts(H, I, E, 41)
+    x, lg = identity_inputs(T, H, E, 42)
+    ids, w = oracle.route(lg, k)
+    xc, xX = mxref.quantize(mxref.bf16_to_f64(x), fmt)
+    xd = mxref.dequantize(xc, xX, fmt).astype(np.float32)
+    terms = np.zeros((T, k, H), np.float32)
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            o = np.zeros(H, np.float32)
+            o[:I] = xd[t, cmap[e, tau[e]]]
+            terms[t, j] = np.float32(w[t, j]) * o
+    assert np.all(ids[:, 0] != ids[:, 1])
+
+    def slot_sum(tt):
+        acc = np.zeros((T, H), np.float32)
+        for j in range(k):
+            acc = acc + tt[:, j]
+        return acc
+
+    for mode in (oracle.COMBINE_BF16, oracle.COMBINE_FP8):
+        if mode == oracle.COMBINE_BF16:
+            sent = _bf16_round(terms)
+        else:
+            c, X = mxref.quantize(terms.reshape(T * k, H).astype(np.float64), E4M3)
+            sent = mxref.dequantize(c, X, E4M3).astype(np.float32).reshape(T, k, H)
+        want = slot_sum(sent)
+        y, yf = oracle.forward(x, lg, w13, w13s, w2, w2s, k, fmt, want_f32=True, combine=mode)
+        assert np.array_equal(yf, want), mode
+        assert np.array_equal(mxref.bf16_to_f64(y), _bf16_round(want).astype(np.float64))
+        # rounding the sum instead of each term gives other values
+        raw = slot_sum(terms)
+        if mode == oracle.COMBINE_BF16:
+            alt = _bf16_round(raw)
+        else:
+            c, X = mxref.quantize(raw.astype(np.float64), E4M3)
+            alt = mxref.dequantize(c, X, E4M3).astype(np.float32)
+        assert (alt != want).mean() > 0.01, mode
+
+
+def test_e4m3_nan_codes_decode_to_nan():
+    """OCP E4M3FN has no infinities; the all-ones magnitude (0x7F and 0xFF) is
+    NaN.  The oracle decodes it as NaN (the quantiser never emits it), and it
+    poisons only the elements that depend on it."""
+    assert np.isnan(oracle.code_value(E4M3, 0x7F)) and np.isnan(oracle.code_value(E4M3, 0xFF))
+    assert oracle.code_value(E4M3, 0x7E) == 448.0 and oracle.code_value(E4M3, 0xFE) == -448.0
+    codes = np.full((1, 64), 0x38, np.uint8)  # 1.0
+    codes[0, 5] = 0x7F
+    codes[0, 40] = 0xFF
+    scales = np.full((1, 2), 127, np.uint8)
+    d = oracle.mx_dequantize(codes, scales, 64, E4M3)
+    nan = np.isnan(d[0])
+    assert nan[5] and nan[40] and nan.sum() == 2 and np.all(d[0][~nan] == 1.0)
