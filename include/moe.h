@@ -151,7 +151,10 @@ size_t moe_workspace_bytes(moe_layer_t layer, int T, int top_k, moe_act_dtype ac
  * Only enqueues kernels on s: no allocation, no host synchronisation and no
  * memcpy, so the call can be captured into a HIP graph.  T == 0 is a no-op.
  * Calls sharing a workspace must be ordered (same stream); different
- * workspaces may run concurrently against one handle.
+ * workspaces may run concurrently against one handle, except that a call
+ * running the fused plan (MOE_PLAN_FUSED, opt-in) needs the device's compute
+ * units to itself: beside other long-running work its bounded waits can give
+ * up, which moe_fused_status reports.
  */
 moe_status moe_forward(moe_layer_t layer, const void *x, const float *logits, int T, int top_k,
                        moe_act_dtype act, void *y, void *ws, size_t ws_bytes, hipStream_t s);
@@ -186,11 +189,26 @@ moe_status moe_forward_ex(moe_layer_t layer, const void *x, const float *logits,
  * in the layout moe_quant_act writes, so moe_quant_act followed by this call
  * gives exactly moe_forward_ex's output.  The buffers are read, never
  * written; the workspace is the one moe_forward takes (its activation-code
- * region is left unused).  Errors as for moe_forward_ex. */
+ * region is left unused).  Errors as for moe_forward_ex.  E4M3 codes 0x7F and
+ * 0xFF are NaN in OCP E4M3FN (moe_quant_act never writes them): they are not
+ * valid input, and the output rows of a token holding one are unspecified
+ * (NaN propagates through that token's experts). */
 moe_status moe_forward_prequant(moe_layer_t layer, const uint8_t *x_codes, const uint8_t *x_scales,
                                 const float *logits, int T, int top_k, moe_act_dtype act,
                                 uint32_t flags, void *y, void *ws, size_t ws_bytes,
                                 hipStream_t s);
+
+/* Whether a forward call on workspace ws (for T, top_k, act) had a wait of
+ * the fused plan give up (MOE_PLAN_FUSED: a GEMM2 work item waits, with a
+ * bound, for the GEMM1 items of its rows; past the bound it goes on with
+ * whatever rows it reads, so that call's output is unreliable).  Every
+ * forward call clears the flag in its routing launch, so read it after the
+ * call and before the next call on the same workspace.  Waits for stream s,
+ * copies the flag to *gave_up (host): 0 = no wait gave up (always so for the
+ * stream and tiled plans), 1 = at least one did.  Not graph-capturable (it
+ * synchronises). */
+moe_status moe_fused_status(moe_layer_t layer, const void *ws, int T, int top_k,
+                            moe_act_dtype act, hipStream_t s, int32_t *gave_up);
 
 /* Regions of the forward workspace, for inspection after a call (all device
  * pointers into ws; layouts as listed). */
@@ -267,9 +285,11 @@ typedef enum {
                             MegaMoE"); a GEMM2 item waits on a device-side count
                             for its 16 rows' SwiGLU activations.  The launch
                             sizes its grid to the workgroups the device holds at
-                            once; work on other streams that keeps CUs busy for
-                            seconds can make its bounded waits give up (wrong
-                            output).  Opt-in: never the built-in choice */
+                            once; work on other streams (or another fused call)
+                            that keeps CUs busy for seconds can make its bounded
+                            waits give up, and then the call's output is wrong:
+                            moe_fused_status reports it.  Opt-in: never the
+                            built-in choice, nor the tuner's unless asked */
 } moe_plan_variant;
 
 typedef struct {

@@ -44,7 +44,7 @@ EXPORTS = ("moe_prepare_weights", "moe_destroy", "moe_workspace_bytes", "moe_for
            "moe_pack_weights", "moe_create_layer", "moe_bind_weights",
            "moe_workspace_offsets", "moe_route", "moe_sort_workspace_bytes", "moe_sort",
            "moe_quant_act", "moe_set_plans", "moe_get_plan", "moe_profile_enable",
-           "moe_profile_read", "moe_status_str", "moe_last_error")
+           "moe_profile_read", "moe_status_str", "moe_last_error", "moe_fused_status")
 
 MOE_COMBINE_FP32 = 0  # transport of the weighted GEMM2 rows into the FP32 top-k sum
 MOE_COMBINE_BF16 = 1
@@ -98,6 +98,7 @@ def load_library(path: str = LIB_PATH):
         lib.moe_create_layer.argtypes = [I, I, I, ctypes.POINTER(P)]
         lib.moe_bind_weights.argtypes = [P, P]
         lib.moe_workspace_offsets.argtypes = [P, I, I, I, P]
+        lib.moe_fused_status.argtypes = [P, P, I, I, I, P, P]
         lib.moe_route.argtypes = [P, I, I, I, P, P, P]
         lib.moe_sort_workspace_bytes.argtypes = [I, I, I]
         lib.moe_sort_workspace_bytes.restype = Z
@@ -113,7 +114,8 @@ def load_library(path: str = LIB_PATH):
         lib.moe_last_error.restype = ctypes.c_char_p
         for name in ("moe_prepare_weights", "moe_forward", "moe_forward_ex",
                      "moe_forward_prequant", "moe_packed_weight_bytes", "moe_pack_weights",
-                     "moe_create_layer", "moe_bind_weights", "moe_workspace_offsets", "moe_route",
+                     "moe_create_layer", "moe_bind_weights", "moe_workspace_offsets",
+                     "moe_fused_status", "moe_route",
                      "moe_sort", "moe_quant_act", "moe_set_plans", "moe_get_plan",
                      "moe_profile_enable", "moe_profile_read"):
             getattr(lib, name).restype = I
@@ -289,6 +291,15 @@ def moe_forward_prequant(layer: MoeLayer, codes, scales, logits, top_k: int, act
                                     top_k, act, combine, _ptr(y), _ptr(ws), ws.numel(),
                                     _stream(stream)))
     return y
+
+
+def moe_fused_status(layer: MoeLayer, ws, T: int, top_k: int, act: int, stream=None) -> int:
+    """1 if a bounded wait of the fused plan gave up in the last forward call on
+    workspace ws (that call's output is unreliable), else 0.  Synchronises."""
+    out = ctypes.c_int32()
+    _check(load_library().moe_fused_status(layer.handle, _ptr(ws), T, top_k, act,
+                                           _stream(stream), ctypes.byref(out)))
+    return out.value
 
 
 def moe_workspace_offsets(layer: MoeLayer, T: int, top_k: int, act: int):

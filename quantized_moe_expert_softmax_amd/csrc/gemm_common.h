@@ -75,11 +75,13 @@ __device__ __forceinline__ v4f mfma_q(int q, v8i a, v8i b, v4f c, int sa, int sb
   }
 }
 
-// silu(g) = g / (1 + exp(-g)) with the hardware exp2 and reciprocal; for very
+// silu(g) = g / (1 + exp(-g)) in FP32 with the library exponential (about one
+// ulp) and a correctly rounded division, so h tracks an FP32 evaluation of
+// the same formula to an ulp or two (the hardware exp2 of -g * log2(e) and an
+// approximate reciprocal were several ulps off for |g| of a few units, which
+// moved requantised A2 codes across rounding boundaries more often); for very
 // negative g the exponential overflows to inf and silu goes to (-)0.
-__device__ __forceinline__ float silu(float g) {
-  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-}
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // Cross-lane moves within 16-lane rows (DPP, no LDS traffic).
 template <int CTRL>

@@ -352,7 +352,9 @@ static moe_status forward_impl(moe_layer_t L, bool prequant, const void *x, cons
   g.combine = (int)flags;
   // the fused launch's counters, zeroed by the route/sort launch before it
   g.sync = reinterpret_cast<int32_t *>(base + W.sync);
-  const int nsync = g.plan.fused ? (int)(kSyncHead + g.max_mtiles) : 0;
+  // the routing launch clears the give-up flag on every call (moe_fused_status
+  // reads it) and, for the fused plan, its per-m-tile counts
+  const int nsync = g.plan.fused ? (int)(kSyncHead + g.max_mtiles) : kSyncHead;
 
   const bool prof = L->profiling && L->prof_calls < L->prof_max;
   hipEvent_t *ev = prof ? &L->events[(size_t)L->prof_calls * (MOE_K_NUM + 1)] : nullptr;
@@ -432,6 +434,23 @@ moe_status moe_forward_prequant(moe_layer_t L, const uint8_t *x_codes, const uin
                                 hipStream_t s) {
   return forward_impl(L, true, nullptr, x_codes, x_scales, logits, T, top_k, act, flags, y, ws,
                       ws_bytes, s);
+}
+
+moe_status moe_fused_status(moe_layer_t L, const void *ws, int T, int top_k, moe_act_dtype act,
+                            hipStream_t s, int32_t *gave_up) {
+  moe_status st = check_call(L, T, top_k, act);
+  if (st != MOE_OK) return st;
+  if (!ws || !gave_up) return fail(MOE_ERR_INVALID_ARG, "null pointer");
+  *gave_up = 0;
+  if (T == 0) return MOE_OK;  // a T = 0 call launches nothing
+  const WsLayout W = ws_layout(T, top_k, L->E, L->H, L->I, act);
+  int32_t flag = 0;
+  hipError_t e = hipMemcpyAsync(&flag, static_cast<const uint8_t *>(ws) + W.sync, sizeof flag,
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "moe_fused_status");
+  *gave_up = flag != 0;
+  return MOE_OK;
 }
 
 moe_status moe_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w,

@@ -25,9 +25,13 @@ from . import (MOE_PLAN_FUSED, MOE_PLAN_STREAM, MOE_PLAN_TILED,
 _NAMES = {MOE_PLAN_STREAM: "stream", MOE_PLAN_TILED: "tiled", MOE_PLAN_FUSED: "fused"}
 
 
-def candidates(act: int):
-    rows = (32, 64, 96, 128, 160, 192)  # both activation formats
-    return [(MOE_PLAN_STREAM, 16), (MOE_PLAN_FUSED, 16)] + [(MOE_PLAN_TILED, r) for r in rows]
+def candidates(act: int, include_fused: bool = False):
+    """Plans to time: the stream plan and every tiled tile height (both
+    activation formats); the fused single launch only when the caller opts in
+    (its bounded waits rely on having the device to itself)."""
+    rows = (32, 64, 96, 128, 160, 192)
+    fused = [(MOE_PLAN_FUSED, 16)] if include_fused else []
+    return [(MOE_PLAN_STREAM, 16)] + fused + [(MOE_PLAN_TILED, r) for r in rows]
 
 
 def _time(layer, x, lgs, top_k, act, y, ws, steps, warmup):
@@ -43,9 +47,10 @@ def _time(layer, x, lgs, top_k, act, y, ws, steps, warmup):
 
 
 def tune(layer, inputs, top_k: int, act: int, steps: int = 10, warmup: int = 3,
-         margin: float = 0.03, log=None):
+         margin: float = 0.03, log=None, include_fused: bool = False):
     """inputs: {T: (x [T, H] bf16 device tensor, [logits [T, E] fp32 device tensors])}.
-    Returns (table, report); the table is also installed on the layer."""
+    Returns (table, report); the table is also installed on the layer.
+    include_fused: also time MOE_PLAN_FUSED (opt-in; see moe.h)."""
     import torch
     table, report = [], {}
     for T in sorted(inputs):
@@ -55,7 +60,7 @@ def tune(layer, inputs, top_k: int, act: int, steps: int = 10, warmup: int = 3,
         moe_set_plans(layer, [])
         builtin = moe_get_plan(layer, T, top_k, act)
         times = {}
-        for variant, rows in candidates(act):
+        for variant, rows in candidates(act, include_fused):
             moe_set_plans(layer, [dict(act=act, top_k=top_k, t_max=T, variant=variant, rows=rows)])
             times[(variant, rows)] = _time(layer, x, lgs, top_k, act, y, ws, steps, warmup)
         best = min(times, key=times.get)
@@ -80,6 +85,8 @@ def main():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--out", default=None, help="write the table as JSON")
+    p.add_argument("--include-fused", action="store_true",
+                   help="also time the fused single launch (needs the device to itself)")
     a = p.parse_args()
     import torch
     from . import moe_prepare_weights, synth
@@ -93,7 +100,8 @@ def main():
         x = torch.from_numpy(wl.x(T).view("int16")).cuda().view(torch.bfloat16)
         inputs[T] = (x, [torch.from_numpy(wl.logits(T, r)).cuda() for r in range(4)])
     table, report = tune(layer, inputs, wl.top_k, act, a.steps, a.warmup,
-                         log=lambda s: print(s, file=sys.stderr, flush=True))
+                         log=lambda s: print(s, file=sys.stderr, flush=True),
+                         include_fused=a.include_fused)
     out = {"workload": a.workload, "act": act, "plans": table, "report": report}
     if a.out:
         with open(a.out, "w") as fh:

@@ -11,8 +11,8 @@ import oracle
 import quantized_moe_expert_softmax_amd as moe
 from quantized_moe_expert_softmax_amd import synth
 from tests import test_oracle_layer as ol
-from tests.gpu_util import (ROUTE_ULP_TOL, assert_output_close, bf16_dev, bf16_host_bits, dev,
-                            host, ulp_diff, unpack_fp4, ws_view)
+from tests.gpu_util import assert_output_close, bf16_dev, bf16_host_bits, dev
+from tests.layer_check import check_front, check_tokens, forward_and_check
 
 pytestmark = pytest.mark.gpu
 
@@ -32,39 +32,14 @@ def _run(layer, x, lg, k, act, combine=moe.MOE_COMBINE_FP32):
     return bf16_host_bits(y), ws
 
 
-def _check_workspace(layer, ws, x, lg, k, act, ref_a2=None):
-    T, H = x.shape
-    E, I = layer.E, layer.I
-    N = T * k
-    offs = moe.moe_workspace_offsets(layer, T, k, act)
-    rid, rw = oracle.route(lg, k)
-    assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_IDS, N * 4, np.int32), rid.reshape(-1))
-    w = ws_view(ws, offs, moe.MOE_WS_WEIGHTS, N * 4, np.float32)
-    assert ulp_diff(w, rw.reshape(-1)).max() <= ROUTE_ULP_TOL
-    rc, ro, rp = oracle.sort(rid, E)
-    assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_COUNTS, E * 4, np.int32), rc)
-    assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_OFFSETS, (E + 1) * 4, np.int32), ro)
-    perm = ws_view(ws, offs, moe.MOE_WS_PERM, N * 4, np.int32)
-    assert np.array_equal(perm, rp)
-    slot = ws_view(ws, offs, moe.MOE_WS_SLOT, N * 4, np.int32)
-    assert np.array_equal(slot[rp], np.arange(N))
-    a1row = H if act == 0 else H // 2
-    xc, xs = oracle.mx_quantize_bf16(x, act)
-    assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_A1_CODES, T * a1row).reshape(T, a1row), xc)
-    assert np.array_equal(ws_view(ws, offs, moe.MOE_WS_A1_SCALES, T * (H // 32)).reshape(T, -1), xs)
-    if ref_a2 is None:
-        return None
-    # A2 diagnostic: GPU row p holds assignment perm[p]
-    a2row = I if act == 0 else I // 2
-    g_c = ws_view(ws, offs, moe.MOE_WS_A2_CODES, N * a2row).reshape(N, a2row)
-    g_s = ws_view(ws, offs, moe.MOE_WS_A2_SCALES, N * (I // 32)).reshape(N, I // 32)
-    r_c, r_s = ref_a2
-    r_c, r_s = r_c[perm], r_s[perm]
-    if act == 1:
-        g_c, r_c = unpack_fp4(g_c), unpack_fp4(r_c)
-    mism = (g_c != r_c).mean()
-    smism = (g_s != r_s).mean()
-    return mism, smism
+def host_weights(w):
+    """weights_for(e) of a host expert set (w13, w13s, w2, w2s stacked by expert)."""
+    return lambda e: tuple(a[e] for a in w)
+
+
+def _check_workspace(layer, ws, x, lg, k, act):
+    """Bit-exact first-stage checks on every token (see tests/layer_check.py)."""
+    return check_front(layer, ws, x, lg, k, act)
 
 
 def _small(T, H, I, E, k, seed):
@@ -94,16 +69,14 @@ CASES = [
 @pytest.mark.parametrize("act", [0, 1])
 @pytest.mark.parametrize("T,H,I,E,k", CASES)
 def test_forward_small(T, H, I, E, k, act):
+    """Every token: ids / perm / A1 bit-exact, A2 a valid neighbour of the
+    oracle's, GEMM2 of the device A2 and the combine exact, y within the
+    layer's tolerances of the oracle."""
     w, x, lg = _small(T, H, I, E, k, seed=T + H + I + E + k)
     layer = _layer(*w)
-    y, ws = _run(layer, x, lg, k, act)
-    ref, a2c, a2s = oracle.forward(x, lg, *w, k, act, want_a2=True)
-    rel, row = assert_output_close(y, ref, "T=%d H=%d I=%d E=%d k=%d act=%d" % (T, H, I, E, k, act))
-    mism, smism = _check_workspace(layer, ws, x, lg, k, act, (a2c, a2s))
-    # diagnostic: SwiGLU requantisation may flip a code at a rounding boundary
-    assert mism < 1e-2 and smism < 1e-2, (mism, smism)
-    print("T=%d H=%d I=%d E=%d k=%d act=%d rel=%.2e row=%.2e a2_code_mism=%.2e a2_scale_mism=%.2e"
-          % (T, H, I, E, k, act, rel, row, mism, smism))
+    what = "T=%d H=%d I=%d E=%d k=%d act=%d" % (T, H, I, E, k, act)
+    _, _, st = forward_and_check(layer, x, lg, k, act, host_weights(w), what=what)
+    print(what, st)
 
 
 @pytest.mark.parametrize("act", [0, 1])
@@ -190,10 +163,12 @@ def test_repeat_calls_agree():
                                                (130, 512, 640, 32, 8, 1)])
 def test_prequant_entry(T, H, I, E, k, combine, act):
     """The layer fed the oracle's MX codes and scales of x gives the BF16
-    entry's output bit for bit (the quantiser is exact), and the oracle's."""
+    entry's output bit for bit (the quantiser is exact), which passes the
+    whole check against the oracle."""
     w, x, lg = _small(T, H, I, E, k, seed=T + 11 * k)
     layer = _layer(*w)
-    y, _ = _run(layer, x, lg, k, act, combine)
+    y, _, _ = forward_and_check(layer, x, lg, k, act, host_weights(w), combine,
+                                what="prequant T=%d act=%d" % (T, act))
     xc, xs = oracle.mx_quantize_bf16(x, act)
     ws = moe.alloc_workspace(layer, T, k, act)
     ws.fill_(0xA5)
@@ -203,8 +178,6 @@ def test_prequant_entry(T, H, I, E, k, combine, act):
     torch.cuda.synchronize()
     yq = bf16_host_bits(yq)
     assert np.array_equal(yq, y)
-    ref = oracle.forward(x, lg, *w, k, act, combine=combine)
-    assert_output_close(yq, ref, "prequant T=%d act=%d" % (T, act))
 
 
 def test_graph_capture_replays():
@@ -234,18 +207,19 @@ def test_graph_capture_replays():
 @pytest.mark.parametrize("act", [0, 1])
 @pytest.mark.parametrize("T,H,I,E,k", [CASES[0], CASES[4], CASES[5], CASES[6]])
 def test_forward_combine_transports(T, H, I, E, k, act, combine):
-    """The compressed combine transports against the oracle's same transport;
-    the FP8 one must differ from the FP32 transport (it quantises)."""
+    """The compressed combine transports: staging rows are one BF16 rounding
+    (or a valid MXFP8 quantisation) of the oracle's GEMM2 of the device A2,
+    y is exactly their FP32 slot-order sum, and y is within the tolerances of
+    the oracle's same transport; the FP8 one must differ from the FP32
+    transport (it quantises)."""
     w, x, lg = _small(T, H, I, E, k, seed=T + H + I + E + k)
     layer = _layer(*w)
-    y, ws = _run(layer, x, lg, k, act, combine=combine)
-    ref = oracle.forward(x, lg, *w, k, act, combine=combine)
-    rel, row = assert_output_close(y, ref, "T=%d act=%d combine=%d" % (T, act, combine))
-    _check_workspace(layer, ws, x, lg, k, act)
+    what = "T=%d act=%d combine=%d" % (T, act, combine)
+    y, _, st = forward_and_check(layer, x, lg, k, act, host_weights(w), combine, what=what)
     if combine == moe.MOE_COMBINE_FP8:
         y32, _ = _run(layer, x, lg, k, act)
         assert not np.array_equal(y, y32)
-    print("T=%d act=%d combine=%d rel=%.2e row=%.2e" % (T, act, combine, rel, row))
+    print(what, st)
 
 
 def test_forward_rejects_unknown_flags():
