@@ -61,7 +61,7 @@ def _load():
         lib.oracle_sort.argtypes = [P, i32, i32, i32, P, P, P]
         lib.oracle_forward.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P, P, P, i32,
                                        i32, P, P, P, P, P]
-        lib.oracle_gemm1_rows.argtypes = [P, P, i64, i32, i32, i32, P, P, P, P, P]
+        lib.oracle_gemm1_rows.argtypes = [P, P, i64, i32, i32, i32, P, P, P, P, P, P]
         lib.oracle_gemm2_rows.argtypes = [P, P, i64, i32, i32, i32, P, P, P, P, P]
         lib.oracle_combine.argtypes = [P, i64, i32, i32, i32, P, P]
         for f in (lib.oracle_mx_quantize, lib.oracle_mx_quantize_bf16, lib.oracle_mx_dequantize,
@@ -233,13 +233,14 @@ def forward_rows(x_bits, logits, rows, weights_for, top_k: int, fmt: int,
 # ---- the layer's steps on their own (FP32 evaluation, as oracle_forward runs
 # them), for checking a device's intermediate results row by row ----
 
-def gemm1_rows(a1_codes, a1_scales, slab, w13, w13s, fmt: int):
+def gemm1_rows(a1_codes, a1_scales, slab, w13, w13s, fmt: int, want_gu: bool = False):
     """Steps 3-5 (GEMM1, SwiGLU, requantisation) on n given rows.
 
     a1_codes [n, H or H/2], a1_scales [n, H/32]: the quantised token row of
     each assignment; slab [n]: its expert's index into w13 [S, 2I, H/2] /
     w13s [S, 2I, H/32].  Returns the A2 rows (codes [n, I or I/2], scales
-    [n, I/32]).
+    [n, I/32]) and, when want_gu, the FP32 GEMM1 results [n, 2I] (gate
+    columns, then up columns) the SwiGLU read.
     """
     a1c = _c(a1_codes, np.uint8)
     a1s = _c(a1_scales, np.uint8)
@@ -253,9 +254,10 @@ def gemm1_rows(a1_codes, a1_scales, slab, w13, w13s, fmt: int):
     assert sl.size == 0 or (sl.min() >= 0 and sl.max() < w13.shape[0])
     a2c = np.zeros((n, code_bytes_per_row(I, fmt)), np.uint8)
     a2s = np.zeros((n, I // 32), np.uint8)
+    gu = np.zeros((n, 2 * I), np.float32) if want_gu else None
     _load().oracle_gemm1_rows(_ptr(a1c), _ptr(a1s), n, H, I, fmt, _ptr(sl), _ptr(w13), _ptr(w13s),
-                              _ptr(a2c), _ptr(a2s))
-    return a2c, a2s
+                              _ptr(a2c), _ptr(a2s), _ptr(gu))
+    return (a2c, a2s, gu) if want_gu else (a2c, a2s)
 
 
 def gemm2_rows(a2_codes, a2_scales, slab, wts, w2, w2s, fmt: int):

@@ -604,10 +604,12 @@ void oracle_forward(const uint16_t *x, const float *logits, int T, int H, int I,
 
 /* Steps 3-5 for n assignments: row r of a1c/a1s is the quantised token row
  * of assignment r (H or H/2 code bytes, H/32 scales), slab[r] its expert's
- * weight slab; writes A2 row r (I or I/2 code bytes, I/32 scales). */
+ * weight slab; writes A2 row r (I or I/2 code bytes, I/32 scales) and, when
+ * gu is given, the row's FP32 GEMM1 results [n][2I] (gate columns, then up
+ * columns) that the SwiGLU read. */
 void oracle_gemm1_rows(const uint8_t *a1c, const uint8_t *a1s, long n, int H, int I, int fmt,
                        const int32_t *slab, const uint8_t *w13, const uint8_t *w13s,
-                       uint8_t *a2c, uint8_t *a2s)
+                       uint8_t *a2c, uint8_t *a2s, float *gu)
 {
     long a1_row = (fmt == FMT_E4M3) ? H : H / 2;
     long a2_row = (fmt == FMT_E4M3) ? I : I / 2;
@@ -618,6 +620,9 @@ void oracle_gemm1_rows(const uint8_t *a1c, const uint8_t *a1s, long n, int H, in
         dequant_row(a1c + r * a1_row, a1s + r * (long)(H / 32), H, fmt, xdq);
         gemm1_swiglu_requant(xdq, (long)slab[r], H, I, fmt, w13, w13s, 0, &s,
                              a2c + r * a2_row, a2s + r * (long)(I / 32));
+        if (gu)
+            for (int c = 0; c < 2 * I; ++c)
+                gu[r * 2 * (long)I + c] = (float)s.gu[c];
     }
     free(xdq);
     scratch_free(&s);

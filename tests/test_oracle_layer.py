@@ -154,6 +154,40 @@ def identity_experts(H, I, E, seed):
             mxref.pack_fp4(w2c), (w2X + 127).astype(np.uint8), cmap, tau)
 
 
+def identity_experts_packed(H, I, E, seed):
+    """identity_experts built straight into the canonical packed bytes (the
+    same weights, without the [E, 2I, H] code arrays, for the large shapes)."""
+    assert H >= 32 + I
+    rng = np.random.default_rng(seed)
+    w13 = np.zeros((E, 2 * I, H // 2), np.uint8)
+    w13s = np.full((E, 2 * I, H // 32), 127, np.uint8)
+    w2 = np.zeros((E, H, I // 2), np.uint8)
+    w2s = np.full((E, H, I // 32), 127, np.uint8)
+    cmap = np.zeros((E, I), np.int64)
+    tau = np.zeros((E, I), np.int64)
+    rows = np.arange(I)
+    for e in range(E):
+        w13[e, :I, 0] = 0x6        # element 0 (low nibble): 4.0
+        w13s[e, :I, 0] = 127 + 3   # 4 * 2^3 = 32
+        pi = rng.permutation(I // 32)
+        for b in range(I // 32):
+            sig = rng.permutation(32)
+            cmap[e, 32 * b:32 * b + 32] = 32 + 32 * pi[b] + sig
+        c = cmap[e]
+        w13[e, I + rows, c // 2] = np.where(c % 2 == 1, 0x20, 0x02)  # 1.0 in c's nibble
+        tau[e] = rng.permutation(I)
+        w2[e, rows, tau[e] // 2] = np.where(tau[e] % 2 == 1, 0x20, 0x02)
+        w2s[e, :I, :] = 127 - 5
+    return w13, w13s, w2, w2s, cmap, tau
+
+
+def test_identity_packed_builder_matches():
+    a = identity_experts(384, 256, 3, 9)
+    b = identity_experts_packed(384, 256, 3, 9)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
 def identity_inputs(T, H, E, seed):
     rng = np.random.default_rng(seed)
     x = synth.tokens_bf16(T, H, seed)
@@ -307,7 +341,15 @@ def test_steps_compose_to_forward(fmt):
     ids, w = oracle.route(lg, k)
     xc, xs = oracle.mx_quantize_bf16(x, fmt)
     tok = np.repeat(np.arange(T), k)  # assignment a = t*k + j belongs to token t
-    a2c, a2s = oracle.gemm1_rows(xc[tok], xs[tok], ids.reshape(-1), w13, w13s, fmt)
+    a2c, a2s, gu = oracle.gemm1_rows(xc[tok], xs[tok], ids.reshape(-1), w13, w13s, fmt,
+                                     want_gu=True)
+    # the GEMM1 results it reports are the products of the token rows with the
+    # expert's gate and up rows (brute force in float64, the FP32 sum bound)
+    xd = mxref.dequantize(*mxref.quantize(mxref.bf16_to_f64(x), fmt), fmt)
+    W13 = mxref.dequant_weights(w13, w13s)
+    for a in range(T * k):
+        prods = W13[ids.reshape(-1)[a]] * xd[tok[a]][None, :]
+        assert np.all(np.abs(gu[a] - prods.sum(axis=1)) <= 256 * 2.0 ** -24 * np.abs(prods).sum(axis=1))
     rows = oracle.gemm2_rows(a2c, a2s, ids.reshape(-1), w.reshape(-1), w2, w2s, fmt)
     for mode in (oracle.COMBINE_FP32, oracle.COMBINE_BF16, oracle.COMBINE_FP8):
         y, yf, rc, rs = oracle.forward(x, lg, w13, w13s, w2, w2s, k, fmt, want_f32=True,
