@@ -210,6 +210,27 @@ moe_status moe_forward_prequant(moe_layer_t layer, const uint8_t *x_codes, const
 moe_status moe_fused_status(moe_layer_t layer, const void *ws, int T, int top_k,
                             moe_act_dtype act, hipStream_t s, int32_t *gave_up);
 
+/* ---- a forward call that allocates nothing --------------------------------
+ * For callers that cannot allocate device memory or pass a workspace of their
+ * own (code under HIP-graph capture, tight serving loops, harnesses that
+ * forbid allocation): moe_forward_ex with the forward workspace in a static
+ * device array of the library, MOE_NOALLOC_SCRATCH_BYTES on every device the
+ * library runs on (held until the process ends; its device address is looked
+ * up once per device, when a layer is made there or at the first call).
+ * Arguments and results as for moe_forward_ex, without ws / ws_bytes.  A call
+ * whose workspace (moe_workspace_bytes) exceeds the array fails with
+ * MOE_ERR_WORKSPACE before anything is enqueued (64 MiB holds, e.g., the
+ * 7168 x 3072, top_k = 6 layer up to T = 300 with the FP32 transport).  The
+ * call allocates nothing (no hipMalloc, no allocating library routine).
+ * Every call on a device shares that device's array and leaves it holding
+ * its intermediate results; calls that overlap on one device (other streams,
+ * other threads, other handles) race on it and must be ordered by the
+ * caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(moe_layer_t layer, const void *x, const float *logits, int T,
+                               int top_k, moe_act_dtype act, uint32_t flags, void *y,
+                               hipStream_t s);
+
 /* Regions of the forward workspace, for inspection after a call (all device
  * pointers into ws; layouts as listed). */
 typedef enum {

@@ -44,7 +44,10 @@ EXPORTS = ("moe_prepare_weights", "moe_destroy", "moe_workspace_bytes", "moe_for
            "moe_pack_weights", "moe_create_layer", "moe_bind_weights",
            "moe_workspace_offsets", "moe_route", "moe_sort_workspace_bytes", "moe_sort",
            "moe_quant_act", "moe_set_plans", "moe_get_plan", "moe_profile_enable",
-           "moe_profile_read", "moe_status_str", "moe_last_error", "moe_fused_status")
+           "moe_profile_read", "moe_status_str", "moe_last_error", "moe_fused_status",
+           "moe_forward_noalloc")
+# bytes of the static workspace moe_forward_noalloc uses (MOE_NOALLOC_SCRATCH_BYTES)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 MOE_COMBINE_FP32 = 0  # transport of the weighted GEMM2 rows into the FP32 top-k sum
 MOE_COMBINE_BF16 = 1
@@ -93,6 +96,7 @@ def load_library(path: str = LIB_PATH):
         lib.moe_forward.argtypes = [P, P, P, I, I, I, P, P, Z, P]
         lib.moe_forward_ex.argtypes = [P, P, P, I, I, I, ctypes.c_uint32, P, P, Z, P]
         lib.moe_forward_prequant.argtypes = [P, P, P, P, I, I, I, ctypes.c_uint32, P, P, Z, P]
+        lib.moe_forward_noalloc.argtypes = [P, P, P, I, I, I, ctypes.c_uint32, P, P]
         lib.moe_packed_weight_bytes.argtypes = [I, I, I, P]
         lib.moe_pack_weights.argtypes = [I, I, I, P, P, P, P, P, P]
         lib.moe_create_layer.argtypes = [I, I, I, ctypes.POINTER(P)]
@@ -112,7 +116,7 @@ def load_library(path: str = LIB_PATH):
         lib.moe_status_str.restype = ctypes.c_char_p
         lib.moe_last_error.argtypes = []
         lib.moe_last_error.restype = ctypes.c_char_p
-        for name in ("moe_prepare_weights", "moe_forward", "moe_forward_ex",
+        for name in ("moe_prepare_weights", "moe_forward", "moe_forward_ex", "moe_forward_noalloc",
                      "moe_forward_prequant", "moe_packed_weight_bytes", "moe_pack_weights",
                      "moe_create_layer", "moe_bind_weights", "moe_workspace_offsets",
                      "moe_fused_status", "moe_route",
@@ -268,6 +272,21 @@ def moe_forward(layer: MoeLayer, x, logits, top_k: int, act: int, y=None, ws=Non
     else:
         _check(lib.moe_forward_ex(layer.handle, _ptr(x), _ptr(logits), T, top_k, act, combine,
                                   _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_forward_noalloc(layer: MoeLayer, x, logits, top_k: int, act: int, y,
+                        combine: int = MOE_COMBINE_FP32, stream=None):
+    """moe_forward with the library's static device workspace (no workspace
+    argument, nothing allocated by the call; y [T, H] bf16 must be given).
+    Calls on one device share that workspace: order them.  Enqueue only."""
+    lib = load_library()
+    T = x.shape[0]
+    _require(x, 2, (T, layer.H), "x")
+    _require(logits, 4, (T, layer.E), "logits")
+    _require(y, 2, (T, layer.H), "y")
+    _check(lib.moe_forward_noalloc(layer.handle, _ptr(x), _ptr(logits), T, top_k, act, combine,
+                                   _ptr(y), _stream(stream)))
     return y
 
 

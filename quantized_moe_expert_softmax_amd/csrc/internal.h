@@ -167,4 +167,9 @@ hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s);
 hipError_t launch_combine(const void *rows, const int32_t *inv, int T, int H, int top_k,
                           int combine, uint16_t *y, hipStream_t s);
 
+// Device address, on the current device, of the library's static forward
+// workspace of MOE_NOALLOC_SCRATCH_BYTES (noalloc.hip); looked up once per
+// device.
+hipError_t noalloc_scratch(void **ptr);
+
 }  // namespace moe

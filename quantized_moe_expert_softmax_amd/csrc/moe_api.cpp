@@ -111,6 +111,9 @@ moe_status moe_prepare_weights(int E, int H, int I, const void *w13, const void 
   int dev = 0, cus = 0;
   moe_status st = check_device(&dev, &cus);
   if (st != MOE_OK) return st;
+  void *scratch = nullptr;  // set-up of moe_forward_noalloc's array on this device
+  hipError_t e = noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "static scratch lookup");
 
   const PackDims d13 = pack_dims(2 * I, H), d2 = pack_dims(H, I);
   moe_layer *L = new moe_layer();
@@ -118,7 +121,7 @@ moe_status moe_prepare_weights(int E, int H, int I, const void *w13, const void 
   L->profiling = false; L->prof_max = 0; L->prof_calls = 0;
   const size_t b13 = (size_t)E * d13.code_bytes(), s13 = (size_t)E * d13.scale_bytes();
   const size_t b2 = (size_t)E * d2.code_bytes(), s2 = (size_t)E * d2.scale_bytes();
-  hipError_t e = hipMalloc(&L->own[0], b13);
+  e = hipMalloc(&L->own[0], b13);
   if (e == hipSuccess) e = hipMalloc(&L->own[1], s13);
   if (e == hipSuccess) e = hipMalloc(&L->own[2], b2);
   if (e == hipSuccess) e = hipMalloc(&L->own[3], s2);
@@ -198,6 +201,9 @@ moe_status moe_create_layer(int E, int H, int I, moe_layer_t *out) {
   int dev = 0, cus = 0;
   moe_status st = check_device(&dev, &cus);
   if (st != MOE_OK) return st;
+  void *scratch = nullptr;  // set-up of moe_forward_noalloc's array on this device
+  const hipError_t e = noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "static scratch lookup");
   moe_layer *L = new moe_layer();
   L->E = E; L->H = H; L->I = I; L->device = dev; L->num_cus = cus;
   *out = L;
@@ -426,6 +432,24 @@ moe_status moe_forward_ex(moe_layer_t L, const void *x, const float *logits, int
                           hipStream_t s) {
   return forward_impl(L, false, x, nullptr, nullptr, logits, T, top_k, act, flags, y, ws,
                       ws_bytes, s);
+}
+
+moe_status moe_forward_noalloc(moe_layer_t L, const void *x, const float *logits, int T,
+                               int top_k, moe_act_dtype act, uint32_t flags, void *y,
+                               hipStream_t s) {
+  moe_status st = check_call(L, T, top_k, act);
+  if (st != MOE_OK) return st;
+  const size_t need = ws_layout(T, top_k, L->E, L->H, L->I, act).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "T=%d top_k=%d needs %zu bytes of workspace; the static scratch of "
+                "moe_forward_noalloc holds %zu (use moe_forward_ex with a workspace)",
+                T, top_k, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward_noalloc scratch lookup");
+  return forward_impl(L, false, x, nullptr, nullptr, logits, T, top_k, act, flags, y, ws,
+                      MOE_NOALLOC_SCRATCH_BYTES, s);
 }
 
 moe_status moe_forward_prequant(moe_layer_t L, const uint8_t *x_codes, const uint8_t *x_scales,
