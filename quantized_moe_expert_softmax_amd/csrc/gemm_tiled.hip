@@ -47,6 +47,21 @@ __device__ __forceinline__ void barrier_keep_copies() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
   __builtin_amdgcn_s_barrier();
 }
+// LDS position of the activation tile's 16-byte chunks: chunk c of tile row
+// `row` sits at position c ^ act_swizzle(row) of that row.  A wave reads one
+// chunk from each of 16 consecutive rows per 16-lane group (the MFMA operand
+// of lane group g), so those 16 chunks must fall in different 16-byte bank
+// groups of a 256-byte LDS line.  MXFP8 rows are 128 bytes (8 chunks): two
+// rows per line, the XOR with the row's low three bits spreads them.  MXFP4
+// rows are 64 bytes (4 chunks): four rows per line, rows r and r + 4, r + 8,
+// r + 12 share a line position, so the XOR takes bits 2-3 of the row.  (It
+// took bits 0-1 before, which vary with the line position itself: 29% of the
+// LDS cycles of the A4W4 GEMM1 were bank conflicts.)
+template <int FMT>
+__device__ __forceinline__ int act_swizzle(int row) {
+  return FMT == 0 ? (row & 7) : ((row >> 2) & 3);
+}
+
 // Epilogue of one weight quad u of a work item (output tiles 4u .. 4u+3 of
 // acc; tile0 the quad's first 16-row weight tile): GEMM1 SwiGLU + requant to
 // the A2 rows, GEMM2 weighted rows to the staging buffer.  A padded row
@@ -191,7 +206,7 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
   const uint8_t *__restrict__ As = SECOND ? p.a2s : p.a1s;
   const int G = gridDim.x;
   const int L = (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8);
-  const int swz = (FMT == 0) ? (r16 & 7) : (r16 & 3);
+  const int swz = act_swizzle<FMT>(r16);
   const int aoff_lo = r16 * ROWB + 16 * (g ^ swz);
   const int aoff_hi = r16 * ROWB + 16 * ((4 + g) ^ swz);
 
@@ -213,9 +228,24 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
   const int rh = PS::RS == 1 ? 0 : uniform(wave >> 2);  // its share of the copies and m-tiles
   constexpr int MTW = PS::MTW;
   const int total_i = (int)total;      // items fit 32 bits (m-blocks x n-blocks)
+  // Item wi of the list: the items of expert e are [NBLK mtoff[e], NBLK
+  // mtoff[e+1]), n-block major and m-block minor, so the m-blocks that read
+  // one weight panel are consecutive items: they run at the same time on
+  // neighbouring workgroups of one XCD (see L above), and all but the first
+  // find the panel in that XCD's L2.  (With the m-block-major order an
+  // expert's second m-block read its panels again from HBM, NBLK items later
+  // and usually on another XCD.)
+  auto coords = [&](int wi, int &ei, int &nbi, int &mbi) __attribute__((always_inline)) {
+    ei = uniform(p.mbexp[wi / NBLK]);
+    const int m0 = uniform(p.mtoff[ei]), nmb = uniform(p.mtoff[ei + 1]) - m0;
+    const int i = wi - NBLK * m0;
+    nbi = uniform(i / nmb);
+    mbi = uniform(i - nbi * nmb);
+  };
   auto quad_of = [&](int wi) __attribute__((always_inline)) {
-    const int ei = uniform(p.mbexp[wi / NBLK]);
-    const int ti = 16 * (wi % NBLK) + 4 * qd;  // quads past the last tile read quad 0
+    int ei, nbi, mbi;
+    coords(wi, ei, nbi, mbi);
+    const int ti = 16 * nbi + 4 * qd;  // quads past the last tile read quad 0
     return uniform(ei * (ntiles / 4) + (ti < ntiles ? ti / 4 : 0));
   };
   int cw = L;         // item of the next copy
@@ -265,9 +295,8 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
   }
 
   for (long w = L; w < total; w += G) {
-    const int gmb = (int)(w / NBLK), nb = (int)(w % NBLK);
-    const int e = uniform(p.mbexp[gmb]);
-    const int mb = gmb - uniform(p.mtoff[e]);
+    int e, nb, mb;
+    coords((int)w, e, nb, mb);
     const int row0 = uniform(p.offsets[e]) + BM * mb;
     const int nrows = min(BM, uniform(p.offsets[e + 1]) - row0);
 
@@ -287,7 +316,7 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
           const int rr = min(row, nrows - 1);
           const size_t ridx =
               SECOND ? (size_t)(row0 + rr) : (size_t)(p.perm[row0 + rr] / p.top_k);
-          csrc[c] = chunk ? A + ridx * arow + 16 * ((ci % CH) ^ (row & (CH - 1)))
+          csrc[c] = chunk ? A + ridx * arow + 16 * ((ci % CH) ^ act_swizzle<FMT>(row))
                           : As + ridx * srow;
         }
         auto issue_a = [&](int st) __attribute__((always_inline)) {
