@@ -300,7 +300,7 @@ moe_status moe_quant_act(const void *x, int T, int H, moe_act_dtype act, uint8_t
 typedef enum {
     MOE_PLAN_STREAM = 0, /* 16-row m-tiles, K split over the waves, weights to VGPRs */
     MOE_PLAN_TILED = 1,  /* BM-row m-blocks staged in LDS, 256 weight rows per item */
-    MOE_PLAN_FUSED = 2   /* the stream items of both GEMMs in one persistent launch
+    MOE_PLAN_FUSED = 2,  /* the stream items of both GEMMs in one persistent launch
                             (the pages' MegaMoE runs Stage1 and Stage2 as one
                             launch: "add A4W4 and FP8 P2P transport support to
                             MegaMoE"); a GEMM2 item waits on a device-side count
@@ -311,6 +311,14 @@ typedef enum {
                             waits give up, and then the call's output is wrong:
                             moe_fused_status reports it.  Opt-in: never the
                             built-in choice, nor the tuner's unless asked */
+    MOE_PLAN_DECODE = 3  /* the stream GEMM1, then GEMM2 token-major: a work item
+                            is (token, 64 output columns) over all its top_k
+                            experts, which sums the token's weighted rows in
+                            FP32 in slot order and writes y itself (no combine
+                            launch; "feat(moe): FlyDSL MegaMoE fused EP-MoE
+                            integration", summary: one fused operation).  With
+                            the BF16 or FP8 combine transport the call runs the
+                            stream plan instead */
 } moe_plan_variant;
 
 typedef struct {
@@ -319,8 +327,8 @@ typedef struct {
     int32_t t_max;   /* applies to calls with T <= t_max; the first matching entry
                         in table order is used                                    */
     int32_t variant; /* moe_plan_variant                                          */
-    int32_t rows;    /* token rows per work item: 16 for MOE_PLAN_STREAM and
-                        MOE_PLAN_FUSED; for
+    int32_t rows;    /* token rows per work item: 16 for MOE_PLAN_STREAM,
+                        MOE_PLAN_FUSED and MOE_PLAN_DECODE; for
                         MOE_PLAN_TILED 32, 64, 96, 128, 160 or 192 (both
                         activation formats)                                       */
 } moe_plan;

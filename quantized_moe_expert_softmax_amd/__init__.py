@@ -56,6 +56,7 @@ MOE_COMBINE_FP8 = 2
 MOE_PLAN_STREAM = 0
 MOE_PLAN_TILED = 1
 MOE_PLAN_FUSED = 2
+MOE_PLAN_DECODE = 3
 
 
 class MoePlan(ctypes.Structure):

@@ -455,9 +455,130 @@ __global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
   }
 }
 
+// Steps 1-3 for decode batches (T <= kFrontMaxT, so T * top_k <= 128): one
+// 256-thread workgroup routes every token (one wave per token), counts the
+// assignments per expert in LDS, turns the counts into offsets, m-block
+// prefixes and the m-block table with one wave-level scan per wave (each
+// thread owns four consecutive experts) and three barriers, and ranks each
+// assignment among the lower assignments of its expert (at most 127 LDS
+// compares); workgroups 1.. quantise the token rows.  The same outputs as the
+// separate kernels (and front_kernel), with far fewer block-wide steps than
+// front_kernel's 1024-wide scans, which the decode sizes do not need.
+template <int NV>
+__global__ __launch_bounds__(256) void front_small_kernel(FrontArgs p) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x > 0) {
+    const long nblocks = (long)p.T * (p.H / 32);
+    const long stride = (long)(gridDim.x - 1) * 256;
+    for (long b = (long)(blockIdx.x - 1) * 256 + tid; b < nblocks; b += stride) {
+      if (p.act == MOE_ACT_MXFP8_E4M3)
+        quant_block<E4M3>(p.x, b, p.codes, p.scales);
+      else
+        quant_block<E2M1>(p.x, b, p.codes, p.scales);
+    }
+    return;
+  }
+  __shared__ int32_t sid[kFrontMaxT * 8];
+  __shared__ float sw[kFrontMaxT * 8];
+  __shared__ int32_t base[1024];  // per expert: count, then first sorted row
+  __shared__ int32_t wsum[4][2];
+  const int wave = tid >> 6, lane = tid & 63;
+  const int T = p.T, E = p.E, k = p.top_k, N = T * k;
+  for (int i = tid; i < p.nsync; i += 256) p.sync[i] = 0;
+  for (int e = tid; e < E; e += 256) base[e] = 0;
+  // wave w routes tokens w, w + 4, ...
+  for (int t = wave; t < T; t += 4) {
+    float v[NV];
+    load_logits<NV>(p.logits + (long)t * E, E, lane, v);
+    route_values<NV>(v, E, k, lane, sid + t * k, sw + t * k);
+  }
+  __syncthreads();
+  for (int a = tid; a < N; a += 256) {
+    p.ids[a] = sid[a];
+    p.wts[a] = sw[a];
+    atomicAdd(&base[sid[a]], 1);
+  }
+  __syncthreads();
+  // exclusive prefix sums of the counts and of the m-blocks per expert
+  int c[4], m[4], lc = 0, lm = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * tid + i;
+    c[i] = e < E ? base[e] : 0;
+    m[i] = (c[i] + p.bm - 1) / p.bm;
+    lc += c[i];
+    lm += m[i];
+  }
+  int ic = lc, im = lm;  // inclusive scan over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int oc = __shfl_up(ic, d), om = __shfl_up(im, d);
+    if (lane >= d) {
+      ic += oc;
+      im += om;
+    }
+  }
+  if (lane == 63) {
+    wsum[wave][0] = ic;
+    wsum[wave][1] = im;
+  }
+  __syncthreads();
+  int oc = ic - lc, om = im - lm;
+  for (int w = 0; w < wave; ++w) {
+    oc += wsum[w][0];
+    om += wsum[w][1];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * tid + i;
+    if (e < E) {
+      p.counts[e] = c[i];
+      p.offsets[e] = oc;
+      p.mtoff[e] = om;
+      for (int j = 0; j < m[i]; ++j) p.mbexp[om + j] = e;
+      base[e] = oc;
+    }
+    oc += c[i];
+    om += m[i];
+  }
+  if (4 * tid <= E - 1 && E - 1 < 4 * tid + 4) {  // the owner of the last expert
+    p.offsets[E] = oc;
+    p.mtoff[E] = om;
+  }
+  __syncthreads();
+  // assignment a's row: its expert's first row plus the number of lower
+  // assignments of the same expert (ascending a within an expert)
+  for (int a = tid; a < N; a += 256) {
+    const int e = sid[a];
+    int r = 0;
+    for (int b = 0; b < a; ++b) r += sid[b] == e;
+    const int pos = base[e] + r;
+    p.perm[pos] = a;
+    p.inv[a] = pos;
+    p.wsorted[pos] = sw[a];
+  }
+}
+
 hipError_t launch_front(const FrontArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (a.T > kSortBlock || a.E > 1024 || a.top_k > 8) return hipErrorInvalidValue;
+  if (a.logits && a.T <= kFrontMaxT) {
+    const long nq = a.x ? ((long)a.T * (a.H / 32) + 255) / 256 : 0;
+    const dim3 grid((unsigned)(1 + nq)), block(256);
+#define FRONT_SMALL_CASE(NV_)                                 \
+  case NV_:                                                   \
+    front_small_kernel<NV_><<<grid, block, 0, s>>>(a);        \
+    break;
+    switch (ceil_div(a.E, 64)) {
+      FRONT_SMALL_CASE(1) FRONT_SMALL_CASE(2) FRONT_SMALL_CASE(3) FRONT_SMALL_CASE(4)
+      FRONT_SMALL_CASE(5) FRONT_SMALL_CASE(6) FRONT_SMALL_CASE(7) FRONT_SMALL_CASE(8)
+      FRONT_SMALL_CASE(9) FRONT_SMALL_CASE(10) FRONT_SMALL_CASE(11) FRONT_SMALL_CASE(12)
+      FRONT_SMALL_CASE(13) FRONT_SMALL_CASE(14) FRONT_SMALL_CASE(15) FRONT_SMALL_CASE(16)
+      default: return hipErrorInvalidValue;
+    }
+#undef FRONT_SMALL_CASE
+    return hipGetLastError();
+  }
   // no quantisation workgroups when the caller passes MX codes (x null)
   const long nq = a.x ? ((long)a.T * (a.H / 32) + 1023) / 1024 : 0;
   const dim3 grid((unsigned)(1 + nq)), block(1024);

@@ -58,6 +58,10 @@ struct KArgs {
   const uint8_t *w2p;
   const uint32_t *w2sp;
   int32_t *sync;
+  // token-major GEMM2 only: routing by assignment and the output
+  const int32_t *ids, *inv;
+  const float *wts_a;
+  uint16_t *y;
 };
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -192,6 +196,7 @@ inline KArgs make_args(const GemmArgs &a, bool second) {
   k.w2p = a.w2p;
   k.w2sp = reinterpret_cast<const uint32_t *>(a.w2sp);
   k.sync = a.sync;
+  k.ids = a.ids; k.inv = a.inv; k.wts_a = a.wts_a; k.y = a.y;
   return k;
 }
 

@@ -171,6 +171,138 @@ __global__ __launch_bounds__(64 * NW) void gemm2_kernel(KArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Token-major GEMM2 with the top-k combine folded in (decode batches, plan
+// MOE_PLAN_DECODE; "feat(moe): FlyDSL MegaMoE fused EP-MoE integration",
+// summary: one fused operation in place of the separate GEMM2 and combine).
+// A work item is (token t, 16 TPI output columns).  The pairs (slot j, K step) of
+// the token's top_k slots, top_k * I/128 of them, are split into contiguous
+// ranges over the NW waves; a wave loads the weight fragments and A2 operands
+// of four pairs at a time (they may span two slots) and accumulates per slot
+// (all 16 rows of the MFMA tile carry the token's A2 row; row 0 is kept).  The
+// per-(wave, slot) partial sums meet in LDS; wave 0 adds them per slot, scales
+// each slot's row by its routing weight, stores it to the assignment's
+// staging row (the layout the combine kernel reads) and writes
+// y[t] = bf16 of the FP32 sum of the weighted rows in slot order: the
+// combine kernel's result, without its launch or its reads of the staging.
+// Measured on the 7168 x 3072, 384 x 6 layer (us per call, eager, one box):
+// T = 1: 58.5 against 55.0 for the stream plan (224 items for 256 CUs read
+// six experts each: fewer, longer items than the stream GEMM2's 672); T = 2:
+// 94.7 against 99.6; T = 3 .. 8: 3-5% slower (experts two tokens share are
+// read twice).  So it is an opt-in plan the tuner may pick, not the built-in
+// choice.
+// ---------------------------------------------------------------------------
+// Operands of four (slot, K step) pairs of one token's token-major GEMM2 item.
+template <int TPI>
+struct TmGroup {
+  v8i a[4];
+  u32x4 b[4][TPI];
+  int sa[4], sb[4];
+};
+
+template <int FMT, int NW, int TPI>
+__global__ __launch_bounds__(64 * NW) void gemm2_tm_kernel(KArgs p) {
+  __shared__ float part[NW][8][TPI][16];  // [wave][slot][tile][column]: row 0 of each tile
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4;
+  const int NB = p.H / (16 * TPI), k = p.top_k, S = p.I / 128, P = k * S;
+  const int i0 = wave * P / NW, i1 = (wave + 1) * P / NW;
+  const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
+  const size_t ntiles = (size_t)p.H / 16;
+  const long total = (long)p.T * NB;
+  for (long w = blockIdx.x; w < total; w += gridDim.x) {
+    const int t = (int)(w / NB), nb = (int)(w % NB);
+    // the first tile of the item: tile u of quad qd is tile 4 qd + u
+    const size_t tile0 = (size_t)nb * TPI;
+    // slots this wave's range does not reach keep zero partial sums
+    for (int x = lane; x < 8 * TPI * 16; x += 64) (&part[wave][0][0][0])[x] = 0.0f;
+    v4f acc[TPI];
+#pragma unroll
+    for (int q = 0; q < TPI; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
+    int cj = i0 / S;  // slot of the accumulation in progress
+    // four pairs at a time: the weight fragments and A2 operands of all four
+    // are loaded before their MFMAs (software-pipelining two such groups, with
+    // the next group's loads issued before the current group's MFMAs,
+    // measured slower: 70 against 61 us per call at T = 1)
+    for (int i4 = i0; i4 < i1; i4 += 4) {
+      TmGroup<TPI> G;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i4 + u;
+        if (i < i1) {
+          const int j = i / S, st = i - j * S;
+          const int asg = t * k + j;
+          const size_t e = (size_t)uniform(p.ids[asg]);
+          const size_t pr = (size_t)uniform(p.inv[asg]);
+          G.a[u] = load_a<FMT>(p.a2c + pr * a2row, st, g);
+          G.sa[u] = p.a2s[pr * (p.I / 32) + 4 * st + g];
+          const size_t qb = e * (ntiles / 4) + tile0 / 4;  // the item's tiles share a quad
+#pragma unroll
+          for (int q = 0; q < TPI; ++q)
+            G.b[u][q] = *reinterpret_cast<const u32x4 *>(
+                p.wp + (qb * S + st) * 4096 + ((tile0 + q) % 4) * 1024 + lane * 16);
+          G.sb[u] = (int)p.wsp[(qb * S + st) * 64 + lane];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i4 + u;
+        if (i < i1) {
+          const int j = i / S;
+          if (j != cj) {  // the range moves on to the next slot: park the finished one
+            if (lane < 16)
+#pragma unroll
+              for (int q = 0; q < TPI; ++q) part[wave][cj][q][lane] = acc[q][0];
+#pragma unroll
+            for (int q = 0; q < TPI; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
+            cj = j;
+          }
+#pragma unroll
+          for (int q = 0; q < TPI; ++q) {
+            v8i bq;
+            bq[0] = (int)G.b[u][q][0]; bq[1] = (int)G.b[u][q][1];
+            bq[2] = (int)G.b[u][q][2]; bq[3] = (int)G.b[u][q][3];
+            bq[4] = 0; bq[5] = 0; bq[6] = 0; bq[7] = 0;
+            // byte (tile0 + q) % 4 of the quad's scale dword is this tile's
+            acc[q] = mfma_q<FMT>((int)((tile0 + q) % 4), G.a[u], bq, acc[q], G.sa[u], G.sb[u]);
+          }
+        }
+      }
+    }
+    if (i0 < i1 && lane < 16)
+#pragma unroll
+      for (int q = 0; q < TPI; ++q) part[wave][cj][q][lane] = acc[q][0];
+    __syncthreads();
+    if (wave == 0 && lane < 16) {
+      // each weighted row is rounded on its own before it joins the sum (no
+      // fused multiply-add), so y is exactly the slot-order sum of the rows
+      // stored for the combine
+#pragma clang fp contract(off)
+      float sum[TPI];
+#pragma unroll
+      for (int q = 0; q < TPI; ++q) sum[q] = 0.f;
+      const size_t col = (size_t)16 * tile0 + lane;
+      for (int j = 0; j < k; ++j) {
+        const int asg = t * k + j;
+        const float wj = p.wts_a[asg];
+        float *row = p.rows + (size_t)p.inv[asg] * p.H + col;
+#pragma unroll
+        for (int q = 0; q < TPI; ++q) {
+          float o = 0.f;
+#pragma unroll
+          for (int v = 0; v < NW; ++v) o += part[v][j][q][lane];
+          const float tj = wj * o;
+          row[16 * q] = tj;
+          sum[q] += tj;
+        }
+      }
+      uint16_t *yr = p.y + (size_t)t * p.H + col;
+#pragma unroll
+      for (int q = 0; q < TPI; ++q) yr[16 * q] = f32_to_bf16(sum[q]);
+    }
+    __syncthreads();  // part is free again
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Fused stream launch (MegaMoE's single launch of Stage1 and Stage2, "add
 // A4W4 and FP8 P2P transport support to MegaMoE"): the GEMM1 items (gate/up
 // unit, m-tile) and then the GEMM2 items (64 output columns, m-tile) of one
@@ -450,6 +582,18 @@ hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s) {
   if (a.plan.fused) return hipSuccess;  // launch_gemm1 ran both GEMMs
   const KArgs k = make_args(a, true);
   if (a.plan.tiled) return launch_tiled_gemm2(a, k, s);
+  if (gemm2_writes_y(a)) {
+    // token-major with the combine folded in: one item per (token, 32
+    // columns).  32-column items measured at or below 64-column ones at every
+    // decode size (T = 1: 58.5 against 61.1 us per call; they give 224 items
+    // per token instead of 112 for the device's 256 CUs)
+    const long items = (long)a.T * (a.H / 32);
+    const long cap = 2L * a.num_cus;
+    const unsigned grid = (unsigned)(items < cap ? items : cap);
+    if (a.act == MOE_ACT_MXFP8_E4M3) gemm2_tm_kernel<0, 8, 2><<<grid, 512, 0, s>>>(k);
+    else gemm2_tm_kernel<4, 8, 2><<<grid, 512, 0, s>>>(k);
+    return hipGetLastError();
+  }
   const long items = a.max_mtiles * (a.H / 64);
   const unsigned grid = persistent_grid(items, a.num_cus);
   const bool f8 = a.act == MOE_ACT_MXFP8_E4M3;

@@ -139,6 +139,7 @@ struct GemmPlan {
   int mt;   // 16-row MFMA tiles per work item (1 for stream)
   int split;  // tiled kernel form (kTiledSplit)
   bool fused = false;  // stream only: GEMM1 and GEMM2 items in one persistent launch
+  bool tm = false;     // stream only: token-major GEMM2 with the top-k combine folded in
   int bm() const { return 16 * mt; }
 };
 GemmPlan choose_plan(int T, int top_k, int E, int act);
@@ -161,7 +162,14 @@ struct GemmArgs {
   float *rows;  // [N][H] weighted GEMM2 rows (layout by combine)
   int combine;  // moe_combine transport of the rows
   int32_t *sync;  // fused launch: work counter, wait flag, per-m-tile counts (zeroed)
+  // token-major GEMM2 (plan.tm): routing by assignment and the output
+  const int32_t *ids, *inv;  // [N] expert and sorted row of assignment a
+  const float *wts_a;        // [N] routing weight of assignment a
+  uint16_t *y;               // [T][H] bf16 output
 };
+// Whether launch_gemm2 writes y itself (token-major GEMM2 with the combine
+// folded in; the FP32 transport only), so that no combine launch follows.
+inline bool gemm2_writes_y(const GemmArgs &a) { return a.plan.tm && a.combine == MOE_COMBINE_FP32; }
 hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s);
 hipError_t launch_combine(const void *rows, const int32_t *inv, int T, int H, int top_k,

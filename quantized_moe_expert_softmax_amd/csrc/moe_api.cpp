@@ -249,8 +249,10 @@ namespace {
 GemmPlan plan_for(const moe_layer *L, int T, int top_k, int act) {
   for (const moe_plan &p : L->plans)
     if (p.act == act && p.top_k == top_k && T <= p.t_max)
-      return p.variant == MOE_PLAN_TILED ? GemmPlan{true, p.rows / 16, kTiledSplit}
-                                         : GemmPlan{false, 1, 1, p.variant == MOE_PLAN_FUSED};
+      return p.variant == MOE_PLAN_TILED
+                 ? GemmPlan{true, p.rows / 16, kTiledSplit}
+                 : GemmPlan{false, 1, 1, p.variant == MOE_PLAN_FUSED,
+                            p.variant == MOE_PLAN_DECODE};
   return choose_plan(T, top_k, L->E, act);
 }
 
@@ -268,9 +270,10 @@ moe_status moe_set_plans(moe_layer_t L, const moe_plan *plans, int n) {
     if (p.top_k < 1 || p.top_k > 8 || p.top_k > L->E)
       return fail(MOE_ERR_INVALID_ARG, "plan %d: top_k %d", i, p.top_k);
     if (p.t_max < 1) return fail(MOE_ERR_INVALID_ARG, "plan %d: t_max %d", i, p.t_max);
-    if (p.variant == MOE_PLAN_STREAM || p.variant == MOE_PLAN_FUSED) {
+    if (p.variant == MOE_PLAN_STREAM || p.variant == MOE_PLAN_FUSED ||
+        p.variant == MOE_PLAN_DECODE) {
       if (p.rows != 16)
-        return fail(MOE_ERR_INVALID_ARG, "plan %d: stream and fused rows must be 16", i);
+        return fail(MOE_ERR_INVALID_ARG, "plan %d: stream, fused and decode rows must be 16", i);
     } else if (p.variant == MOE_PLAN_TILED) {
       if (p.rows % 16 != 0 || !tiled_mt_built(p.act, p.rows / 16))
         return fail(MOE_ERR_INVALID_ARG, "plan %d: no tiled kernel with %d rows for act %d", i,
@@ -289,7 +292,8 @@ moe_status moe_get_plan(moe_layer_t L, int T, int top_k, moe_act_dtype act, moe_
   if (!out) return fail(MOE_ERR_INVALID_ARG, "null output");
   const GemmPlan g = plan_for(L, T, top_k, act);
   *out = moe_plan{(int32_t)act, top_k, T,
-                  g.tiled ? MOE_PLAN_TILED : (g.fused ? MOE_PLAN_FUSED : MOE_PLAN_STREAM),
+                  g.tiled ? MOE_PLAN_TILED
+                          : (g.fused ? MOE_PLAN_FUSED : (g.tm ? MOE_PLAN_DECODE : MOE_PLAN_STREAM)),
                   g.tiled ? 16 * g.mt : 16};
   return MOE_OK;
 }
@@ -356,6 +360,7 @@ static moe_status forward_impl(moe_layer_t L, bool prequant, const void *x, cons
   g.w13p = L->w13p; g.w13sp = L->w13sp; g.w2p = L->w2p; g.w2sp = L->w2sp;
   g.rows = rows;
   g.combine = (int)flags;
+  g.ids = ids; g.inv = inv; g.wts_a = wts; g.y = static_cast<uint16_t *>(y);
   // the fused launch's counters, zeroed by the route/sort launch before it
   g.sync = reinterpret_cast<int32_t *>(base + W.sync);
   // the routing launch clears the give-up flag on every call (moe_fused_status
@@ -419,7 +424,7 @@ static moe_status forward_impl(moe_layer_t L, bool prequant, const void *x, cons
   mark();
   if (e == hipSuccess) e = launch_gemm2(g, s);
   mark();
-  if (e == hipSuccess)
+  if (e == hipSuccess && !gemm2_writes_y(g))
     e = launch_combine(rows, inv, T, L->H, top_k, (int)flags, static_cast<uint16_t *>(y), s);
   mark();
   if (e != hipSuccess) return hip_fail(e, "moe_forward launch");

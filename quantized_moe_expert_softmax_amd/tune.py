@@ -18,20 +18,23 @@ import json
 import sys
 import time
 
-from . import (MOE_PLAN_FUSED, MOE_PLAN_STREAM, MOE_PLAN_TILED,
+from . import (MOE_PLAN_DECODE, MOE_PLAN_FUSED, MOE_PLAN_STREAM, MOE_PLAN_TILED,
                alloc_workspace, moe_forward, moe_get_plan, moe_set_plans)
 
 
-_NAMES = {MOE_PLAN_STREAM: "stream", MOE_PLAN_TILED: "tiled", MOE_PLAN_FUSED: "fused"}
+_NAMES = {MOE_PLAN_STREAM: "stream", MOE_PLAN_TILED: "tiled", MOE_PLAN_FUSED: "fused",
+          MOE_PLAN_DECODE: "decode"}
 
 
 def candidates(act: int, include_fused: bool = False):
-    """Plans to time: the stream plan and every tiled tile height (both
-    activation formats); the fused single launch only when the caller opts in
-    (its bounded waits rely on having the device to itself)."""
+    """Plans to time: the stream plan, the decode plan (token-major GEMM2 with
+    the combine folded in) and every tiled tile height (both activation
+    formats); the fused single launch only when the caller opts in (its
+    bounded waits rely on having the device to itself)."""
     rows = (32, 64, 96, 128, 160, 192)
     fused = [(MOE_PLAN_FUSED, 16)] if include_fused else []
-    return [(MOE_PLAN_STREAM, 16)] + fused + [(MOE_PLAN_TILED, r) for r in rows]
+    return ([(MOE_PLAN_STREAM, 16), (MOE_PLAN_DECODE, 16)] + fused +
+            [(MOE_PLAN_TILED, r) for r in rows])
 
 
 def _time(layer, x, lgs, top_k, act, y, ws, steps, warmup):

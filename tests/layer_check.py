@@ -211,8 +211,16 @@ def check_tokens(layer, ws, y_bits, x, lg, k, act, weights_for, tokens=None,
     yb = np.asarray(y_bits)[tokens]
     y_dev = oracle.combine(g_vals.reshape(-1, H), k, moe.MOE_COMBINE_FP32)
     bad = np.where((y_dev != yb).any(axis=1))[0]
-    assert bad.size == 0, "%s: y is not the FP32 slot-order sum of the staging rows at " \
-        "tokens %s" % (what, tokens[bad][:8].tolist())
+    if bad.size:
+        r0 = bad[0]
+        cols = np.where(y_dev[r0] != yb[r0])[0]
+        rows_t = g_vals.reshape(-1, k, H)[r0]
+        raise AssertionError(
+            "%s: y is not the FP32 slot-order sum of the staging rows at tokens %s; token %d "
+            "columns %s: device y %s, sum of its staging rows %s, the rows there %s" % (
+                what, tokens[bad][:8].tolist(), tokens[r0], cols[:4].tolist(),
+                [hex(v) for v in yb[r0][cols[:4]]], [hex(v) for v in y_dev[r0][cols[:4]]],
+                rows_t[:, cols[:2]].T.tolist()))
     explained = row_diff.reshape(-1, k).any(axis=1)
     rel, row = assert_output_close(yb, y_ref, what, explained)
     return {"tokens": int(tokens.size), "rel": rel, "max_row": row, "a2_mism": mism,

@@ -89,9 +89,9 @@ def test_builtin_plan_choices(E, k):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(rows=48), dict(rows=224, act=1), dict(variant=3), dict(act=5), dict(top_k=0),
+    dict(rows=48), dict(rows=224, act=1), dict(variant=4), dict(act=5), dict(top_k=0),
     dict(top_k=9), dict(t_max=0), dict(variant=moe.MOE_PLAN_STREAM, rows=32),
-    dict(variant=moe.MOE_PLAN_FUSED, rows=32),
+    dict(variant=moe.MOE_PLAN_FUSED, rows=32), dict(variant=moe.MOE_PLAN_DECODE, rows=32),
 ])
 def test_invalid_plans_rejected(bad):
     w, _, _ = _small(16, 256, 128, 8, 2, seed=13)
