@@ -38,13 +38,12 @@ __device__ __forceinline__ void mma_4tiles(v4f acc[4], const uint8_t *__restrict
       if (s < s1) {
         const v8i a = load_a<FMT>(arow, s, g);
         const int sa = asrow[4 * s + g];
-        const int sb = (int)wsq[(size_t)s * 64 + lane];
+        const int sb = load_weight_scales(wsq + (size_t)s * 64 + lane);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint4 bq = *reinterpret_cast<const uint4 *>(wt + (size_t)s * 4096 + q * 1024 +
-                                                           lane * 16);
+          const u32x4 bq = load_weights16(wt + (size_t)s * 4096 + q * 1024 + lane * 16);
           v8i b;
-          b[0] = (int)bq.x; b[1] = (int)bq.y; b[2] = (int)bq.z; b[3] = (int)bq.w;
+          b[0] = (int)bq[0]; b[1] = (int)bq[1]; b[2] = (int)bq[2]; b[3] = (int)bq[3];
           b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
           acc[q] = mfma_q<FMT>(q, a, b, acc[q], sa, sb);
         }
@@ -237,9 +236,9 @@ __global__ __launch_bounds__(64 * NW) void gemm2_tm_kernel(KArgs p) {
           const size_t qb = e * (ntiles / 4) + tile0 / 4;  // the item's tiles share a quad
 #pragma unroll
           for (int q = 0; q < TPI; ++q)
-            G.b[u][q] = *reinterpret_cast<const u32x4 *>(
-                p.wp + (qb * S + st) * 4096 + ((tile0 + q) % 4) * 1024 + lane * 16);
-          G.sb[u] = (int)p.wsp[(qb * S + st) * 64 + lane];
+            G.b[u][q] = load_weights16(p.wp + (qb * S + st) * 4096 + ((tile0 + q) % 4) * 1024 +
+                                       lane * 16);
+          G.sb[u] = load_weight_scales(p.wsp + (qb * S + st) * 64 + lane);
         }
       }
 #pragma unroll
@@ -432,11 +431,10 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(KArgs p) {
               a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
             }
             const int sa = (int)__builtin_amdgcn_raw_buffer_load_b8(rs, soff + 4 * st, 0, kCoherent);
-            const int sb = (int)wsq[(size_t)st * 64 + lane];
+            const int sb = load_weight_scales(wsq + (size_t)st * 64 + lane);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const u32x4 bq = *reinterpret_cast<const u32x4 *>(wt + (size_t)st * 4096 +
-                                                               q * 1024 + lane * 16);
+              const u32x4 bq = load_weights16(wt + (size_t)st * 4096 + q * 1024 + lane * 16);
               v8i b;
               b[0] = (int)bq[0]; b[1] = (int)bq[1]; b[2] = (int)bq[2]; b[3] = (int)bq[3];
               b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;

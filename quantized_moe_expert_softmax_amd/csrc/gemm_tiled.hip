@@ -262,15 +262,31 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
     // the 4 / RS fragments of this wave's share, then the quad's scale
     // dword (each wave of a quad copies it: same bytes, same LDS address)
     const int f = rh * (4 / PS::RS) + i;
-    if (i < 4 / PS::RS)
+    if (i < 4 / PS::RS) {
+      // (copying these with the non-temporal hint measured 4% faster per call
+      // where each expert is one m-block, 5-14% slower where later m-blocks
+      // re-read the panels from L2, and a run-time choice between the two
+      // forms cost 11% through code generation at 160 rows: not used)
       copy16_to_lds(p.wp + ((size_t)cqb * quad_bytes + (size_t)sr * 4096) +
                         (uint32_t)(f * 1024 + lane * 16),
                     sw + (4 * qd + f) * 1024);
-    else
+    } else if (rh == 0) {
+      // the quad's scale dword: one wave of the quad copies it (the barrier of
+      // the step makes it visible to the other)
       copy4_to_lds(reinterpret_cast<const uint8_t *>(p.wsp + (size_t)cqb * quad_dwords +
                                                      (size_t)sr * 64) +
                        (uint32_t)(lane * 4),
                    sw + PS::OFF_BS + qd * 256);
+    }
+  };
+  // the wait for the copies of the step NB - 2 steps behind the cursor: the
+  // wave with rh == 0 issues CB copies per step (its fragments and the scale
+  // dword), the others CB - 1
+  auto wait_weights = [&]() __attribute__((always_inline)) {
+    if (rh == 0)
+      wait_vm<(NB - 2) * PS::CB>();
+    else
+      wait_vm<(NB - 2) * (PS::CB - 1)>();
   };
   // the cursor moves to the next step once all its copies are issued
   auto advance = [&]() __attribute__((always_inline)) {
@@ -381,7 +397,7 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
       // step 0's copies were issued NB - 1 steps ago (with XITEM: in the last
       // steps of the previous item, or before the first; the previous
       // epilogue's stores, issued after them, also drain here)
-      wait_vm<(NB - 2) * PS::CB>();  // step 0 has landed
+      wait_weights();  // step 0 has landed
       barrier_keep_copies();
 
       // the MFMA loop and epilogue of this wave's m-tiles, compiled once per
@@ -431,7 +447,7 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
           }
           __builtin_amdgcn_sched_barrier(0);
           advance();
-          wait_vm<(NB - 2) * PS::CB>();  // step s+1's weights have landed
+          wait_weights();  // step s+1's weights have landed
           barrier_keep_copies();
         }
         // without XITEM the re-reads past the last step land before the next
