@@ -3,38 +3,42 @@
 A step is one moe_forward call (routing, expert sort, activation quant,
 GEMM1 + SwiGLU + requant, GEMM2 + weighted FP32 combine, BF16 finalize) on
 a batch of T synthetic tokens already resident in HBM (--combine picks the
-transport of the weighted GEMM2 rows: fp32 by default, or bf16 / fp8).  The default workload
-is the DeepSeek-V4-Pro-shaped A8W4 decode layer (H=7168, I=3072, E=384,
-top_k=6, all experts resident) at T=64; the other decode sizes of that
-workload (T=1, 2, 8, 32) are timed too and reported under "sweep".
+transport of the weighted GEMM2 rows: fp32 by default, or bf16 / fp8).
+
+The headline (`value`, `ms_per_step`, `roofline`, `cpu_baseline`) is the
+largest configuration that one GPU holds: the DeepSeek-V4-Pro-shaped expert
+layer (H=7168, I=3072, E=384, top_k=6, all experts resident) with MXFP4
+activations (A4W4) at T=16384 tokens.  `sweep` then times every
+configuration point of the five workloads -- V4-Pro decode T=1..64 and prefill
+T=512..8192 (A8W4, uniform and skewed routing), A4W4 T=1..16384, and the four
+V4.1-Flash TP-shard shapes at 16 token counts (A8W4) -- each with its GEMM1
+roofline entry (--sweep workload: only the headline workload's points;
+--sweep none: none).
 
 Between steps the router logits rotate over 8 pre-drawn sets, so successive
-calls touch different experts (the touched weights of one call are larger
-than the MI355X last-level cache at T >= 8, and rotate through ~1.7 GB at
-T = 1).  Each token count is timed in passes over the same calls: eager
-launches (this is `value` and `ms_per_step`), HIP-graph replay (one graph
-captured per logits set; `ms_per_step_graph`, slower than eager launches on
-this stack), and eager launches with HIP events the library records around
-every kernel (per-kernel times; an event record costs a few microseconds, so
-this pass is not used for the step time).  A fourth pass times each call on
-its own (HIP events on the launch stream) after a 512 MiB device read that
-evicts the last-level cache: `us_per_call_flushed` gives its p10, median and
-p90.  The roofline
-entry is for the dominant kernel (GEMM1), against whichever ceiling leaves
-it less time: HBM bandwidth with its algorithmic bytes per launch (touched
-experts x gate/up weight bytes, codes + E8M0 scales, + the quantised token
-rows read + the requantised rows written; the decode sizes), or the dense
-MFMA peak of its operand formats with its algorithmic FLOPs (4 T top_k H I;
-the large shards at prefill sizes).  layer_mfma_frac is the whole layer's
-6 T top_k H I FLOPs per step against that peak.
+calls touch different experts.  Each token count is timed in passes over the
+same calls: eager launches (this is `value` and `ms_per_step`), HIP-graph
+replay (one graph captured per logits set; decode sizes only in the sweep),
+eager launches with HIP events the library records around every kernel on
+the launch stream (per-kernel times; an event record costs a few
+microseconds, so this pass is not used for the step time), and each call on
+its own after a 512 MiB device read that evicts the last-level cache
+(`us_per_call_flushed`: p10, median, p90).  The roofline entry is for the
+dominant kernel (GEMM1), against whichever ceiling needs the longer time: HBM
+bandwidth with its algorithmic bytes per launch (touched experts x gate/up
+weight bytes, codes + E8M0 scales, + the quantised token rows read + the
+requantised rows written), or the dense MFMA peak of its operand formats
+with its algorithmic FLOPs (4 T top_k H I).  layer_mfma_frac is the whole
+layer's 6 T top_k H I FLOPs per step against that peak.
 
-cpu_baseline: the CPU oracle (test infrastructure, single-threaded C)
-timed on a bounded sample of the same workload: routing, sort and
-quantisation of all T tokens plus the expert FFN of a few sampled tokens;
-cpu_baseline_all_cores: the same oracle over token partitions, one thread
-per host core (up to 16), on 2 sampled tokens per thread.
+cpu_baseline: the CPU oracle (test infrastructure, single-threaded C) timed
+on a bounded sample of the headline workload: routing, sort and quantisation
+of all T tokens plus the expert FFN of as many sampled tokens as fit about
+15 s; cpu_baseline_all_cores: the same oracle over token partitions, one
+thread per host core (up to 16), on 2 sampled tokens per thread.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
+                  [--sweep all|workload|none]
 """
 from __future__ import annotations
 
@@ -49,6 +53,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+# the headline: the largest configuration one GPU holds (7168 x 3072, 384 x 6, A4W4)
+HEADLINE = ("v4pro_a4w4", 16384)
+# the sweep's workloads, grouped so that workloads sharing an expert set follow each other
+SWEEP = ("v4pro_decode", "v4pro_prefill", "v4pro_prefill_skewed", "v4pro_a4w4",
+         "v41flash_i640_e384", "v41flash_i1152_e384", "v41flash_i640_e128", "v41flash_i1152_e128")
 # MI355X dense matrix peaks, TFLOP/s: MXFP8 x MXFP4 runs at the FP8 rate, MXFP4 x MXFP4 at FP4's
 MFMA_PEAK_TFLOPS = {0: 5000.0, 1: 10100.0}
 PROFILES = os.path.join(ROOT, "profiles")
@@ -67,12 +76,17 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="v4pro_decode")
-    p.add_argument("--T", type=int, default=None, help="headline token count")
+    p.add_argument("--workload", default=HEADLINE[0])
+    p.add_argument("--T", type=int, default=None,
+                   help="headline token count (default: %d for the default workload, else the "
+                        "workload's largest)" % HEADLINE[1])
     p.add_argument("--act", type=int, default=None, help="0 = MXFP8 (A8W4), 1 = MXFP4 (A4W4)")
-    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--sweep", default="all", choices=("all", "workload", "none"),
+                   help="configuration points timed after the headline")
+    p.add_argument("--no-sweep", action="store_true", help="same as --sweep none")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=4, help="tokens the oracle FFN runs on")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="about how long the single-thread oracle FFN sample runs")
     p.add_argument("--prequant", action="store_true",
                    help="feed MX-quantised activations (moe_forward_prequant)")
     p.add_argument("--combine", default="fp32", choices=("fp32", "bf16", "fp8"),
@@ -167,7 +181,7 @@ def gemm1_flops(layer, T, top_k):
 def roofline_entry(layer, U, T, top_k, act, g1_ms):
     """Roofline of GEMM1 (the dominant kernel): its algorithmic bytes against
     HBM and its algorithmic FLOPs against the dense MFMA peak of its operand
-    formats; `bound` is the ceiling that leaves less time, `achieved` the
+    formats; `bound` is the ceiling that needs the longer time, `achieved` the
     launch's rate against it (the other ceiling's fraction is kept beside)."""
     b = gemm1_bytes(layer, U, T, top_k, act)
     f = gemm1_flops(layer, T, top_k)
@@ -195,12 +209,14 @@ def layer_weight_bytes(layer, U):
 COMBINES = {"fp32": 0, "bf16": 1, "fp8": 2}
 
 
-def time_T(moe, torch, layer, wl, T, act, steps, warmup, combine=0, prequant=False):
-    """Three passes over the same `steps` calls (logits rotating over 8 sets):
-    eager launches, HIP-graph replays (one graph captured per logits set),
-    both with no events, then an eager pass with per-kernel HIP events.
-    prequant: the calls take x already MX-quantised (moe_forward_prequant; the
-    codes are made once, outside the timed region)."""
+def time_T(moe, torch, layer, wl, T, act, steps, warmup, combine=0, prequant=False,
+           graphs=True):
+    """Passes over the same `steps` calls (logits rotating over 8 sets): eager
+    launches and (graphs) HIP-graph replays (one graph captured per logits
+    set), both with no events; an eager pass with per-kernel HIP events; and
+    the calls one by one after a cache-evicting read.  prequant: the calls
+    take x already MX-quantised (moe_forward_prequant; the codes are made
+    once, outside the timed region)."""
     x = torch.from_numpy(wl.x(T).view("int16")).cuda().view(torch.bfloat16)
     lgs = [torch.from_numpy(wl.logits(T, r)).cuda() for r in range(8)]
     ws = moe.alloc_workspace(layer, T, wl.top_k, act)
@@ -230,24 +246,26 @@ def time_T(moe, torch, layer, wl, T, act, steps, warmup, combine=0, prequant=Fal
     torch.cuda.synchronize()
     dt_eager = time.perf_counter() - t0
 
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    graphs = []
-    for r in range(8):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            call(lgs[r], cap)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    for i in range(warmup):
-        graphs[i % 8].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % 8].replay()
-    torch.cuda.synchronize()
-    dt_graph = time.perf_counter() - t0
-    del graphs
+    dt_graph = None
+    if graphs:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        gl = []
+        for r in range(8):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                call(lgs[r], cap)
+            gl.append(g)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            gl[i % 8].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            gl[i % 8].replay()
+        torch.cuda.synchronize()
+        dt_graph = time.perf_counter() - t0
+        del gl
 
     moe.moe_profile_enable(layer, True, steps)
     for i in range(steps):
@@ -276,12 +294,38 @@ def time_T(moe, torch, layer, wl, T, act, steps, warmup, combine=0, prequant=Fal
     def pct(q):
         return round(per_call[min(len(per_call) - 1, int(q * len(per_call)))], 2)
     flushed = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}
+    plan = moe.moe_get_plan(layer, T, wl.top_k, act)
     return {"dt_eager": dt_eager, "dt_graph": dt_graph, "kern": kern, "ncalls": ncalls, "U": U,
-            "flushed": flushed}
+            "flushed": flushed, "plan": [plan["variant"], plan["rows"]], "steps": steps}
 
 
-def cpu_baseline(moe, torch, layer_dev_weights, wl, T, act, rows):
-    """Oracle on a bounded sample: route/sort/quant of all T tokens + FFN of `rows` tokens."""
+def point_entry(layer, wl, T, act, r):
+    """The sweep entry of one configuration point."""
+    nc = max(r["ncalls"], 1)
+    g1 = r["kern"]["gemm1"] / nc
+    d = r["dt_eager"] / r["steps"]
+    roof, _ = roofline_entry(layer, r["U"], T, wl.top_k, act, g1)
+    e = {
+        "us_per_call": round(d * 1e6, 2),
+        "us_per_call_flushed": r["flushed"],
+        "tokens_per_s": round(T / d, 1),
+        "touched_experts": round(r["U"], 1),
+        "layer_weight_GBps": round(layer_weight_bytes(layer, r["U"]) / d / 1e9, 1),
+        "layer_mfma_frac": round(6.0 * T * wl.top_k * wl.H * wl.I / d / 1e12 /
+                                 MFMA_PEAK_TFLOPS[act], 4),
+        "gemm1_us": round(g1 * 1e3, 2),
+        "roofline_gemm1": {k: roof[k] for k in ("bound", "achieved", "unit", "frac")},
+        "plan": r["plan"],
+        "kernels_us": {k: round(v / nc * 1e3, 2) for k, v in r["kern"].items()},
+    }
+    if r["dt_graph"] is not None:
+        e["us_per_call_graph"] = round(r["dt_graph"] * 1e6 / r["steps"], 2)
+    return e
+
+
+def cpu_baseline(moe, torch, layer_dev_weights, wl, T, act, seconds):
+    """Oracle on a bounded sample: route/sort/quant of all T tokens + the FFN of
+    as many evenly spaced tokens as fit about `seconds` (at least 2)."""
     import numpy as np
     import oracle
     w13, w13s, w2, w2s = layer_dev_weights
@@ -292,16 +336,26 @@ def cpu_baseline(moe, torch, layer_dev_weights, wl, T, act, rows):
     oracle.sort(ids, wl.E)
     oracle.mx_quantize_bf16(x, act)
     t_front = time.perf_counter() - t0
-    sample = np.linspace(0, T - 1, num=min(rows, T)).astype(np.int64)
     cache = {}
 
     def wfor(e):
         if e not in cache:
             cache[e] = tuple(a[e].cpu().numpy() for a in (w13, w13s, w2, w2s))
         return cache[e]
-    sel, _ = oracle.route(lg[sample], wl.top_k)
-    for e in set(int(v) for v in sel.reshape(-1)):
-        wfor(e)  # fetch the sampled tokens' experts outside the timed part
+
+    def fetch(rows):  # the sampled tokens' experts, outside the timed part
+        sel, _ = oracle.route(lg[rows], wl.top_k)
+        for e in set(int(v) for v in sel.reshape(-1)):
+            wfor(e)
+    # one token first, to size the sample
+    first = np.array([T // 2], np.int64)
+    fetch(first)
+    t0 = time.perf_counter()
+    oracle.forward_rows(x, lg, first, wfor, wl.top_k, act)
+    t_one = time.perf_counter() - t0
+    n = int(max(2, min(T, 64, seconds / max(t_one, 1e-6))))
+    sample = np.unique(np.linspace(0, T - 1, num=n).astype(np.int64))
+    fetch(sample)
     t0 = time.perf_counter()
     oracle.forward_rows(x, lg, sample, wfor, wl.top_k, act)
     t_ffn = time.perf_counter() - t0
@@ -312,9 +366,9 @@ def cpu_baseline(moe, torch, layer_dev_weights, wl, T, act, rows):
         "cores": 1,
         "kind": "oracle",
         "front_s_per_token": t_front / T,
-        "sample": ("route+sort+quant of all %d tokens (%.3f s) + expert FFN of %d sampled tokens "
-                   "(%.2f s); value = 1 / (front time per token + FFN time per sampled token)"
-                   % (T, t_front, len(sample), t_ffn)),
+        "sample": ("route+sort+quant of all %d tokens (%.2f s) + expert FFN of %d evenly spaced "
+                   "tokens (%.2f s); value = 1 / (front time per token + FFN time per sampled "
+                   "token)" % (T, t_front, len(sample), t_ffn)),
     }
 
 
@@ -364,6 +418,21 @@ def cpu_baseline_all_cores(torch, layer_dev_weights, wl, T, act, single):
     }
 
 
+def sweep_points(args, wl_head, T_head, act_override):
+    """(workload, T) of every configuration point to time after the headline."""
+    from quantized_moe_expert_softmax_amd import synth
+    mode = "none" if args.no_sweep else args.sweep
+    if mode == "none":
+        return []
+    names = SWEEP if mode == "all" else (wl_head.name,)
+    pts = []
+    for n in names:
+        for t in synth.WORKLOADS[n].Ts:
+            if (n, t) != (wl_head.name, T_head):
+                pts.append((n, t))
+    return pts
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -379,65 +448,70 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     act = wl.act if args.act is None else args.act
-    T = args.T or max(wl.Ts)
+    T = args.T or (HEADLINE[1] if wl.name == HEADLINE[0] else max(wl.Ts))
     torch.cuda.set_device(0)
-    log("building %s weights on the device (H=%d I=%d E=%d)" % (wl.name, wl.H, wl.I, wl.E))
-    t0 = time.perf_counter()
-    w = synth.device_weights(wl.H, wl.I, wl.E, wl.seed)
-    layer = moe.moe_prepare_weights(wl.E, wl.H, wl.I, *w)
-    torch.cuda.synchronize()
-    log("weights ready in %.1f s" % (time.perf_counter() - t0))
+    plans = None
     if args.plans:
         with open(args.plans) as fh:
-            moe.moe_set_plans(layer, json.load(fh)["plans"])
+            plans = json.load(fh)["plans"]
+    layers = {}
+
+    def layer_for(w):
+        """The layer of workload w (one expert set resident at a time)."""
+        key = (w.H, w.I, w.E, w.seed)
+        if key not in layers:
+            for k in list(layers):
+                layers.pop(k)[1].close()
+            torch.cuda.empty_cache()
+            log("building %s weights on the device (H=%d I=%d E=%d)" % (w.name, w.H, w.I, w.E))
+            t0 = time.perf_counter()
+            wd = synth.device_weights(w.H, w.I, w.E, w.seed)
+            lay = moe.moe_prepare_weights(w.E, w.H, w.I, *wd)
+            if plans:
+                moe.moe_set_plans(lay, plans)
+            torch.cuda.synchronize()
+            log("weights ready in %.1f s" % (time.perf_counter() - t0))
+            layers[key] = (wd, lay)
+        return layers[key]
 
     combine = COMBINES[args.combine]
+    w, layer = layer_for(wl)
+    layers.clear()  # the headline's expert set is released once the sweep moves on
+    layers[(wl.H, wl.I, wl.E, wl.seed)] = (None, layer)
     r = time_T(moe, torch, layer, wl, T, act, args.steps, args.warmup, combine, args.prequant)
     ms_step = r["dt_eager"] * 1e3 / args.steps
     value = T * args.steps / r["dt_eager"]
     ncalls = max(r["ncalls"], 1)
     g1_ms = r["kern"]["gemm1"] / ncalls
-    U_mean = r["U"]
-    roof, g1_bytes = roofline_entry(layer, U_mean, T, wl.top_k, act, g1_ms)
-    achieved = g1_bytes / (g1_ms * 1e-3) / 1e9
+    roof, g1_bytes = roofline_entry(layer, r["U"], T, wl.top_k, act, g1_ms)
     kernels_us = {k: round(v / ncalls * 1e3, 2) for k, v in r["kern"].items()}
-    log("T=%d: %.1f us/step (eager), %.1f graph, %.0f tokens/s, gemm1 %.1f us (%.0f GB/s), "
+    log("T=%d: %.1f us/step (eager), %.1f graph, %.0f tokens/s, gemm1 %.1f us, roofline %s, "
         "kernels %s" % (T, ms_step * 1e3, r["dt_graph"] * 1e6 / args.steps, value, g1_ms * 1e3,
-                        achieved, kernels_us))
+                        roof, kernels_us))
 
-    def entry(t, r):
-        nc = max(r["ncalls"], 1)
-        g1 = r["kern"]["gemm1"] / nc
-        d = r["dt_eager"] / args.steps
-        return {
-            "us_per_call": round(d * 1e6, 2),
-            "us_per_call_graph": round(r["dt_graph"] * 1e6 / args.steps, 2),
-            "us_per_call_flushed": r["flushed"],
-            "tokens_per_s": round(t / d, 1),
-            "touched_experts": round(r["U"], 1),
-            "layer_weight_GBps": round(layer_weight_bytes(layer, r["U"]) / d / 1e9, 1),
-            "gemm1_us": round(g1 * 1e3, 2),
-            "gemm1_GBps": round(gemm1_bytes(layer, r["U"], t, wl.top_k, act) / (g1 * 1e-3) / 1e9, 1),
-            "kernels_us": {k: round(v / nc * 1e3, 2) for k, v in r["kern"].items()},
-        }
-
-    sweep = {}
-    if not args.no_sweep:
-        for t in wl.Ts:
-            if t == T:
-                continue
-            sweep[str(t)] = entry(t, time_T(moe, torch, layer, wl, t, act, args.steps, args.warmup,
-                                            combine, args.prequant))
-            log("T=%d: %s" % (t, sweep[str(t)]))
-    sweep[str(T)] = entry(T, r)
+    head_entry = point_entry(layer, wl, T, act, r)
 
     cpu = cpu_all = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        cpu = cpu_baseline(moe, torch, w, wl, T, act, args.cpu_rows)
+        cpu = cpu_baseline(moe, torch, w, wl, T, act, args.cpu_seconds)
         cpu_all = cpu_baseline_all_cores(torch, w, wl, T, act, cpu)
         cpu.pop("front_s_per_token")
+    del w  # the layer keeps its packed copy
     traffic, traffic_src = measured_traffic(wl.name, T, act)
+
+    sweep = {}
+    for name, t in sweep_points(args, wl, T, args.act):
+        sw = synth.WORKLOADS[name]
+        sact = sw.act if args.act is None or name != wl.name else act
+        _, lay = layer_for(sw)
+        decode = t <= 64
+        rr = time_T(moe, torch, lay, sw, t, sact, args.steps if decode else max(5, args.steps // 2),
+                    args.warmup, combine, args.prequant, graphs=decode)
+        sweep.setdefault(name, {})[str(t)] = point_entry(lay, sw, t, sact, rr)
+        log("%s T=%d: %s" % (name, t, sweep[name][str(t)]))
+    sweep.setdefault(wl.name, {})[str(T)] = head_entry
+
     dtype = "mxfp8xmxfp4" if act == 0 else "mxfp4xmxfp4"
     line = {
         "metric": "MoE layer tokens/s at T=%d (%s) on one MI355X; us/call vs T in sweep"
@@ -467,8 +541,8 @@ def main():
             "flops_per_launch": gemm1_flops(layer, T, wl.top_k),
             "avg_launch_us": round(g1_ms * 1e3, 2)}),
         # the whole layer's 6 T k H I algorithmic FLOPs per step against the dense MFMA peak
-        "layer_mfma_frac": round(6.0 * T * wl.top_k * wl.H * wl.I / (ms_step * 1e-3) / 1e12 /
-                                 MFMA_PEAK_TFLOPS[act], 4),
+        "layer_mfma_frac": head_entry["layer_mfma_frac"],
+        "plan": r["plan"],
         "kernels_us": kernels_us,
         "sweep": sweep,
         "cpu_baseline": cpu,
@@ -477,7 +551,8 @@ def main():
         "build": build_info(torch),
     }
     print(json.dumps(line), flush=True)
-    layer.close()
+    for _, lay in layers.values():
+        lay.close()
 
 
 if __name__ == "__main__":
