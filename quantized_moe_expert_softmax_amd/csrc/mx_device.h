@@ -1,9 +1,10 @@
 // mx_device.h -- device-side MX (OCP microscaling) and BF16 conversions.
 //
 // Conversions take IEEE bit patterns; element rounding uses exact fp32 adds
-// under the default round-to-nearest-even mode.  They implement the 1x32-block rule the pages quantise with ("quantize BF16
-// activations to MXFP4 with per-1x32 E8M0 scales", FlyDSL #972 Technical
-// Details): block exponent X = floor(log2(amax)) - emax of the element type,
+// under the default round-to-nearest-even mode.  They implement the 1x32-block
+// rule with which the pages turn BF16 activations into MX codes, one E8M0 scale
+// per 32 elements (FlyDSL #972 Technical Details):
+// block exponent X = floor(log2(amax)) - emax of the element type,
 // clamped to [-127, 127]; each element rounded to nearest even on the
 // element grid and saturated; the sign of zero kept.
 #pragma once

@@ -8,9 +8,8 @@ Workloads (the shapes the pages measure; there are no checkpoints, prompts or
 datasets here, so these stand in for them):
 
 * ``tiny``      T=16, H=256, I=128, E=8, top_k=2, A8W4.
-* ``v4pro``     H=7168, I=3072, E=384, top_k=6 (DeepSeek-V4-Pro expert shape,
-                "hidden/intermediate 7168/3072, experts/top-k 384/6" in the
-                Test Result of FlyDSL #972), decode T in {1,2,8,32,64}, prefill
+* ``v4pro``     H=7168, I=3072, E=384, top_k=6 (the DeepSeek-V4-Pro expert
+                shape of the Test Result of FlyDSL #972), decode T in {1,2,8,32,64}, prefill
                 T in {512,1024,4096,8192} with uniform or skewed routing, A4W4
                 at T in {1,64,512,1024,8192,16384}.
 * ``v41flash``  H=5120, I in {640, 1152}, (E, top_k) in {(384, 6), (128, 3)}
