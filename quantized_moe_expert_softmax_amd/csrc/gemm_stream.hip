@@ -524,9 +524,14 @@ GemmPlan choose_plan(int T, int top_k, int E, int act) {
 // the 7168 x 3072 layer: GEMM1 runs faster with eight once there are more
 // items than four per CU (below that, eight-wave workgroups at two per CU
 // leave part of the items for a second round); GEMM2 (K = I, a third of
-// GEMM1's steps) is faster with four at every decode size.
+// GEMM1's steps) is faster with four at every decode size.  With at most one
+// GEMM1 item per CU (the 5120 x {640, 1152} shards at T = 1, 2: 60-252 items)
+// sixteen waves put four times the weight loads in flight: 10% less per call
+// (v41flash I = 640, E = 128, T = 1: 28.5 -> 25.5 us; GEMM1 18.3 -> 15.1).
 static int stream_waves(long items_upper, int num_cus, bool second) {
-  return !second && items_upper > 4L * num_cus ? 8 : 4;
+  if (second) return 4;
+  if (items_upper <= num_cus) return 16;
+  return items_upper > 4L * num_cus ? 8 : 4;
 }
 
 static unsigned persistent_grid(long items_upper, int num_cus) {
@@ -566,7 +571,11 @@ hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s) {
   const long items = a.max_mtiles * (a.I / 32);
   const unsigned grid = persistent_grid(items, a.num_cus);
   const bool f8 = a.act == MOE_ACT_MXFP8_E4M3;
-  if (stream_waves(items, a.num_cus, false) == 8) {
+  const int nw = stream_waves(items, a.num_cus, false);
+  if (nw == 16) {
+    if (f8) gemm1_kernel<0, 16><<<grid, 1024, 0, s>>>(k);
+    else gemm1_kernel<4, 16><<<grid, 1024, 0, s>>>(k);
+  } else if (nw == 8) {
     if (f8) gemm1_kernel<0, 8><<<grid, 512, 0, s>>>(k);
     else gemm1_kernel<4, 8><<<grid, 512, 0, s>>>(k);
   } else {

@@ -80,6 +80,26 @@ def test_forward_small(T, H, I, E, k, act):
 
 
 @pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("T,H,I,E,k", [(37, 384, 256, 5, 3), (300, 512, 640, 16, 4)])
+def test_forward_wide_weight_scales(T, H, I, E, k, act):
+    """Weight scale bytes drawn over 2^-19 .. 2^13 independently per 1x32
+    block (the generated weights span two adjacent bytes per K): every block
+    of the scaled MFMA's B operand carries its own exponent, so a scale
+    applied to the wrong block or row shows up; the same check as above."""
+    w13, w13s, w2, w2s = synth.all_weights(H, I, E, seed=T + 7)
+    rng = np.random.default_rng(T + 11)
+    w13s = rng.integers(108, 141, size=w13s.shape, dtype=np.uint8)
+    w2s = rng.integers(108, 141, size=w2s.shape, dtype=np.uint8)
+    w = (w13, w13s, w2, w2s)
+    x = synth.tokens_bf16(T, H, T + 8)
+    lg = synth.router_logits(T, E, T + 9)
+    layer = _layer(*w)
+    what = "wide scales T=%d H=%d I=%d E=%d k=%d act=%d" % (T, H, I, E, k, act)
+    _, _, st = forward_and_check(layer, x, lg, k, act, host_weights(w), what=what)
+    print(what, st)
+
+
+@pytest.mark.parametrize("act", [0, 1])
 def test_identity_experts_exact(act):
     H, I, E, T = 256, 128, 8, 16
     w13, w13s, w2, w2s, cmap, tau = ol.identity_experts(H, I, E, 5)
