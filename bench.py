@@ -31,6 +31,9 @@ requantised rows written), or the dense MFMA peak of its operand formats
 with its algorithmic FLOPs (4 T top_k H I).  layer_mfma_frac is the whole
 layer's 6 T top_k H I FLOPs per step against that peak.
 
+combine_transports: the headline workload again with the weighted GEMM2 rows carried to the
+FP32 top-k sum as BF16 or MXFP8 rows (one more rounding per term; not the value).
+
 cpu_baseline: the CPU oracle (test infrastructure, single-threaded C) timed
 on a bounded sample of the headline workload: routing, sort and quantisation
 of all T tokens plus the expert FFN of as many sampled tokens as fit about
@@ -38,7 +41,7 @@ of all T tokens plus the expert FFN of as many sampled tokens as fit about
 thread per host core (up to 16), on 2 sampled tokens per thread.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
-                  [--sweep all|workload|none]
+                  [--sweep all|workload|none] [--no-transports] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -62,9 +65,12 @@ SWEEP = ("v4pro_decode", "v4pro_prefill", "v4pro_prefill_skewed", "v4pro_a4w4",
 MFMA_PEAK_TFLOPS = {0: 5000.0, 1: 10100.0}
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "quantized_moe_expert_softmax_amd", "csrc")
-# sources that decide GEMM1's memory traffic: its kernels (stream and tiled), the weight layout
-GEMM_SOURCES = ("gemm_common.h", "gemm_stream.hip", "gemm_tiled.hip", "prepack.hip", "mx_device.h",
-                "internal.h")
+# sources that decide GEMM1's memory traffic, by plan variant: its kernel, the shared GEMM code
+# and the weight layout (the traffic lines in profiles/ are keyed by the hash of these)
+GEMM_SOURCES = {
+    0: ("gemm_common.h", "gemm_stream.hip", "prepack.hip", "mx_device.h", "internal.h"),
+    1: ("gemm_common.h", "gemm_tiled.hip", "prepack.hip", "mx_device.h", "internal.h"),
+}
 
 
 def log(*a):
@@ -85,6 +91,8 @@ def parse():
                    help="configuration points timed after the headline")
     p.add_argument("--no-sweep", action="store_true", help="same as --sweep none")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-transports", action="store_true",
+                   help="skip timing the headline with the BF16 and MXFP8 row transports")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="about how long the single-thread oracle FFN sample runs")
     p.add_argument("--prequant", action="store_true",
@@ -110,10 +118,11 @@ def copy_calibration(torch, mib, reps=3):
     print(json.dumps({"copy_bytes": n, "reps": reps}), flush=True)
 
 
-def gemm_source_hash():
+def gemm_source_hash(variant=1):
+    """Hash of the sources of GEMM1's plan variant (0 stream, 1 tiled)."""
     import hashlib
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in GEMM_SOURCES[variant]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -129,19 +138,21 @@ def build_info(torch):
     for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + fh.read())
-    return {"csrc_sha256": h.hexdigest()[:16], "gemm_source_hash": gemm_source_hash(),
+    return {"csrc_sha256": h.hexdigest()[:16],
+            "gemm_source_hash": {"stream": gemm_source_hash(0), "tiled": gemm_source_hash(1)},
             "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
             "device": torch.cuda.get_device_name(0)}
 
 
-def measured_traffic(workload, T, act):
+def measured_traffic(workload, T, act, plan):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 --pmc summary
     (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by what the
     same counter reads for a plain copy of known size), or (None, None) when
-    there is none for this workload or the GEMM sources changed since the
-    counters were taken."""
+    there is none for this workload and plan or the sources of that plan's
+    GEMM1 changed since the counters were taken."""
     import glob
-    src = gemm_source_hash()
+    src = gemm_source_hash(plan[0])
+    want_plan = "%d:%d" % (plan[0], plan[1])
     for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
         with open(path) as fh:
             for line in fh:
@@ -151,7 +162,7 @@ def measured_traffic(workload, T, act):
                 kv = dict(t.split("=", 1) for t in line[len("traffic:"):].split())
                 if (kv.get("kernel") == "gemm1" and kv.get("workload") == workload
                         and int(kv.get("T", -1)) == T and int(kv.get("act", -1)) == act
-                        and kv.get("source") == src):
+                        and kv.get("plan") == want_plan and kv.get("source") == src):
                     b = (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
                          float(kv["write_kib"]) * float(kv["write_scale"])) * 1024.0
                     return b, os.path.relpath(path, ROOT)
@@ -491,6 +502,20 @@ def main():
 
     head_entry = point_entry(layer, wl, T, act, r)
 
+    # the headline workload with the other transports of the weighted GEMM2 rows into
+    # the FP32 top-k sum (one more rounding per term: an alternative, not the value)
+    transports = {}
+    if combine == 0 and not args.no_transports:
+        for name, c in (("bf16", 1), ("fp8", 2)):
+            rt = time_T(moe, torch, layer, wl, T, act, max(5, args.steps // 2), args.warmup, c,
+                        args.prequant, graphs=False)
+            d = rt["dt_eager"] / rt["steps"]
+            nc = max(rt["ncalls"], 1)
+            transports[name] = {"us_per_call": round(d * 1e6, 2), "tokens_per_s": round(T / d, 1),
+                                "gemm2_us": round(rt["kern"]["gemm2"] / nc * 1e3, 2),
+                                "combine_us": round(rt["kern"]["combine"] / nc * 1e3, 2)}
+            log("transport %s: %s" % (name, transports[name]))
+
     cpu = cpu_all = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
@@ -498,7 +523,7 @@ def main():
         cpu_all = cpu_baseline_all_cores(torch, w, wl, T, act, cpu)
         cpu.pop("front_s_per_token")
     del w  # the layer keeps its packed copy
-    traffic, traffic_src = measured_traffic(wl.name, T, act)
+    traffic, traffic_src = measured_traffic(wl.name, T, act, r["plan"])
 
     sweep = {}
     for name, t in sweep_points(args, wl, T, args.act):
@@ -544,6 +569,9 @@ def main():
         "layer_mfma_frac": head_entry["layer_mfma_frac"],
         "plan": r["plan"],
         "kernels_us": kernels_us,
+        # the same workload with the weighted GEMM2 rows carried to the FP32 sum as BF16 or
+        # MXFP8 (the pages' combine payloads) instead of FP32
+        "combine_transports": transports or None,
         "sweep": sweep,
         "cpu_baseline": cpu,
         # the same oracle over token partitions on all host cores (a baseline, not the target)
