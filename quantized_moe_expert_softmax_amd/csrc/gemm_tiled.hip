@@ -103,14 +103,19 @@ __device__ __forceinline__ void store_item(const KArgs &p, const v4f (&acc)[MTW]
 #pragma unroll
     for (int m = 0; m < MTW; ++m) {
       size_t prow[4];
-      float t[4][4];
+      float wa[4], t[4][4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         prow[r] = (size_t)(row0 + min(16 * (mw0 + m) + 4 * g + r, nrows - 1));
-        const float wa = p.wts[prow[r]];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) t[r][q] = wa * acc[m][4 * u + q][r];
+        wa[r] = p.wts[prow[r]];
       }
+      // the four loads leave together and are waited for once (scheduled
+      // next to their uses, each waited for all copies in flight in turn)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[r][q] = wa[r] * acc[m][4 * u + q][r];
       // (a quad-transposed form with one 16-byte store per tile measured
       // 14-22% slower for GEMM2 than these 64-byte row pieces)
       stage_store_n<4>(p, prow, 16 * tile0, r16, t);
@@ -179,7 +184,7 @@ struct PcShape {
   static_assert(BM <= 256, "scale slots");
   static_assert(NB >= 3, "weight ring");
   static_assert((NA - 1) * CA < 64 && (NB - 1) * CB < 64, "vmcnt range");
-  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(LDS + 16 <= 160 * 1024, "LDS");
 };
 
 template <int FMT, int MT, bool SECOND>
@@ -187,7 +192,10 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
   using F = typename ActFmt<FMT>::F;
   using PS = PcShape<FMT, MT>;
   constexpr int NA = PS::NA, NB = PS::NB, BM = PS::BM, ROWB = PS::ROWB, CH = PS::CH;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[PS::LDS];
+  // (one LDS object: the work-distribution slots sit after the rings; a
+  // second __shared__ array made the compiler wait for every copy in flight
+  // before each LDS read of the MFMA loop)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[PS::LDS + 16];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool producer = uniform(wave) >= PS::NC;
@@ -224,10 +232,43 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
   // height up to 160 rows; at 192 rows (6 m-tiles a wave) its registers
   // would spill, so there each item issues its own first steps.)
   constexpr bool XITEM = MT / kPcRowSplit <= 5;
+  // Work distribution.  The list is dealt to the eight XCDs in chunks of G / 8
+  // consecutive items, chunk j to XCD j % 8 (the order a fixed stride of G
+  // gives: the whole device works on neighbouring items), and the workgroups
+  // of XCD x (b % 8 == x: the hardware deals workgroups to the XCDs in turn)
+  // take XCD x's items in order from the XCD's own counter, one at a time:
+  // whatever their timing, the workgroups of one XCD work on neighbouring
+  // items (one expert's m-blocks and n-blocks), so the m-blocks that read one
+  // weight panel run together and find it in the XCD's L2.  (With each
+  // workgroup on a fixed stride of G items, workgroups that started together
+  // on two m-blocks of one panel drifted apart over the rounds.)  Workgroup
+  // item k is taken at the start of item k - 1 by the first producer wave
+  // and passed on in LDS; the weight cursor needs item k + 1 from step
+  // S - NB + 1 of item k on, so counters are used when S >= NB (every
+  // measured shape), else the fixed stride.
+  int *const qslot = reinterpret_cast<int *>(lds + PS::LDS);
+  const bool dyn = !SECOND && S >= NB;
+  const int xcd = (int)(blockIdx.x % 8);
+  const int qchunk = G / 8;
+  int *const qctr = p.sync + kQueueBase + (SECOND ? 8 : 0) + xcd;
+  // the c-th item of XCD x's sequence (total when past the list's end)
+  auto xcd_item = [&](int c) __attribute__((always_inline)) {
+    const long w = ((long)(c / qchunk) * 8 + xcd) * qchunk + c % qchunk;
+    return w < total ? (int)w : (int)total;
+  };
   const int qd = uniform(wave & 3);  // the weight quad a consumer wave computes and copies
   const int rh = PS::RS == 1 ? 0 : uniform(wave >> 2);  // its share of the copies and m-tiles
   constexpr int MTW = PS::MTW;
   const int total_i = (int)total;      // items fit 32 bits (m-blocks x n-blocks)
+  // this workgroup's item k, given its item k - 1 (items at or past total_i:
+  // none left)
+  auto next_item = [&](int wprev, int k) __attribute__((always_inline)) {
+    return dyn ? uniform(qslot[k & 3]) : wprev + G;
+  };
+  if (dyn) {
+    if (tid == 0) qslot[0] = xcd_item(atomicAdd(qctr, 1));
+    __syncthreads();
+  }
   // Item wi of the list: the items of expert e are [NBLK mtoff[e], NBLK
   // mtoff[e+1]), n-block major and m-block minor, so the m-blocks that read
   // one weight panel are consecutive items: they run at the same time on
@@ -248,10 +289,11 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
     const int ti = 16 * nbi + 4 * qd;  // quads past the last tile read quad 0
     return uniform(ei * (ntiles / 4) + (ti < ntiles ? ti / 4 : 0));
   };
-  int cw = L;         // item of the next copy
-  int cs = 0;         // its step
-  int cslot = 0;      // its ring slot
-  int cqb = L < total_i ? quad_of(L) : 0;
+  int ck = 0;                                // this workgroup's index of the item of the next copy
+  int cw = dyn ? uniform(qslot[0]) : L;      // that item
+  int cs = 0;                                // its step
+  int cslot = 0;                             // its ring slot
+  int cqb = cw < total_i ? quad_of(cw) : 0;
   int rslot = 0;      // ring slot of the current item's step 0
   // weight copy i of the cursor's step
   auto issue_next = [&](int i) __attribute__((always_inline)) {
@@ -294,7 +336,7 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
     if (++cs == S) {
       if (XITEM) {
         cs = 0;
-        cw += G;
+        cw = next_item(cw, ++ck);
         if (cw < total_i) cqb = quad_of(cw);
       } else {
         cs = S - 1;  // re-read the last step until the next item starts
@@ -310,9 +352,9 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
     }
   }
 
-  for (long w = L; w < total; w += G) {
+  for (int k = 0, w = dyn ? uniform(qslot[0]) : L; w < total_i; w = next_item(w, ++k)) {
     int e, nb, mb;
-    coords((int)w, e, nb, mb);
+    coords(w, e, nb, mb);
     const int row0 = uniform(p.offsets[e]) + BM * mb;
     const int nrows = min(BM, uniform(p.offsets[e + 1]) - row0);
 
@@ -335,6 +377,11 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
           csrc[c] = chunk ? A + ridx * arow + 16 * ((ci % CH) ^ act_swizzle<FMT>(row))
                           : As + ridx * srow;
         }
+        // the first producer takes this workgroup's next item, after the row
+        // gathers above (its reply is older than the first stages' copies, so
+        // their wait covers it)
+        int taken = 0;
+        if (PW == 0 && dyn && lane == 0) taken = atomicAdd(qctr, 1);
         auto issue_a = [&](int st) __attribute__((always_inline)) {
           const int sr = min(st, S - 1);
           uint8_t *stg = lds + (st % NA) * PS::A_STAGE;
@@ -350,6 +397,7 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
 #pragma unroll
         for (int st = 0; st < NA - 1; ++st) issue_a(st);
         wait_vm<(NA - 2) * PS::CA>();  // step 0 has landed
+        if (PW == 0 && dyn && lane == 0) qslot[(k + 1) & 3] = xcd_item(taken);
         barrier_keep_copies();
         for (int s = 0; s < S; ++s) {
           issue_a(s + NA - 1);

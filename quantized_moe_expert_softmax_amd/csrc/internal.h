@@ -11,9 +11,12 @@ namespace moe {
 constexpr int kSortBlock = 256;  // tokens per sort workgroup
 constexpr int kFrontMaxT = 16;   // largest T routed/sorted/quantised by one fused launch
 constexpr int kMTile = 16;       // rows per MFMA m-tile
-// Head of the fused launch's sync region: [0] set when a wait gave up (a
-// guard; never expected), then one GEMM1 completion count per m-tile.
-constexpr int kSyncHead = 1;
+// Head of the sync region (zeroed by the routing launch of every call): [0]
+// set when a fused-launch wait gave up (a guard; never expected), [1, 9) the
+// tiled GEMM1's per-XCD item counters, [9, 17) GEMM2's; then the fused
+// launch's GEMM1 completion count per m-tile.
+constexpr int kQueueBase = 1;
+constexpr int kSyncHead = kQueueBase + 16;
 constexpr int kUnit = 32;        // h columns per GEMM1 work unit (one requant block)
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -43,7 +46,7 @@ struct WsLayout {
   size_t mtoff;   // [E+1] int32 prefix sum of m-blocks per expert
   size_t mbexp;   // [N/16 + E] int32 expert of each m-block
   size_t wsorted; // [N] fp32 routing weight of sorted row p (assignment perm[p])
-  size_t sync;    // [kSyncHead + N/16 + E + 1] int32 of the fused launch (zeroed before it)
+  size_t sync;    // [kSyncHead + N/16 + E + 1] int32: item counters, fused-launch sync (zeroed per call)
   size_t total;
   int nb;
 };
