@@ -119,10 +119,11 @@ def copy_calibration(torch, mib, reps=3):
 
 
 def gemm_source_hash(variant=1):
-    """Hash of the sources of GEMM1's plan variant (0 stream, 1 tiled)."""
+    """Hash of the sources of GEMM1's plan variant (1 tiled; 0 stream, 2 fused and 3 decode run
+    the stream GEMM1)."""
     import hashlib
     h = hashlib.sha256()
-    for f in GEMM_SOURCES[variant]:
+    for f in GEMM_SOURCES[1 if variant == 1 else 0]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
