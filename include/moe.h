@@ -294,8 +294,9 @@ moe_status moe_quant_act(const void *x, int T, int H, moe_act_dtype act, uint8_t
  * experts", Changes: tuned entries per token count; "add A4W4 and FP8 P2P
  * transport support to MegaMoE", Technical Details: BM profiles chosen by
  * token count).  A layer starts with an empty table; calls no entry matches
- * use the built-in choice (stream below 2 rows per expert, else tiled with
- * BM from the expected expert load, at least 64 rows).  Every plan computes the same result
+ * use the built-in choice (below 2 rows per expert: decode for T <= 2, else
+ * stream; otherwise tiled with BM from the expected expert load, at least 64
+ * rows).  Every plan computes the same result
  * (parity is tested per plan); plans differ only in speed. */
 typedef enum {
     MOE_PLAN_STREAM = 0, /* 16-row m-tiles, K split over the waves, weights to VGPRs */
@@ -312,7 +313,7 @@ typedef enum {
                             moe_fused_status reports it.  Opt-in: never the
                             built-in choice, nor the tuner's unless asked */
     MOE_PLAN_DECODE = 3  /* the stream GEMM1, then GEMM2 token-major: a work item
-                            is (token, 64 output columns) over all its top_k
+                            is (token, 32 output columns) over all its top_k
                             experts, which sums the token's weighted rows in
                             FP32 in slot order and writes y itself (no combine
                             launch; "feat(moe): FlyDSL MegaMoE fused EP-MoE

@@ -183,12 +183,14 @@ __global__ __launch_bounds__(64 * NW) void gemm2_kernel(KArgs p) {
 // staging row (the layout the combine kernel reads) and writes
 // y[t] = bf16 of the FP32 sum of the weighted rows in slot order: the
 // combine kernel's result, without its launch or its reads of the staging.
-// Measured on the 7168 x 3072, 384 x 6 layer (us per call, eager, one box):
-// T = 1: 58.5 against 55.0 for the stream plan (224 items for 256 CUs read
-// six experts each: fewer, longer items than the stream GEMM2's 672); T = 2:
-// 94.7 against 99.6; T = 3 .. 8: 3-5% slower (experts two tokens share are
-// read twice).  So it is an opt-in plan the tuner may pick, not the built-in
-// choice.
+// With eight waves per item it measured on the 7168 x 3072, 384 x 6 layer
+// (us per call, eager, one box) T = 1: 58.5 against 55.0 for the stream plan
+// (224 items for 256 CUs read six experts each: fewer, longer items than the
+// stream GEMM2's 672); T = 2: 94.7 against 99.6; T = 3 .. 8: 3-5% slower
+// (experts two tokens share are read twice).  With sixteen waves when there
+// is at most one item per CU (one token) it is faster at T = 1 too, and the
+// built-in choice for T <= 2 (choose_plan); 16-column items measured 5-20%
+// slower than 32-column ones.
 // ---------------------------------------------------------------------------
 // Operands of four (slot, K step) pairs of one token's token-major GEMM2 item.
 template <int TPI>
@@ -487,7 +489,12 @@ GemmPlan choose_plan(int T, int top_k, int E, int act) {
   // more than ~2%.
   const long N = (long)T * top_k;
   const double avg = (double)N / E;
-  if (avg < 2.0) return GemmPlan{false, 1, 1};
+  // T <= 2: the token-major GEMM2 with the combine folded in (one launch
+  // fewer), sixteen waves per item at one token; measured faster than two
+  // launches on every measured layer at T = 1 and 2 (7168 x 3072: 53.6 ->
+  // 52.9 and 92.9 -> 90.5 us per call; the 5120 x {640, 1152} shards 3-12%)
+  // and 3-5% slower from T = 3 (experts two tokens share are read twice)
+  if (avg < 2.0) return T <= 2 ? GemmPlan{false, 1, 1, false, true} : GemmPlan{false, 1, 1};
   const double want = avg + 1.5 * sqrt(avg);
   {
     int mt = (int)ceil(want / 16.0);
@@ -597,8 +604,13 @@ hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s) {
     const long items = (long)a.T * (a.H / 32);
     const long cap = 2L * a.num_cus;
     const unsigned grid = (unsigned)(items < cap ? items : cap);
-    if (a.act == MOE_ACT_MXFP8_E4M3) gemm2_tm_kernel<0, 8, 2><<<grid, 512, 0, s>>>(k);
-    else gemm2_tm_kernel<4, 8, 2><<<grid, 512, 0, s>>>(k);
+    if (items <= a.num_cus) {
+      if (a.act == MOE_ACT_MXFP8_E4M3) gemm2_tm_kernel<0, 16, 2><<<grid, 1024, 0, s>>>(k);
+      else gemm2_tm_kernel<4, 16, 2><<<grid, 1024, 0, s>>>(k);
+    } else {
+      if (a.act == MOE_ACT_MXFP8_E4M3) gemm2_tm_kernel<0, 8, 2><<<grid, 512, 0, s>>>(k);
+      else gemm2_tm_kernel<4, 8, 2><<<grid, 512, 0, s>>>(k);
+    }
     return hipGetLastError();
   }
   const long items = a.max_mtiles * (a.H / 64);

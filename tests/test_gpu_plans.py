@@ -56,12 +56,15 @@ def test_table_lookup_order_and_fallback():
 
 # The built-in choice on the layer shapes it was measured on (7168 x 3072 with
 # E = 384, top_k = 6; the 5120 x {640, 1152} shards with E = 384 x 6 and
-# 128 x 3): weight streaming below 2 rows per expert, tiled at least 64 rows,
+# 128 x 3): weight streaming below 2 rows per expert (with the token-major
+# GEMM2 at T <= 2), tiled at least 64 rows,
 # BM covering the mean plus 1.5 sigma up to 160 rows, and above that the tile
 # with the fewest expected padded rows.  It depends on T, top_k and E only.
 BUILTIN = [
     # (E, top_k, T, variant, rows)
-    (384, 6, 1, moe.MOE_PLAN_STREAM, 16),
+    (384, 6, 1, moe.MOE_PLAN_DECODE, 16),      # T <= 2: token-major GEMM2, combine folded in
+    (384, 6, 2, moe.MOE_PLAN_DECODE, 16),
+    (384, 6, 3, moe.MOE_PLAN_STREAM, 16),
     (384, 6, 127, moe.MOE_PLAN_STREAM, 16),    # 1.98 rows per expert
     (384, 6, 128, moe.MOE_PLAN_TILED, 64),     # 2 rows: tiled, at the 64-row minimum
     (384, 6, 1024, moe.MOE_PLAN_TILED, 64),
