@@ -152,7 +152,18 @@ __device__ __forceinline__ void store_item(const KArgs &p, const v4f (&acc)[MTW]
 // T = 16384 and 2.5% on the 5120 x 640 shard than one wave per quad, equal
 // on the 7168 x 3072 layer at A8W4 T = 4096 and 8192.
 constexpr int kPcProducers = 2, kPcActStages = 4, kPcWStages = 4, kPcRowSplit = 2;
-template <int FMT, int MT>
+// Activation scales (SG): a row's E8M0 bytes of one K step are one dword, so
+// a step's scale copies gather 4 bytes from each of BM rows (64 rows, 64
+// cache lines, per copy), which on this device costs about as much per copy
+// as a whole 1 KiB activation chunk.  Where K / 128 is a multiple of four,
+// the copies instead take 16 bytes per row, the scales of four K steps (a
+// group), one 64-row part of the next group per step, into three rotating
+// group buffers (group g is read in steps 4g .. 4g + 3; its parts are issued
+// with steps 4g - 4 .. 4g - 1, so the ring's step wait covers them, and the
+// buffer they fill was last read in steps 4g - 12 .. 4g - 9, before any of
+// them is issued).  Rows past a part's 64 (BM not a multiple of 64, fewer
+// than four parts) repeat the last part: the same bytes to the same place.
+template <int FMT, int MT, bool SG = false>
 struct PcShape {
   static constexpr int NP = kPcProducers;             // producer waves
   static constexpr int RS = kPcRowSplit;              // consumer waves per weight quad
@@ -165,32 +176,36 @@ struct PcShape {
   static constexpr int A_BYTES = BM * ROWB;
   static constexpr int A_CHUNKS = A_BYTES / 1024;     // 1 KiB copies per stage
   static constexpr int SC = (BM + 63) / 64;           // scale copies per stage (64 rows each)
-  static constexpr int CA_ALL = A_CHUNKS + SC;        // activation copies per step
+  static constexpr int CA_ALL = A_CHUNKS + (SG ? 1 : SC);  // activation copies per step
   static constexpr int CA = (CA_ALL + NP - 1) / NP;   // per producer wave (the last repeats)
-  static constexpr int OFF_AS = A_BYTES;              // [BM] scale dwords
-  static constexpr int A_STAGE = A_BYTES + 1024;
+  static constexpr int OFF_AS = A_BYTES;              // [BM] scale dwords (not SG)
+  static constexpr int A_STAGE = A_BYTES + (SG ? 0 : 1024);
+  static constexpr int GRP = SC * 1024;               // SG: one group buffer, [64 SC rows][16 B]
+  static constexpr int NGRP = SG ? 3 : 0;
   static constexpr int CB = 4 / RS + 1;               // consumer copies per step (fragments, scale)
   static constexpr int OFF_BS = 4 * 4096;
   static constexpr int B_STAGE = OFF_BS + 4 * 256;
   // a 192-row MXFP8 tile (24 KiB a stage) keeps three activation stages so
   // that four weight stages still fit
   static constexpr int NA = A_BYTES > 20 * 1024 ? 3 : kPcActStages;
-  static constexpr int NB_FIT = (160 * 1024 - NA * A_STAGE) / B_STAGE;
+  static constexpr int GRP_BASE = NA * A_STAGE;
+  static constexpr int NB_FIT = (160 * 1024 - NA * A_STAGE - NGRP * GRP) / B_STAGE;
   static constexpr int NB = NB_FIT < kPcWStages ? NB_FIT : kPcWStages;
-  static constexpr int B_BASE = NA * A_STAGE;
+  static constexpr int B_BASE = GRP_BASE + NGRP * GRP;
   static constexpr int LDS = B_BASE + NB * B_STAGE;
   static_assert(A_BYTES % 1024 == 0, "activation tile must fill whole copies");
   static_assert(MT % RS == 0 && 4 % RS == 0, "even row split");
   static_assert(BM <= 256, "scale slots");
   static_assert(NB >= 3, "weight ring");
-  static_assert((NA - 1) * CA < 64 && (NB - 1) * CB < 64, "vmcnt range");
+  static_assert((NA - 1) * CA + 4 < 64 && (NB - 1) * CB < 64, "vmcnt range");
+  static_assert(!SG || SC <= 4, "four parts per group");
   static_assert(LDS + 16 <= 160 * 1024, "LDS");
 };
 
-template <int FMT, int MT, bool SECOND>
+template <int FMT, int MT, bool SECOND, bool SG>
 __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_kernel(KArgs p) {
   using F = typename ActFmt<FMT>::F;
-  using PS = PcShape<FMT, MT>;
+  using PS = PcShape<FMT, MT, SG>;
   constexpr int NA = PS::NA, NB = PS::NB, BM = PS::BM, ROWB = PS::ROWB, CH = PS::CH;
   // (one LDS object: the work-distribution slots sit after the rings; a
   // second __shared__ array made the compiler wait for every copy in flight
@@ -364,10 +379,38 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
       // repeats the last copy (same bytes to the same LDS address)
       auto produce = [&](auto pwc) __attribute__((always_inline)) {
         constexpr int PW = decltype(pwc)::value;
+        // copy index c of this wave: activation chunk i < A_CHUNKS, else a
+        // scale copy; an index past the last repeats a copy (SG: the last
+        // chunk, so that the group part is issued once per step)
+        auto copy_index = [&](int c) __attribute__((always_inline)) {
+          return PW * PS::CA + c < PS::CA_ALL ? PW * PS::CA + c
+                                             : (SG ? PS::A_CHUNKS - 1 : PS::CA_ALL - 1);
+        };
+        // SG: the wave issuing the group parts, and the offset of each part's
+        // row for this lane in 16-byte units (rows are whole units under SG)
+        constexpr bool GW = SG && PW * PS::CA <= PS::A_CHUNKS && PS::A_CHUNKS < PW * PS::CA + PS::CA;
+        uint32_t gro[4];
+        if (GW) {
+#pragma unroll
+          for (int part = 0; part < 4; ++part) {
+            const int row = min(64 * min(part, PS::SC - 1) + lane, BM - 1);
+            const int rr = min(row, nrows - 1);
+            const size_t ridx =
+                SECOND ? (size_t)(row0 + rr) : (size_t)(p.perm[row0 + rr] / p.top_k);
+            gro[part] = (uint32_t)(ridx * (srow / 16));
+          }
+        }
+        // part `part` of group gi (data of group min(gi, last)) into its buffer
+        auto issue_group = [&](int part, int gi) __attribute__((always_inline)) {
+          const int gd = min(gi, S / 4 - 1);
+          const uint32_t ro = part == 0 ? gro[0] : part == 1 ? gro[1] : part == 2 ? gro[2] : gro[3];
+          copy16_to_lds(As + 16 * ((size_t)ro + gd),
+                        lds + PS::GRP_BASE + (gi % 3) * PS::GRP + 1024 * min(part, PS::SC - 1));
+        };
         const uint8_t *csrc[PS::CA];
 #pragma unroll
         for (int c = 0; c < PS::CA; ++c) {
-          const int i = PW * PS::CA + c < PS::CA_ALL ? PW * PS::CA + c : PS::CA_ALL - 1;
+          const int i = copy_index(c);
           const bool chunk = i < PS::A_CHUNKS;
           const int ci = i * 64 + lane;  // 16-byte LDS chunk this lane fills
           const int row = chunk ? ci / CH : min(64 * (i - PS::A_CHUNKS) + lane, BM - 1);
@@ -387,13 +430,21 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
           uint8_t *stg = lds + (st % NA) * PS::A_STAGE;
 #pragma unroll
           for (int c = 0; c < PS::CA; ++c) {
-            const int i = PW * PS::CA + c < PS::CA_ALL ? PW * PS::CA + c : PS::CA_ALL - 1;
+            const int i = copy_index(c);
             if (i < PS::A_CHUNKS)
               copy16_to_lds(csrc[c] + (size_t)ROWB * sr, stg + i * 1024);
+            else if (SG)
+              issue_group(st & 3, (st >> 2) + 1);  // part st % 4 of the next group
             else
               copy4_to_lds(csrc[c] + 4 * sr, stg + PS::OFF_AS + 256 * (i - PS::A_CHUNKS));
           }
         };
+        // SG: group 0 before the first steps (older than step 0's copies, so
+        // the wait for step 0 covers it)
+        if (GW) {
+#pragma unroll
+          for (int part = 0; part < PS::SC; ++part) issue_group(part, 0);
+        }
 #pragma unroll
         for (int st = 0; st < NA - 1; ++st) issue_a(st);
         wait_vm<(NA - 2) * PS::CA>();  // step 0 has landed
@@ -427,8 +478,11 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
         }
         return a;
       };
+      // the scale byte of this lane's row and block g: st is the step's stage
+      // (its scale dwords), or with SG the step's dword column of its group
+      // buffer
       auto read_sa = [&](const uint8_t *st, int m) __attribute__((always_inline)) {
-        return (int)st[PS::OFF_AS + 4 * (16 * m + r16) + g];
+        return SG ? (int)st[16 * (16 * m + r16) + g] : (int)st[PS::OFF_AS + 4 * (16 * m + r16) + g];
       };
       if (!XITEM) {
         cw = w;
@@ -470,12 +524,14 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
         };
         for (int s = 0; s < S; ++s) {
           const uint8_t *st = lds + (s % NA) * PS::A_STAGE;
+          const uint8_t *ss =
+              SG ? lds + PS::GRP_BASE + ((s >> 2) % 3) * PS::GRP + 4 * (s & 3) : st;
           int sb;
           v8i b[4];
           read_b(rslot, b, sb);
           rslot = rslot + 1 == NB ? 0 : rslot + 1;
           v8i acur = read_a(st, MW0);
-          int sacur = read_sa(st, MW0);
+          int sacur = read_sa(ss, MW0);
   #pragma unroll
           for (int m = 0; m < MTW; ++m) {
   #pragma unroll
@@ -484,7 +540,7 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
             int sanext = sacur;
             if (m + 1 < MTW) {
               anext = read_a(st, MW0 + m + 1);
-              sanext = read_sa(st, MW0 + m + 1);
+              sanext = read_sa(ss, MW0 + m + 1);
             }
   #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -512,12 +568,12 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
   wait_vm<0>();  // no copy into this workgroup's LDS outlives it
 }
 
-template <bool SECOND>
+template <bool SECOND, bool SG>
 static hipError_t launch_pc(const GemmArgs &a, const KArgs &k, hipStream_t s) {
   const unsigned grid = (unsigned)(a.num_cus / 8 * 8);  // one workgroup per CU
 #define PC(F_, MT_)                                          \
   case MT_:                                                  \
-    pc_kernel<F_, MT_, SECOND><<<grid, 64 * PcShape<F_, MT_>::NWAVES, 0, s>>>(k); \
+    pc_kernel<F_, MT_, SECOND, SG><<<grid, 64 * PcShape<F_, MT_, SG>::NWAVES, 0, s>>>(k); \
     break;
   if (a.act == MOE_ACT_MXFP8_E4M3) {
     switch (a.plan.mt) {
@@ -537,7 +593,14 @@ static hipError_t launch_pc(const GemmArgs &a, const KArgs &k, hipStream_t s) {
 template <bool SECOND>
 static hipError_t launch_tiled(const GemmArgs &a, const KArgs &k, hipStream_t s) {
   if (a.plan.split != kTiledSplit) return hipErrorInvalidValue;
-  return launch_pc<SECOND>(a, k, s);
+  // scale groups: whole groups of four K steps, and 16-byte aligned rows;
+  // not at 192 MXFP8 rows, where the group addresses made the kernel spill
+  // registers (2-5% slower per call on the 5120 x 640 shard at T = 32768)
+  const int S = (SECOND ? a.I : a.H) / 128;
+  const uint8_t *as = SECOND ? a.a2s : a.a1s;
+  const bool sg = S % 4 == 0 && reinterpret_cast<uintptr_t>(as) % 16 == 0 &&
+                  !(a.act == MOE_ACT_MXFP8_E4M3 && a.plan.mt == 12);
+  return sg ? launch_pc<SECOND, true>(a, k, s) : launch_pc<SECOND, false>(a, k, s);
 }
 
 hipError_t launch_tiled_gemm1(const GemmArgs &a, const KArgs &k, hipStream_t s) {

@@ -200,6 +200,29 @@ def test_prequant_entry(T, H, I, E, k, combine, act):
     assert np.array_equal(yq, y)
 
 
+@pytest.mark.parametrize("act", [0, 1])
+def test_prequant_scales_4_byte_aligned(act):
+    """Token scales at a 4-byte but not 16-byte aligned address (allowed by the
+    prequant entry) take the tiled GEMM1's per-step scale copies instead of the
+    16-byte ones of four K steps (H = 512 would allow those): same output as
+    the BF16 entry, bit for bit."""
+    import torch
+    T, H, I, E, k = 130, 512, 640, 32, 8
+    w, x, lg = _small(T, H, I, E, k, seed=21 + act)
+    layer = _layer(*w)
+    assert moe.moe_get_plan(layer, T, k, act)["variant"] == moe.MOE_PLAN_TILED
+    y, _, _ = forward_and_check(layer, x, lg, k, act, host_weights(w),
+                                what="prequant-4-aligned act=%d" % act)
+    xc, xs = oracle.mx_quantize_bf16(x, act)
+    buf = torch.zeros(xs.size + 64, dtype=torch.uint8, device="cuda")
+    xs_dev = buf[4:4 + xs.size].view(xs.shape)
+    xs_dev.copy_(torch.from_numpy(np.ascontiguousarray(xs)))
+    assert xs_dev.data_ptr() % 16 == 4
+    yq = moe.moe_forward_prequant(layer, dev(xc), xs_dev, dev(lg), k, act)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host_bits(yq), y)
+
+
 def test_graph_capture_replays():
     """moe_forward captured into a HIP graph replays to the eager result, repeatedly."""
     import torch

@@ -158,6 +158,26 @@ def test_fused_plan(T, H, I, E, k, act):
     assert np.array_equal(bf16_host_bits(y2), y)
 
 
+# Tiled plans where K / 128 is a multiple of four, so that the activation
+# scales are copied four K steps at a time (H = 512, I = 512: one such group
+# in each GEMM; H = 1024, I = 1536: two and three), every tile height in both
+# formats, with partial m-blocks at every height.
+SCALE_GROUP_SHAPES = [(700, 512, 512, 16, 4), (300, 1024, 1536, 8, 2)]
+
+
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("T,H,I,E,k", SCALE_GROUP_SHAPES)
+def test_tiled_scale_groups(T, H, I, E, k, act):
+    w, x, lg = _small(T, H, I, E, k, seed=T + H + act)
+    layer = _layer(*w)
+    for variant, rows in tune.candidates(act):
+        if variant != moe.MOE_PLAN_TILED:
+            continue
+        moe.moe_set_plans(layer, [dict(act=act, top_k=k, t_max=T, variant=variant, rows=rows)])
+        forward_and_check(layer, x, lg, k, act, host_weights(w),
+                          what="tiled rows=%d T=%d H=%d I=%d act=%d" % (rows, T, H, I, act))
+
+
 # Tiled plans with more items than workgroups (one per CU, 256) and K of 1 or 2
 # steps of 128: a consumer wave's weight copies run NB - 1 = 3 steps ahead,
 # so they reach into the next item and the one after it (MT <= 8), or
