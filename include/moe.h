@@ -242,9 +242,12 @@ typedef enum {
                            by expert, ascending within an expert             */
     MOE_WS_A1_CODES,    /* [T][H] (E4M3) or [T][H/2] (E2M1) token codes      */
     MOE_WS_A1_SCALES,   /* [T][H/32] E8M0                                    */
-    MOE_WS_A2_CODES,    /* [T*top_k][I] or [..][I/2] SwiGLU codes, row p is
-                           the assignment perm[p]                           */
-    MOE_WS_A2_SCALES,   /* [T*top_k][I/32] E8M0, same rows                   */
+    MOE_WS_A2_CODES,    /* SwiGLU codes of sorted row p (the assignment
+                           perm[p]), K-step-major: [I/128][T*top_k][128]
+                           E4M3 or [I/128][T*top_k][64] packed E2M1 (K step
+                           s of every row, then step s + 1)                 */
+    MOE_WS_A2_SCALES,   /* [I/128][T*top_k][4] E8M0, the same rows and steps
+                           (the four 1x32 blocks of a step)                 */
     MOE_WS_ROWS,        /* [T*top_k][H] GEMM2 rows times their routing weight,
                            row p is the assignment perm[p]: fp32 (FP32
                            transport), bf16 (BF16), or E4M3 codes followed by

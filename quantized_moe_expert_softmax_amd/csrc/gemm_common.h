@@ -66,6 +66,23 @@ struct KArgs {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// A2 layout.  The SwiGLU codes GEMM1 writes and GEMM2 reads are stored
+// K-step-major: K step s of GEMM2 (columns [128 s, 128 s + 128) of I) holds
+// the N = T * top_k sorted rows' bytes of that step one after another --
+// codes [I/128][N][128] (E4M3) or [I/128][N][64] (packed E2M1), scales
+// [I/128][N][4] (the step's four E8M0 block bytes) -- so the rows of an
+// m-block, which GEMM2 reads one step at a time, are one contiguous run per
+// step.  (From row-major rows the tiled GEMM2's copies of a step gathered
+// 16-row pieces and one scale dword per row from separate cache lines:
+// 8.7% slower per GEMM2 at A4W4, T = 16384.)
+template <int FMT>
+__device__ __forceinline__ size_t a2c_at(size_t row, int s, size_t N) {
+  return ((size_t)s * N + row) * (FMT == 0 ? 128 : 64);
+}
+__device__ __forceinline__ size_t a2s_at(size_t row, int s, size_t N) {
+  return ((size_t)s * N + row) * 4;
+}
+
 // A weight fragment (16 bytes of a lane) or scale dword of the stream GEMMs,
 // loaded with the non-temporal hint: each is read once per call, and
 // streaming them past the caches leaves those to the activation rows
@@ -160,32 +177,34 @@ __device__ __forceinline__ void swiglu_codes_n(const float (&glo)[NR], const flo
 }
 
 // h = silu(gate) * up; the 32 h values of the row form one 1x32 block (amax
-// over the 16 lanes), requantised and stored to the A2 row.  All lanes call
+// over the 16 lanes), requantised and stored as block j of sorted row rows[i]
+// of A2 (N rows; block j is block j % 4 of K step j / 4).  All lanes call
 // and store: the two lanes of an E2M1 byte both write it whole, all 16 lanes
 // write the scale byte, and a padded row (computed from the last valid row's
 // data) rewrites that row's values, so no store needs a branch.
 template <class F, int FMT, int NR, bool COH = false>
 __device__ __forceinline__ void swiglu_requant_n(const float (&glo)[NR], const float (&ghi)[NR],
                                                  const float (&ulo)[NR], const float (&uhi)[NR],
-                                                 uint8_t *const (&a2row)[NR],
-                                                 uint8_t *const (&a2srow)[NR], int j, int c) {
+                                                 uint8_t *a2c, uint8_t *a2s,
+                                                 const size_t (&rows)[NR], size_t N, int j, int c) {
   uint32_t clo[NR], chi[NR];
   int X[NR];
   swiglu_codes_n<F, NR>(glo, ghi, ulo, uhi, clo, chi, X);
+  const int s = j >> 2, jb = j & 3;
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
+    uint8_t *cr = a2c + a2c_at<FMT>(rows[i], s, N);
     if (FMT == 0) {
-      store_u8<COH>(a2row[i] + 32 * j + c, clo[i]);
-      store_u8<COH>(a2row[i] + 32 * j + 16 + c, chi[i]);
+      store_u8<COH>(cr + 32 * jb + c, clo[i]);
+      store_u8<COH>(cr + 32 * jb + 16 + c, chi[i]);
     } else {
       const uint32_t plo = dpp<0xB1>(clo[i]);  // code of lane c ^ 1
       const uint32_t phi = dpp<0xB1>(chi[i]);
       const bool odd = c & 1;
-      store_u8<COH>(a2row[i] + 16 * j + c / 2, odd ? (plo | (clo[i] << 4)) : (clo[i] | (plo << 4)));
-      store_u8<COH>(a2row[i] + 16 * j + 8 + c / 2,
-                    odd ? (phi | (chi[i] << 4)) : (chi[i] | (phi << 4)));
+      store_u8<COH>(cr + 16 * jb + c / 2, odd ? (plo | (clo[i] << 4)) : (clo[i] | (plo << 4)));
+      store_u8<COH>(cr + 16 * jb + 8 + c / 2, odd ? (phi | (chi[i] << 4)) : (chi[i] | (phi << 4)));
     }
-    store_u8<COH>(a2srow[i] + j, (uint32_t)(X[i] + 127));
+    store_u8<COH>(a2s + a2s_at(rows[i], s, N) + jb, (uint32_t)(X[i] + 127));
   }
 }
 
@@ -278,11 +297,11 @@ __device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t d, int j) {
 // 32 unit + 16 + c; after a byte transpose in each quad, lane (k, jq) holds
 // row 4g + jq's codes of columns 4k .. 4k+3 (and 16 + 4k ..), stored as two
 // dwords, plus the row's scale byte (the four lanes of a row write the same
-// byte).  a2row / a2srow: the A2 code and scale rows of the lane's row.
+// byte).  crow / srow: the lane's row's A2 codes and scale dword of the K
+// step holding the unit; jb = unit % 4, the unit's block in that step.
 __device__ __forceinline__ void swiglu_store_f8_t(const float (&glo)[4], const float (&ghi)[4],
                                                   const float (&ulo)[4], const float (&uhi)[4],
-                                                  uint8_t *a2row, uint8_t *a2srow, int unit,
-                                                  int c) {
+                                                  uint8_t *crow, uint8_t *srow, int jb, int c) {
   uint32_t clo[4], chi[4];
   int X[4];
   swiglu_codes_n<E4M3, 4>(glo, ghi, ulo, uhi, clo, chi, X);
@@ -290,9 +309,9 @@ __device__ __forceinline__ void swiglu_store_f8_t(const float (&glo)[4], const f
   const uint32_t lo = quad_transpose_bytes(clo[0] | (clo[1] << 8) | (clo[2] << 16) | (clo[3] << 24), jq);
   const uint32_t hi = quad_transpose_bytes(chi[0] | (chi[1] << 8) | (chi[2] << 16) | (chi[3] << 24), jq);
   const int Xr = jq == 0 ? X[0] : jq == 1 ? X[1] : jq == 2 ? X[2] : X[3];
-  *reinterpret_cast<uint32_t *>(a2row + 32 * unit + 4 * (c >> 2)) = lo;
-  *reinterpret_cast<uint32_t *>(a2row + 32 * unit + 16 + 4 * (c >> 2)) = hi;
-  a2srow[unit] = (uint8_t)(Xr + 127);
+  *reinterpret_cast<uint32_t *>(crow + 32 * jb + 4 * (c >> 2)) = lo;
+  *reinterpret_cast<uint32_t *>(crow + 32 * jb + 16 + 4 * (c >> 2)) = hi;
+  srow[jb] = (uint8_t)(Xr + 127);
 }
 
 // Tiled (prefill) variant, in gemm_tiled.hip.

@@ -5,17 +5,18 @@
 
 namespace moe {
 
-// A operand of K step s for lane group g from a row-major code row.
+// A operand for lane group g from a row's codes of one K step (128 E4M3
+// bytes or 64 packed E2M1 bytes at `step`).
 template <int FMT>
-__device__ __forceinline__ v8i load_a(const uint8_t *__restrict__ row, int s, int g) {
+__device__ __forceinline__ v8i load_a(const uint8_t *__restrict__ step, int g) {
   v8i a;
   if (FMT == 0) {
-    const uint4 lo = *reinterpret_cast<const uint4 *>(row + 128 * s + 16 * g);
-    const uint4 hi = *reinterpret_cast<const uint4 *>(row + 128 * s + 64 + 16 * g);
+    const uint4 lo = *reinterpret_cast<const uint4 *>(step + 16 * g);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(step + 64 + 16 * g);
     a[0] = (int)lo.x; a[1] = (int)lo.y; a[2] = (int)lo.z; a[3] = (int)lo.w;
     a[4] = (int)hi.x; a[5] = (int)hi.y; a[6] = (int)hi.z; a[7] = (int)hi.w;
   } else {
-    const uint4 lo = *reinterpret_cast<const uint4 *>(row + 64 * s + 16 * g);
+    const uint4 lo = *reinterpret_cast<const uint4 *>(step + 16 * g);
     a[0] = (int)lo.x; a[1] = (int)lo.y; a[2] = (int)lo.z; a[3] = (int)lo.w;
     a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
   }
@@ -23,34 +24,71 @@ __device__ __forceinline__ v8i load_a(const uint8_t *__restrict__ row, int s, in
 }
 
 // acc[q] += A(rows of this lane's m-tile) x B(prepacked tile q of one quad)
-// over the K steps [s0, s1), four steps per unrolled group.
-template <int FMT>
+// over K steps [s, s + G): every load of the G steps (A operand, its scale
+// byte, the weight scale dword, four weight fragments per step) is issued
+// before the first MFMA, so a wave keeps 7G loads in flight.  (With a
+// conditional per step the compiler issued each step's weight fragments one
+// or two at a time behind the previous MFMA, and how many it overlapped
+// changed with unrelated edits: the K-step-major A2 layout moved GEMM2 at
+// T = 64 from two to one and cost 17%.)  arow / asrow: the lane's row's
+// codes and scale dword of K step 0; K step s is cstep / sstep bytes further
+// (a row-major A1 row: the step's code bytes and 4; A2: N times those).
+template <int FMT, int G>
+__device__ __forceinline__ void mma_group(v4f acc[4], const uint8_t *__restrict__ arow,
+                                          const uint8_t *__restrict__ asrow, size_t cstep,
+                                          size_t sstep, const uint8_t *__restrict__ wt,
+                                          const uint32_t *__restrict__ wsq, int s, int lane) {
+  const int g = lane >> 4;
+  v8i a[G];
+  int sa[G], sb[G];
+  u32x4 b[G][4];
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    const size_t st = (size_t)(s + u);
+    a[u] = load_a<FMT>(arow + cstep * st, g);
+    sa[u] = asrow[sstep * st + g];
+    sb[u] = load_weight_scales(wsq + st * 64 + lane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[u][q] = load_weights16(wt + st * 4096 + q * 1024 + lane * 16);
+  }
+  // keep the scheduler from sinking loads between the MFMAs
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < G; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v8i bq;
+      bq[0] = (int)b[u][q][0]; bq[1] = (int)b[u][q][1]; bq[2] = (int)b[u][q][2]; bq[3] = (int)b[u][q][3];
+      bq[4] = 0; bq[5] = 0; bq[6] = 0; bq[7] = 0;
+      acc[q] = mfma_q<FMT>(q, a[u], bq, acc[q], sa[u], sb[u]);
+    }
+}
+
+// The K steps [s0, s1) in groups of G, then one group of the remaining
+// 1 .. G - 1 steps (G is 1, 2 or 4).
+template <int FMT, int G>
 __device__ __forceinline__ void mma_4tiles(v4f acc[4], const uint8_t *__restrict__ arow,
-                                           const uint8_t *__restrict__ asrow,
-                                           const uint8_t *__restrict__ wt,
+                                           const uint8_t *__restrict__ asrow, size_t cstep,
+                                           size_t sstep, const uint8_t *__restrict__ wt,
                                            const uint32_t *__restrict__ wsq, int s0, int s1,
                                            int lane) {
-  const int g = lane >> 4;
-  for (int s4 = s0; s4 < s1; s4 += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s4 + u;
-      if (s < s1) {
-        const v8i a = load_a<FMT>(arow, s, g);
-        const int sa = asrow[4 * s + g];
-        const int sb = load_weight_scales(wsq + (size_t)s * 64 + lane);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 bq = load_weights16(wt + (size_t)s * 4096 + q * 1024 + lane * 16);
-          v8i b;
-          b[0] = (int)bq[0]; b[1] = (int)bq[1]; b[2] = (int)bq[2]; b[3] = (int)bq[3];
-          b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
-          acc[q] = mfma_q<FMT>(q, a, b, acc[q], sa, sb);
-        }
-      }
-    }
-  }
+  static_assert(G == 1 || G == 2 || G == 4, "group size");
+  int s = s0;
+  for (; s + G <= s1; s += G) mma_group<FMT, G>(acc, arow, asrow, cstep, sstep, wt, wsq, s, lane);
+  const int r = s1 - s;
+  if (G == 4 && r == 3) mma_group<FMT, 3>(acc, arow, asrow, cstep, sstep, wt, wsq, s, lane);
+  if (G == 4 && r == 2) mma_group<FMT, 2>(acc, arow, asrow, cstep, sstep, wt, wsq, s, lane);
+  if (G > 1 && r == 1) mma_group<FMT, 1>(acc, arow, asrow, cstep, sstep, wt, wsq, s, lane);
 }
+
+// Steps per load group (mma_group) of the stream GEMMs.  Per call on the
+// decode sizes against the per-step loop with a conditional (eager us, one
+// box, two rounds): 5120 x 640 E = 384 T = 64 250 -> 229, E = 128 T = 8
+// 42.5 -> 38.0 and T = 64 114 -> 103, 5120 x 1152 T = 32 259 -> 240, 7168 x
+// 3072 T = 8 267 -> 257 and T = 64 equal.  Larger groups (GEMM1 2, GEMM2 4)
+// lowered occupancy for less: a GEMM1 of four-step groups held one 8-wave
+// workgroup per CU and was 17% slower on the 5120 x 640 shard at T = 64.
+constexpr int kStreamGroup1 = 1, kStreamGroup2 = 2;
 
 template <int FMT, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm1_kernel(KArgs p) {
@@ -63,7 +101,7 @@ __global__ __launch_bounds__(64 * NW) void gemm1_kernel(KArgs p) {
   const int S = p.H / 128;
   const int s0 = wave * S / NW, s1 = (wave + 1) * S / NW;
   const size_t a1row = FMT == 0 ? (size_t)p.H : (size_t)p.H / 2;
-  const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
+  const size_t N = (size_t)p.T * p.top_k;
   const size_t nquads = (size_t)(2 * p.I) / 64;
   // items m-tile major: consecutive workgroups stream consecutive quads of one
   // expert's weights (measured 2-3% faster at T = 8..64 than unit-major,
@@ -82,7 +120,8 @@ __global__ __launch_bounds__(64 * NW) void gemm1_kernel(KArgs p) {
     v4f acc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
-    mma_4tiles<FMT>(acc, arow, asrow, wt, wsq, s0, s1, lane);
+    mma_4tiles<FMT, kStreamGroup1>(acc, arow, asrow, FMT == 0 ? 128 : 64, 4, wt, wsq, s0, s1,
+                                   lane);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -99,16 +138,14 @@ __global__ __launch_bounds__(64 * NW) void gemm1_kernel(KArgs p) {
       const int c = lane & 15;
       // tiles: 0 = gate cols [32j, +16), 1 = gate [32j+16, +16), 2/3 = up
       float g0[4], g1[4], u0[4], u1[4];
-      uint8_t *ar[4], *sr[4];
+      size_t prow[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * (lane >> 4) + r;
-        const size_t prow = (size_t)(row0 + min(m, nrows - 1));
+        prow[r] = (size_t)(row0 + min(m, nrows - 1));
         g0[r] = v[0 * 4 + r]; g1[r] = v[1 * 4 + r]; u0[r] = v[2 * 4 + r]; u1[r] = v[3 * 4 + r];
-        ar[r] = p.a2c + prow * a2row;
-        sr[r] = p.a2s + prow * (p.I / 32);
       }
-      swiglu_requant_n<F, FMT, 4>(g0, g1, u0, u1, ar, sr, j, c);
+      swiglu_requant_n<F, FMT, 4>(g0, g1, u0, u1, p.a2c, p.a2s, prow, N, j, c);
     }
     __syncthreads();
   }
@@ -123,7 +160,7 @@ __global__ __launch_bounds__(64 * NW) void gemm2_kernel(KArgs p) {
   const long total = (long)n_mt * NB;
   const int S = p.I / 128;
   const int s0 = wave * S / NW, s1 = (wave + 1) * S / NW;
-  const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
+  const size_t N = (size_t)p.T * p.top_k;
   const size_t nquads = (size_t)p.H / 64;
   for (long w = blockIdx.x; w < total; w += gridDim.x) {  // m-tile major, as in GEMM1
     const int mt = (int)(w / NB), nb = (int)(w % NB);
@@ -131,14 +168,15 @@ __global__ __launch_bounds__(64 * NW) void gemm2_kernel(KArgs p) {
     const int row0 = uniform(p.offsets[e]) + kMTile * (mt - uniform(p.mtoff[e]));
     const int nrows = min(kMTile, uniform(p.offsets[e + 1]) - row0);
     const size_t pr = (size_t)(row0 + min(lane & 15, nrows - 1));
-    const uint8_t *arow = p.a2c + pr * a2row;
-    const uint8_t *asrow = p.a2s + pr * (p.I / 32);
+    const uint8_t *arow = p.a2c + a2c_at<FMT>(pr, 0, N);
+    const uint8_t *asrow = p.a2s + a2s_at(pr, 0, N);
     const uint8_t *wt = p.wp + ((size_t)e * nquads + nb) * (size_t)S * 4096;
     const uint32_t *wsq = p.wsp + ((size_t)e * nquads + nb) * (size_t)S * 64;
     v4f acc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
-    mma_4tiles<FMT>(acc, arow, asrow, wt, wsq, s0, s1, lane);
+    mma_4tiles<FMT, kStreamGroup2>(acc, arow, asrow, a2c_at<FMT>(0, 1, N), a2s_at(0, 1, N), wt,
+                                   wsq, s0, s1, lane);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -206,7 +244,7 @@ __global__ __launch_bounds__(64 * NW) void gemm2_tm_kernel(KArgs p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4;
   const int NB = p.H / (16 * TPI), k = p.top_k, S = p.I / 128, P = k * S;
   const int i0 = wave * P / NW, i1 = (wave + 1) * P / NW;
-  const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
+  const size_t N = (size_t)p.T * k;
   const size_t ntiles = (size_t)p.H / 16;
   const long total = (long)p.T * NB;
   for (long w = blockIdx.x; w < total; w += gridDim.x) {
@@ -233,8 +271,8 @@ __global__ __launch_bounds__(64 * NW) void gemm2_tm_kernel(KArgs p) {
           const int asg = t * k + j;
           const size_t e = (size_t)uniform(p.ids[asg]);
           const size_t pr = (size_t)uniform(p.inv[asg]);
-          G.a[u] = load_a<FMT>(p.a2c + pr * a2row, st, g);
-          G.sa[u] = p.a2s[pr * (p.I / 32) + 4 * st + g];
+          G.a[u] = load_a<FMT>(p.a2c + a2c_at<FMT>(pr, st, N), g);
+          G.sa[u] = p.a2s[a2s_at(pr, st, N) + g];
           const size_t qb = e * (ntiles / 4) + tile0 / 4;  // the item's tiles share a quad
 #pragma unroll
           for (int q = 0; q < TPI; ++q)
@@ -335,7 +373,8 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(KArgs p) {
   const long n1 = (long)n_mt * NU, total = n1 + (long)n_mt * NB2;
   const int S1 = p.H / 128, S2 = p.I / 128;
   const size_t a1row = FMT == 0 ? (size_t)p.H : (size_t)p.H / 2;
-  const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
+  const size_t N = (size_t)p.T * p.top_k;
+  constexpr int A2B = FMT == 0 ? 128 : 64;  // A2 code bytes of a row per K step
   const size_t nq1 = (size_t)(2 * p.I) / 64, nq2 = (size_t)p.H / 64;
   int *const flag = p.sync, *const done = p.sync + kSyncHead;
 
@@ -353,8 +392,9 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(KArgs p) {
       v4f acc[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
-      mma_4tiles<FMT>(acc, p.a1c + (size_t)tok * a1row, p.a1s + (size_t)tok * (p.H / 32), wt, wsq,
-                      s0, s1, lane);
+      mma_4tiles<FMT, kStreamGroup1>(acc, p.a1c + (size_t)tok * a1row,
+                                     p.a1s + (size_t)tok * (p.H / 32), FMT == 0 ? 128 : 64, 4, wt,
+                                     wsq, s0, s1, lane);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -369,15 +409,13 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(KArgs p) {
           for (int u = 1; u < NW; ++u) v[i] += red[u][i][lane];
         }
         float g0[4], g1[4], u0[4], u1[4];
-        uint8_t *ar[4], *sr[4];
+        size_t prow[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const size_t prow = (size_t)(row0 + min(4 * g + r, nrows - 1));
+          prow[r] = (size_t)(row0 + min(4 * g + r, nrows - 1));
           g0[r] = v[r]; g1[r] = v[4 + r]; u0[r] = v[8 + r]; u1[r] = v[12 + r];
-          ar[r] = p.a2c + prow * a2row;
-          sr[r] = p.a2s + prow * (p.I / 32);
         }
-        swiglu_requant_n<F, FMT, 4, true>(g0, g1, u0, u1, ar, sr, j, lane & 15);
+        swiglu_requant_n<F, FMT, 4, true>(g0, g1, u0, u1, p.a2c, p.a2s, prow, N, j, lane & 15);
         // publish: the coherent stores above have completed before the count
         __builtin_amdgcn_s_waitcnt(0);
         if (lane == 0)
@@ -405,13 +443,10 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(KArgs p) {
       }
       __syncthreads();
       // the m-tile's activation rows through device-coherent buffer loads
-      // (cache policy sc1), from a workgroup-uniform resource at its first row
+      // (cache policy sc1), from workgroup-uniform resources at its first row
+      // in each K step
       const int r = min(lane & 15, nrows - 1);
-      const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-          p.a2c + (size_t)row0 * a2row, (short)0, (int)(kMTile * a2row), kBufferFlags);
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          p.a2s + (size_t)row0 * (p.I / 32), (short)0, kMTile * (p.I / 32), kBufferFlags);
-      const int aoff = r * (int)a2row + 16 * g, soff = r * (p.I / 32) + g;
+      const int aoff = r * A2B + 16 * g, soff = r * 4 + g;
       v4f acc[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -421,18 +456,20 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(KArgs p) {
         for (int u = 0; u < 4; ++u) {
           const int st = s4 + u;
           if (st < s1) {
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                p.a2c + a2c_at<FMT>(row0, st, N), (short)0, kMTile * A2B, kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                p.a2s + a2s_at(row0, st, N), (short)0, kMTile * 4, kBufferFlags);
             v8i a;
-            const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(
-                ra, aoff + (FMT == 0 ? 128 : 64) * st, 0, kCoherent);
+            const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff, 0, kCoherent);
             a[0] = (int)lo[0]; a[1] = (int)lo[1]; a[2] = (int)lo[2]; a[3] = (int)lo[3];
             if (FMT == 0) {
-              const u32x4 hi =
-                  __builtin_amdgcn_raw_buffer_load_b128(ra, aoff + 128 * st + 64, 0, kCoherent);
+              const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff + 64, 0, kCoherent);
               a[4] = (int)hi[0]; a[5] = (int)hi[1]; a[6] = (int)hi[2]; a[7] = (int)hi[3];
             } else {
               a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
             }
-            const int sa = (int)__builtin_amdgcn_raw_buffer_load_b8(rs, soff + 4 * st, 0, kCoherent);
+            const int sa = (int)__builtin_amdgcn_raw_buffer_load_b8(rs, soff, 0, kCoherent);
             const int sb = load_weight_scales(wsq + (size_t)st * 64 + lane);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {

@@ -70,31 +70,31 @@ __device__ __forceinline__ int act_swizzle(int row) {
 template <class F, int FMT, int MTW, int NT, bool SECOND>
 __device__ __forceinline__ void store_item(const KArgs &p, const v4f (&acc)[MTW][NT], int u,
                                            int tile0, int mw0, int row0, int nrows, int g,
-                                           int r16, size_t a2row) {
+                                           int r16) {
   // the row of this lane after a quad transpose (dword-store epilogue)
   auto trow = [&](int m) __attribute__((always_inline)) {
     return (size_t)(row0 + min(16 * (mw0 + m) + 4 * g + (r16 & 3), nrows - 1));
   };
   if (!SECOND) {
     const int j = tile0 / 4;  // unit: h columns [32j, 32j + 32)
+    const size_t N = (size_t)p.T * p.top_k;
 #pragma unroll
     for (int m = 0; m < MTW; ++m) {
       float g0[4], g1[4], u0[4], u1[4];
-      uint8_t *ar[4], *sr[4];
+      size_t prow[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int mrow = 16 * (mw0 + m) + 4 * g + r;
-        const size_t prow = (size_t)(row0 + min(mrow, nrows - 1));
+        prow[r] = (size_t)(row0 + min(mrow, nrows - 1));
         g0[r] = acc[m][4 * u][r]; g1[r] = acc[m][4 * u + 1][r];
         u0[r] = acc[m][4 * u + 2][r]; u1[r] = acc[m][4 * u + 3][r];
-        ar[r] = p.a2c + prow * a2row;
-        sr[r] = p.a2s + prow * (p.I / 32);
       }
       if (FMT == 0) {
-        const size_t prow = trow(m);
-        swiglu_store_f8_t(g0, g1, u0, u1, p.a2c + prow * a2row, p.a2s + prow * (p.I / 32), j, r16);
+        const size_t tr = trow(m);
+        swiglu_store_f8_t(g0, g1, u0, u1, p.a2c + a2c_at<0>(tr, j >> 2, N),
+                          p.a2s + a2s_at(tr, j >> 2, N), j & 3, r16);
       } else {
-        swiglu_requant_n<F, FMT, 4>(g0, g1, u0, u1, ar, sr, j, r16);
+        swiglu_requant_n<F, FMT, 4>(g0, g1, u0, u1, p.a2c, p.a2s, prow, N, j, r16);
       }
     }
   } else {
@@ -152,17 +152,19 @@ __device__ __forceinline__ void store_item(const KArgs &p, const v4f (&acc)[MTW]
 // T = 16384 and 2.5% on the 5120 x 640 shard than one wave per quad, equal
 // on the 7168 x 3072 layer at A8W4 T = 4096 and 8192.
 constexpr int kPcProducers = 2, kPcActStages = 4, kPcWStages = 4, kPcRowSplit = 2;
-// Activation scales (SG): a row's E8M0 bytes of one K step are one dword, so
-// a step's scale copies gather 4 bytes from each of BM rows (64 rows, 64
-// cache lines, per copy), which on this device costs about as much per copy
-// as a whole 1 KiB activation chunk.  Where K / 128 is a multiple of four,
-// the copies instead take 16 bytes per row, the scales of four K steps (a
-// group), one 64-row part of the next group per step, into three rotating
-// group buffers (group g is read in steps 4g .. 4g + 3; its parts are issued
-// with steps 4g - 4 .. 4g - 1, so the ring's step wait covers them, and the
-// buffer they fill was last read in steps 4g - 12 .. 4g - 9, before any of
-// them is issued).  Rows past a part's 64 (BM not a multiple of 64, fewer
-// than four parts) repeat the last part: the same bytes to the same place.
+// Activation scales of GEMM1 (SG): a token row's E8M0 bytes of one K step
+// are one dword, so a step's scale copies gather 4 bytes from each of BM
+// rows (64 rows, 64 cache lines, per copy), which on this device costs about
+// as much per copy as a whole 1 KiB activation chunk.  (GEMM2's scales are
+// K-step-major: a step's 64 rows are one 256-byte run.)  Where K / 128 is a
+// multiple of four, the copies instead take 16 bytes per row, the scales of
+// four K steps (a group), one 64-row part of the next group per step, into
+// three rotating group buffers (group g is read in steps 4g .. 4g + 3; its
+// parts are issued with steps 4g - 4 .. 4g - 1, so the ring's step wait
+// covers them, and the buffer they fill was last read in steps 4g - 12 ..
+// 4g - 9, before any of them is issued).  Rows past a part's 64 (BM not a
+// multiple of 64, fewer than four parts) repeat the last part: the same
+// bytes to the same place.
 template <int FMT, int MT, bool SG = false>
 struct PcShape {
   static constexpr int NP = kPcProducers;             // producer waves
@@ -221,9 +223,13 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
   const int NBLK = (ntiles + 15) / 16;
   const int n_mb = uniform(p.mtoff[p.E]);
   const long total = (long)n_mb * NBLK;
+  // A1: token rows (row-major: K step s of a row at s times the step bytes);
+  // A2: K-step-major sorted rows (K step s of all N rows one block)
   const size_t arow = FMT == 0 ? (size_t)K : (size_t)K / 2;
   const size_t srow = (size_t)K / 32;
-  const size_t a2row = FMT == 0 ? (size_t)p.I : (size_t)p.I / 2;
+  const size_t NA2 = (size_t)p.T * p.top_k;
+  const size_t cstep = SECOND ? NA2 * ROWB : (size_t)ROWB;  // code bytes from a step to the next
+  const size_t sstep = SECOND ? NA2 * 4 : 4;                 // scale bytes from a step to the next
   const size_t quad_bytes = (size_t)S * 4096, quad_dwords = (size_t)S * 64;
   const uint8_t *__restrict__ A = SECOND ? p.a2c : p.a1c;
   const uint8_t *__restrict__ As = SECOND ? p.a2s : p.a1s;
@@ -417,8 +423,9 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
           const int rr = min(row, nrows - 1);
           const size_t ridx =
               SECOND ? (size_t)(row0 + rr) : (size_t)(p.perm[row0 + rr] / p.top_k);
-          csrc[c] = chunk ? A + ridx * arow + 16 * ((ci % CH) ^ act_swizzle<FMT>(row))
-                          : As + ridx * srow;
+          csrc[c] = chunk ? A + ridx * (SECOND ? (size_t)ROWB : arow) +
+                                16 * ((ci % CH) ^ act_swizzle<FMT>(row))
+                          : As + ridx * (SECOND ? (size_t)4 : srow);
         }
         // the first producer takes this workgroup's next item, after the row
         // gathers above (its reply is older than the first stages' copies, so
@@ -432,11 +439,11 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
           for (int c = 0; c < PS::CA; ++c) {
             const int i = copy_index(c);
             if (i < PS::A_CHUNKS)
-              copy16_to_lds(csrc[c] + (size_t)ROWB * sr, stg + i * 1024);
+              copy16_to_lds(csrc[c] + cstep * sr, stg + i * 1024);
             else if (SG)
               issue_group(st & 3, (st >> 2) + 1);  // part st % 4 of the next group
             else
-              copy4_to_lds(csrc[c] + 4 * sr, stg + PS::OFF_AS + 256 * (i - PS::A_CHUNKS));
+              copy4_to_lds(csrc[c] + sstep * sr, stg + PS::OFF_AS + 256 * (i - PS::A_CHUNKS));
           }
         };
         // SG: group 0 before the first steps (older than step 0's copies, so
@@ -557,7 +564,7 @@ __global__ __launch_bounds__(64 * (4 * kPcRowSplit + kPcProducers), 1) void pc_k
         // without XITEM the re-reads past the last step land before the next
         // item's first copies reuse their slots
         if (!XITEM) wait_vm<0>();
-        if (t0 < ntiles) store_item<F, FMT, MTW, 4, SECOND>(p, acc, 0, t0, MW0, row0, nrows, g, r16, a2row);
+        if (t0 < ntiles) store_item<F, FMT, MTW, 4, SECOND>(p, acc, 0, t0, MW0, row0, nrows, g, r16);
       };
       if (PS::RS == 1 || rh == 0)
         consume(std::integral_constant<int, 0>{});
@@ -593,14 +600,17 @@ static hipError_t launch_pc(const GemmArgs &a, const KArgs &k, hipStream_t s) {
 template <bool SECOND>
 static hipError_t launch_tiled(const GemmArgs &a, const KArgs &k, hipStream_t s) {
   if (a.plan.split != kTiledSplit) return hipErrorInvalidValue;
-  // scale groups: whole groups of four K steps, and 16-byte aligned rows;
-  // not at 192 MXFP8 rows, where the group addresses made the kernel spill
-  // registers (2-5% slower per call on the 5120 x 640 shard at T = 32768)
-  const int S = (SECOND ? a.I : a.H) / 128;
-  const uint8_t *as = SECOND ? a.a2s : a.a1s;
-  const bool sg = S % 4 == 0 && reinterpret_cast<uintptr_t>(as) % 16 == 0 &&
-                  !(a.act == MOE_ACT_MXFP8_E4M3 && a.plan.mt == 12);
-  return sg ? launch_pc<SECOND, true>(a, k, s) : launch_pc<SECOND, false>(a, k, s);
+  // GEMM2's scales are K-step-major (a step's rows contiguous): no groups
+  if constexpr (SECOND) {
+    return launch_pc<true, false>(a, k, s);
+  } else {
+    // scale groups: whole groups of four K steps, and 16-byte aligned rows;
+    // not at 192 MXFP8 rows, where the group addresses made the kernel spill
+    // registers (2-5% slower per call on the 5120 x 640 shard at T = 32768)
+    const bool sg = (a.H / 128) % 4 == 0 && reinterpret_cast<uintptr_t>(a.a1s) % 16 == 0 &&
+                    !(a.act == MOE_ACT_MXFP8_E4M3 && a.plan.mt == 12);
+    return sg ? launch_pc<false, true>(a, k, s) : launch_pc<false, false>(a, k, s);
+  }
 }
 
 hipError_t launch_tiled_gemm1(const GemmArgs &a, const KArgs &k, hipStream_t s) {

@@ -141,6 +141,38 @@ def ws_rows(ws, offset, row_bytes, rows):
     return view.index_select(0, torch.from_numpy(rows).to(ws.device)).cpu().numpy()
 
 
+def a2_step_bytes(act):
+    """Code bytes of one A2 row per K step of 128 (E4M3: 128, packed E2M1: 64)."""
+    return 128 if act == 0 else 64
+
+
+def a2_to_ws(codes, scales, act):
+    """The workspace's K-step-major A2 bytes ([I/128][N][step bytes] codes,
+    [I/128][N][4] scales) from row-major sorted rows [N][...]."""
+    n, sb = codes.shape[0], a2_step_bytes(act)
+    S = codes.shape[1] // sb
+    c = np.ascontiguousarray(codes.reshape(n, S, sb).transpose(1, 0, 2))
+    s = np.ascontiguousarray(scales.reshape(n, S, 4).transpose(1, 0, 2))
+    return c, s
+
+
+def ws_a2_rows(ws, offs, N, I, act, rows):
+    """Host copies of sorted rows `rows` of A2 (codes [n][I or I/2], scales
+    [n][I/32]), gathered on the device from the workspace's K-step-major
+    layout over N = T * top_k rows."""
+    import torch
+    from quantized_moe_expert_softmax_amd import MOE_WS_A2_CODES, MOE_WS_A2_SCALES
+    rows = np.asarray(rows, np.int64)
+    S, sb = I // 128, a2_step_bytes(act)
+    idx = torch.from_numpy(rows).to(ws.device)
+    oc, os_ = offs[MOE_WS_A2_CODES], offs[MOE_WS_A2_SCALES]
+    c = ws[oc:oc + S * N * sb].view(S, N, sb).index_select(1, idx)
+    s = ws[os_:os_ + S * N * 4].view(S, N, 4).index_select(1, idx)
+    c = c.permute(1, 0, 2).reshape(rows.size, S * sb).cpu().numpy()
+    s = s.permute(1, 0, 2).reshape(rows.size, S * 4).cpu().numpy()
+    return c, s
+
+
 def unpack_fp4(packed):
     packed = np.asarray(packed)
     out = np.zeros(packed.shape[:-1] + (packed.shape[-1] * 2,), np.int64)

@@ -16,7 +16,7 @@ import numpy as np
 import oracle
 import quantized_moe_expert_softmax_amd as moe
 from tests.gpu_util import (A2_MISMATCH_TOL, ROUTE_ULP_TOL, a2_compare, a2_mismatch_ok, sum_bound, assert_output_close,
-                            assert_rows_match, bf16_host_bits, ulp_diff, ws_rows, ws_view)
+                            assert_rows_match, bf16_host_bits, ulp_diff, ws_a2_rows, ws_rows, ws_view)
 
 
 def _threads():
@@ -92,11 +92,8 @@ def check_front(layer, ws, x, lg, k, act):
     return rid, gw.reshape(T, k), perm, slot, xc, xs
 
 
-def _a2_rows(ws, offs, I, act, p):
-    a2row = I if act == 0 else I // 2
-    c = ws_rows(ws, offs[moe.MOE_WS_A2_CODES], a2row, p)
-    s = ws_rows(ws, offs[moe.MOE_WS_A2_SCALES], I // 32, p)
-    return c, s
+def _a2_rows(ws, offs, N, I, act, p):
+    return ws_a2_rows(ws, offs, N, I, act, p)
 
 
 def _staged_rows(ws, offs, T, k, H, combine, p):
@@ -152,7 +149,7 @@ def _check_rows(layer, ws, offs, T, k, act, a, front, ex, combine, what):
         lambda c, s, q: oracle.gemm1_rows(c & amask, s, q, w13 & 0x77, w13s, act, want_gu=True),
         a.size, xc[tok], xs[tok], sl)
     delta = swiglu_delta(gu, gu_abs, H, I, act)
-    g_c, g_s = _a2_rows(ws, offs, I, act, p)
+    g_c, g_s = _a2_rows(ws, offs, T * k, I, act, p)
     mism, row_diff = a2_compare(g_c, g_s, r_c, r_s, act, what, delta)
     assert a2_mismatch_ok(mism, a.size * I), "%s: A2 mismatch fraction %.3g > %.0e" % (
         what, mism, A2_MISMATCH_TOL)

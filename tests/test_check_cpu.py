@@ -10,8 +10,9 @@ import oracle
 import quantized_moe_expert_softmax_amd as moe
 from quantized_moe_expert_softmax_amd import synth
 from tests import layer_check as lc
+from tests.gpu_util import a2_step_bytes, a2_to_ws
 
-T, H, I, E, K = 12, 256, 128, 8, 3
+T, H, I, E, K = 12, 256, 256, 8, 3
 REGIONS = moe.MOE_WS_NUM
 
 
@@ -62,8 +63,10 @@ def _fake_device(act, seed=3):
     put(moe.MOE_WS_SLOT, slot)
     put(moe.MOE_WS_A1_CODES, xc)
     put(moe.MOE_WS_A1_SCALES, xs)
-    put(moe.MOE_WS_A2_CODES, a2c[perm])   # row p holds assignment perm[p]
-    put(moe.MOE_WS_A2_SCALES, a2s[perm])
+    # sorted row p holds assignment perm[p]; stored K-step-major
+    c2, s2 = a2_to_ws(a2c[perm], a2s[perm], act)
+    put(moe.MOE_WS_A2_CODES, c2)
+    put(moe.MOE_WS_A2_SCALES, s2)
     put(moe.MOE_WS_ROWS, rows[perm])
     return torch.from_numpy(ws), y, x, lg, w, offs
 
@@ -89,10 +92,22 @@ def test_accepts_the_oracle_itself(patched, act):
 
 
 def _a2_region(ws, offs, act):
-    a2row = I if act == 0 else I // 2
-    c = ws[offs[moe.MOE_WS_A2_CODES]:offs[moe.MOE_WS_A2_CODES] + T * K * a2row].view(T * K, a2row)
-    s = ws[offs[moe.MOE_WS_A2_SCALES]:offs[moe.MOE_WS_A2_SCALES] + T * K * (I // 32)]
-    return c, s.view(T * K, I // 32)
+    """The workspace's A2 codes and scales as [I/128][N][step bytes] and
+    [I/128][N][4] views (K-step-major)."""
+    N, S, sb = T * K, I // 128, a2_step_bytes(act)
+    c = ws[offs[moe.MOE_WS_A2_CODES]:offs[moe.MOE_WS_A2_CODES] + S * N * sb].view(S, N, sb)
+    s = ws[offs[moe.MOE_WS_A2_SCALES]:offs[moe.MOE_WS_A2_SCALES] + S * N * 4].view(S, N, 4)
+    return c, s
+
+
+def _row(v, p):
+    """Sorted row p of a K-step-major [S][N][b] view, as one row-major row."""
+    return v[:, p, :].reshape(-1).numpy().copy()
+
+
+def _set_row(v, p, row):
+    import torch
+    v[:, p, :] = torch.from_numpy(np.ascontiguousarray(row).reshape(v.shape[0], v.shape[2]))
 
 
 def test_rejects_a_staging_element(patched):
@@ -109,9 +124,10 @@ def test_rejects_an_a2_code_two_steps_off(patched):
     ws, y, x, lg, w, offs = _fake_device(0)
     patched["offs"] = offs
     c, _ = _a2_region(ws, offs, 0)
-    row = c[4].numpy()
+    row = _row(c, 4)
     i = int(np.argmax((row & 0x7F) > 0x10))
-    c[4, i] = int(row[i]) + 2 if (row[i] & 0x7F) < 0x7C else int(row[i]) - 2
+    row[i] = int(row[i]) + 2 if (row[i] & 0x7F) < 0x7C else int(row[i]) - 2
+    _set_row(c, 4, row)
     with pytest.raises(AssertionError, match="grid step"):
         _check(patched, ws, y, x, lg, w, 0)
 
@@ -150,18 +166,18 @@ def test_accepts_a_valid_neighbouring_a2_block(patched):
     ws, y, x, lg, w, offs = _fake_device(act)
     patched["offs"] = offs
     c, s = _a2_region(ws, offs, act)
-    cn, sn = c.numpy(), s.numpy()
+    cn = np.stack([_row(c, q) for q in range(T * K)])
     # a block whose largest magnitude code is 0x78 (256 units)
     blkmax = (cn.reshape(T * K, I // 32, 32) & 0x7F).max(axis=2)
     p, b = map(int, np.argwhere(blkmax == 0x78)[0])
     codes = cn[p].copy()
-    sc = sn[p].copy()
+    sc = _row(s, p)
     vals = oracle.mx_dequantize(codes[None], sc[None], I, act)[0].astype(np.float64)
     X = int(sc[b]) - 127
     codes[32 * b:32 * b + 32] = mxref.nearest_codes(vals[32 * b:32 * b + 32] * 2.0 ** -(X - 1), 0)
     sc[b] -= 1
-    c[p] = torch.from_numpy(codes)
-    s[p] = torch.from_numpy(sc)
+    _set_row(c, p, codes)
+    _set_row(s, p, sc)
     perm = ws[offs[moe.MOE_WS_PERM]:offs[moe.MOE_WS_PERM] + 4 * T * K].view(torch.int32).numpy()
     ids = ws[offs[moe.MOE_WS_IDS]:offs[moe.MOE_WS_IDS] + 4 * T * K].view(torch.int32).numpy()
     wts = ws[offs[moe.MOE_WS_WEIGHTS]:offs[moe.MOE_WS_WEIGHTS] + 4 * T * K].view(torch.float32).numpy()
@@ -177,6 +193,6 @@ def test_accepts_a_valid_neighbouring_a2_block(patched):
     assert st["rows_a2_differs"] == 1 and 0 < st["a2_mism"] <= 32 / (T * K * I) + 1e-12
     # two scales apart is not a neighbour
     sc[b] -= 1
-    s[p] = torch.from_numpy(sc)
+    _set_row(s, p, sc)
     with pytest.raises(AssertionError, match="more than one apart"):
         _check(patched, ws, y2, x, lg, w, act)
