@@ -564,18 +564,21 @@ GemmPlan choose_plan(int T, int top_k, int E, int act) {
   }
 }
 
-// Waves per stream workgroup (each takes 1/NW of the K steps).  Measured on
-// the 7168 x 3072 layer: GEMM1 runs faster with eight once there are more
-// items than four per CU (below that, eight-wave workgroups at two per CU
-// leave part of the items for a second round); GEMM2 (K = I, a third of
-// GEMM1's steps) is faster with four at every decode size.  With at most one
-// GEMM1 item per CU (the 5120 x {640, 1152} shards at T = 1, 2: 60-252 items)
-// sixteen waves put four times the weight loads in flight: 10% less per call
-// (v41flash I = 640, E = 128, T = 1: 28.5 -> 25.5 us; GEMM1 18.3 -> 15.1).
+// Waves per stream workgroup (each takes 1/NW of the K steps).  GEMM1: with
+// at most one item per CU (the 5120 x {640, 1152} shards at T = 1, 2: 60-252
+// items) sixteen waves put four times the weight loads in flight: 10% less
+// per call (v41flash I = 640, E = 128, T = 1: 28.5 -> 25.5 us); above three
+// items per CU eight waves (with a step's loads issued together, eight
+// against four measured 2.7% less per call on the 5120 x 640 shard at T = 8
+// and equal on the 7168 x 3072 layer at T = 8 .. 64; at 2.25 items per CU,
+// the 7168 x 3072 layer at T = 1, four were 0.3 us faster).  GEMM2 (K = I, a
+// third of GEMM1's steps or fewer) is faster with four at every decode size
+// (eight: +1% at T = 8 on 7168 x 3072, +47% at T = 64 on the 640-wide shard,
+// where its waves got at most one K step each).
 static int stream_waves(long items_upper, int num_cus, bool second) {
   if (second) return 4;
   if (items_upper <= num_cus) return 16;
-  return items_upper > 4L * num_cus ? 8 : 4;
+  return items_upper > 3L * num_cus ? 8 : 4;
 }
 
 static unsigned persistent_grid(long items_upper, int num_cus) {
