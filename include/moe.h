@@ -297,7 +297,7 @@ moe_status moe_quant_act(const void *x, int T, int H, moe_act_dtype act, uint8_t
  * experts", Changes: tuned entries per token count; "add A4W4 and FP8 P2P
  * transport support to MegaMoE", Technical Details: BM profiles chosen by
  * token count).  A layer starts with an empty table; calls no entry matches
- * use the built-in choice (below 2 rows per expert: decode for T <= 2, else
+ * use the built-in choice (at most 4 rows per expert: decode for T <= 2, else
  * stream; otherwise tiled with BM from the expected expert load, at least 64
  * rows).  Every plan computes the same result
  * (parity is tested per plan); plans differ only in speed. */

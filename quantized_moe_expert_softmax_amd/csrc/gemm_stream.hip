@@ -512,8 +512,8 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(KArgs p) {
 }
 
 GemmPlan choose_plan(int T, int top_k, int E, int act) {
-  // The average rows per expert decides between weight streaming (fewer than
-  // 2 rows) and the pipelined tiled kernel, whose BM covers the mean plus 1.5
+  // The average rows per expert decides between weight streaming (at most 4
+  // rows) and the pipelined tiled kernel, whose BM covers the mean plus 1.5
   // standard deviations of a binomial expert load (under uniform routing
   // most experts are then one m-block and their weights are read once).  An
   // activation tile fills whole 1 KiB copies and splits over two MFMA waves
@@ -531,7 +531,18 @@ GemmPlan choose_plan(int T, int top_k, int E, int act) {
   // launches on every measured layer at T = 1 and 2 (7168 x 3072: 53.6 ->
   // 52.9 and 92.9 -> 90.5 us per call; the 5120 x {640, 1152} shards 3-12%)
   // and 3-5% slower from T = 3 (experts two tokens share are read twice)
-  if (avg < 2.0) return T <= 2 ? GemmPlan{false, 1, 1, false, true} : GemmPlan{false, 1, 1};
+  // Up to 4 rows per expert on average the stream GEMMs (a step's loads
+  // issued together) beat the tiled ones under uniform routing: per call,
+  // 7168 x 3072 T = 128 1805 against 2039 us (tiled 32) and T = 192 1998
+  // against 2206; 5120 x 640 E = 384 T = 128 321 / 377 and T = 256 370 / 410;
+  // E = 128 T = 128 129 / 160; 5120 x 1152 E = 384 T = 128 527 / 592.  They
+  // still win at 6 to 8 rows (7168 x 3072 T = 512: 2275 / 2463), but an
+  // expert with more rows than its share re-reads its weights for every 16
+  // rows, and under skewed routing (half the experts empty) the stream plan
+  // is already 15% slower at a mean of 2 rows (T = 128: 670 against 572), so
+  // the boundary stays where skewed calls of 512 tokens and more keep the
+  // tiled plan.
+  if (avg <= 4.0) return T <= 2 ? GemmPlan{false, 1, 1, false, true} : GemmPlan{false, 1, 1};
   const double want = avg + 1.5 * sqrt(avg);
   {
     int mt = (int)ceil(want / 16.0);

@@ -56,7 +56,7 @@ def test_table_lookup_order_and_fallback():
 
 # The built-in choice on the layer shapes it was measured on (7168 x 3072 with
 # E = 384, top_k = 6; the 5120 x {640, 1152} shards with E = 384 x 6 and
-# 128 x 3): weight streaming below 2 rows per expert (with the token-major
+# 128 x 3): weight streaming up to 4 rows per expert (with the token-major
 # GEMM2 at T <= 2), tiled at least 64 rows,
 # BM covering the mean plus 1.5 sigma up to 160 rows, and above that the tile
 # with the fewest expected padded rows.  It depends on T, top_k and E only.
@@ -65,8 +65,9 @@ BUILTIN = [
     (384, 6, 1, moe.MOE_PLAN_DECODE, 16),      # T <= 2: token-major GEMM2, combine folded in
     (384, 6, 2, moe.MOE_PLAN_DECODE, 16),
     (384, 6, 3, moe.MOE_PLAN_STREAM, 16),
-    (384, 6, 127, moe.MOE_PLAN_STREAM, 16),    # 1.98 rows per expert
-    (384, 6, 128, moe.MOE_PLAN_TILED, 64),     # 2 rows: tiled, at the 64-row minimum
+    (384, 6, 128, moe.MOE_PLAN_STREAM, 16),    # 2 rows per expert
+    (384, 6, 256, moe.MOE_PLAN_STREAM, 16),    # 4 rows: the last streamed
+    (384, 6, 257, moe.MOE_PLAN_TILED, 64),     # 4.02 rows: tiled, at the 64-row minimum
     (384, 6, 1024, moe.MOE_PLAN_TILED, 64),
     (384, 6, 2048, moe.MOE_PLAN_TILED, 64),    # mean 32 + 1.5 sigma -> 48 -> even MT
     (384, 6, 4096, moe.MOE_PLAN_TILED, 96),    # mean 64 -> 76 rows
@@ -74,6 +75,8 @@ BUILTIN = [
     (384, 6, 16384, moe.MOE_PLAN_TILED, 160),  # mean 256: fewest padded rows at 160
     (384, 6, 24576, moe.MOE_PLAN_TILED, 128),  # mean 384: at 128
     (384, 6, 32768, moe.MOE_PLAN_TILED, 192),  # mean 512: at 192
+    (128, 3, 170, moe.MOE_PLAN_STREAM, 16),    # 3.98 rows
+    (128, 3, 171, moe.MOE_PLAN_TILED, 64),     # 4.01 rows
     (128, 3, 16384, moe.MOE_PLAN_TILED, 128),  # mean 384
     (128, 3, 32768, moe.MOE_PLAN_TILED, 160),  # mean 768
 ]
