@@ -586,8 +586,7 @@ GemmPlan choose_plan(int T, int top_k, int E, int act) {
 // third of GEMM1's steps or fewer) is faster with four at every decode size
 // (eight: +1% at T = 8 on 7168 x 3072, +47% at T = 64 on the 640-wide shard,
 // where its waves got at most one K step each).
-static int stream_waves(long items_upper, int num_cus, bool second) {
-  if (second) return 4;
+static int stream_waves(long items_upper, int num_cus) {
   if (items_upper <= num_cus) return 16;
   return items_upper > 3L * num_cus ? 8 : 4;
 }
@@ -629,7 +628,7 @@ hipError_t launch_gemm1(const GemmArgs &a, hipStream_t s) {
   const long items = a.max_mtiles * (a.I / 32);
   const unsigned grid = persistent_grid(items, a.num_cus);
   const bool f8 = a.act == MOE_ACT_MXFP8_E4M3;
-  const int nw = stream_waves(items, a.num_cus, false);
+  const int nw = stream_waves(items, a.num_cus);
   if (nw == 16) {
     if (f8) gemm1_kernel<0, 16><<<grid, 1024, 0, s>>>(k);
     else gemm1_kernel<4, 16><<<grid, 1024, 0, s>>>(k);
@@ -666,14 +665,9 @@ hipError_t launch_gemm2(const GemmArgs &a, hipStream_t s) {
   }
   const long items = a.max_mtiles * (a.H / 64);
   const unsigned grid = persistent_grid(items, a.num_cus);
-  const bool f8 = a.act == MOE_ACT_MXFP8_E4M3;
-  if (stream_waves(items, a.num_cus, true) == 8) {
-    if (f8) gemm2_kernel<0, 8><<<grid, 512, 0, s>>>(k);
-    else gemm2_kernel<4, 8><<<grid, 512, 0, s>>>(k);
-  } else {
-    if (f8) gemm2_kernel<0, 4><<<grid, 256, 0, s>>>(k);
-    else gemm2_kernel<4, 4><<<grid, 256, 0, s>>>(k);
-  }
+  // four waves at every decode size (measurements at stream_waves)
+  if (a.act == MOE_ACT_MXFP8_E4M3) gemm2_kernel<0, 4><<<grid, 256, 0, s>>>(k);
+  else gemm2_kernel<4, 4><<<grid, 256, 0, s>>>(k);
   return hipGetLastError();
 }
 
