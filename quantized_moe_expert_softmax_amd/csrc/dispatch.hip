@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 #include "mx_device.h"
 
@@ -28,65 +30,109 @@ __device__ __forceinline__ void load_logits(const float *__restrict__ row, int E
   }
 }
 
+// Selection key of logit v of expert e: the larger logit, then the lower
+// index, is the larger key.  The float's bits are mapped to an unsigned
+// order (negative values flipped whole, positive ones above them), -0 is
+// taken as +0 (a strict logit compare treats them as equal), and the index
+// is stored inverted below them.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v + 0.0f);  // -0 + 0 = +0
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ float route_key_value(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// The wave's largest key, in every lane, with VALU cross-lane moves only:
+// DPP within each 16-lane row (quad_perm [1,0,3,2], [2,3,0,1],
+// row_half_mirror, row_mirror: every lane then holds its row's largest
+// key), then v_permlane16_swap (rows 0 with 1, 2 with 3) and
+// v_permlane32_swap (the two halves).  The __shfl_xor butterfly this
+// replaces was a chain of dependent ds_bpermute round trips through LDS,
+// about 0.6 us per pick: 3.7 of the 5 us a one-token route took.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
+  auto pack = [](uint32_t hi, uint32_t lo) __attribute__((always_inline)) {
+    return ((uint64_t)hi << 32) | lo;
+  };
+  auto dpp_step = [&](auto ctrl) __attribute__((always_inline)) {
+    constexpr int C = decltype(ctrl)::value;
+    const uint64_t o =
+        pack((uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(key >> 32), C, 0xF, 0xF, false),
+             (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)key, C, 0xF, 0xF, false));
+    key = o > key ? o : key;
+  };
+  dpp_step(std::integral_constant<int, 0xB1>{});
+  dpp_step(std::integral_constant<int, 0x4E>{});
+  dpp_step(std::integral_constant<int, 0x141>{});
+  dpp_step(std::integral_constant<int, 0x140>{});
+  {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)key, (uint32_t)key, false, false);
+    const auto hi =
+        __builtin_amdgcn_permlane16_swap((uint32_t)(key >> 32), (uint32_t)(key >> 32), false, false);
+    const uint64_t a = pack(hi[0], lo[0]), b = pack(hi[1], lo[1]);
+    key = a > b ? a : b;
+  }
+  {
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)key, (uint32_t)key, false, false);
+    const auto hi =
+        __builtin_amdgcn_permlane32_swap((uint32_t)(key >> 32), (uint32_t)(key >> 32), false, false);
+    const uint64_t a = pack(hi[0], lo[0]), b = pack(hi[1], lo[1]);
+    key = a > b ? a : b;
+  }
+  return key;
+}
+
 // One wave routes the token whose logits it holds (load_logits); lanes <
-// top_k write ids[j], w[j].
+// top_k write ids[j], w[j].  The whole wave must be active.
 template <int NV>
 __device__ __forceinline__ void route_values(const float v[NV], int E, int top_k, int lane,
                                              int32_t *__restrict__ ids, float *__restrict__ wts) {
   uint32_t taken = 0;
-  float selv[8];
-  int seli[8];
+  float sel0 = 0.0f, mine = 0.0f;  // the largest logit; lane j: pick j's logit
+  int myid = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j < top_k) {
-      float bv = 0.0f;
-      int bi = 0x7fffffff;
+      uint64_t best = 0;  // below every valid key
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         const int e = lane + 64 * i;
-        // indices grow with i, so a strict compare keeps the lower index on ties
-        if (e < E && !((taken >> i) & 1u) && (bi == 0x7fffffff || v[i] > bv)) {
-          bv = v[i];
-          bi = e;
+        if (e < E && !((taken >> i) & 1u)) {
+          const uint64_t k = route_key(v[i], e);
+          best = k > best ? k : best;
         }
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        const bool better = oi != 0x7fffffff &&
-                            (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
-        if (better) {
-          bv = ov;
-          bi = oi;
-        }
-      }
+      best = wave_max_key(best);
+      const int bi = (int)~(uint32_t)best;
       if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      selv[j] = bv;
-      seli[j] = bi;
+      if (j == 0) sel0 = route_key_value(best);
+      if (j == lane) {
+        mine = route_key_value(best);
+        myid = bi;
+      }
     }
   }
   // weights: exp(l_j - l_0) / sum_j' exp(l_j' - l_0); l_0 is the largest logit.
   // Evaluated in double (the difference of two floats is exact there), then
-  // rounded once to float: at most top_k exponentials per token.
-  double ex[8];
+  // rounded once to float: lane j evaluates pick j's exponential, and every
+  // lane adds them in slot order.
+  const double ex = lane < top_k ? exp((double)mine - (double)sel0) : 0.0;
   double sum = 0.0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    ex[j] = j < top_k ? exp((double)selv[j] - (double)selv[0]) : 0.0;
-    sum += ex[j];
+    if (j < top_k) {
+      const uint64_t b = __double_as_longlong(ex);
+      const uint64_t r = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), j)
+                          << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, j);
+      sum += __longlong_as_double((long long)r);
+    }
   }
   if (lane < top_k) {
-    int id = 0;
-    double e = 0.0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j == lane) {
-        id = seli[j];
-        e = ex[j];
-      }
-    ids[lane] = id;
-    wts[lane] = (float)(e / sum);
+    ids[lane] = myid;
+    wts[lane] = (float)(ex / sum);
   }
 }
 
