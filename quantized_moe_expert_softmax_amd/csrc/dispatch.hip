@@ -510,13 +510,13 @@ __global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
 // compares); workgroups 1.. quantise the token rows.  The same outputs as the
 // separate kernels (and front_kernel), with far fewer block-wide steps than
 // front_kernel's 1024-wide scans, which the decode sizes do not need.
-template <int NV>
-__global__ __launch_bounds__(256) void front_small_kernel(FrontArgs p) {
+template <int NV, int BS>
+__global__ __launch_bounds__(BS) void front_small_kernel(FrontArgs p) {
   const int tid = threadIdx.x;
   if (blockIdx.x > 0) {
     const long nblocks = (long)p.T * (p.H / 32);
-    const long stride = (long)(gridDim.x - 1) * 256;
-    for (long b = (long)(blockIdx.x - 1) * 256 + tid; b < nblocks; b += stride) {
+    const long stride = (long)(gridDim.x - 1) * BS;
+    for (long b = (long)(blockIdx.x - 1) * BS + tid; b < nblocks; b += stride) {
       if (p.act == MOE_ACT_MXFP8_E4M3)
         quant_block<E4M3>(p.x, b, p.codes, p.scales);
       else
@@ -527,25 +527,26 @@ __global__ __launch_bounds__(256) void front_small_kernel(FrontArgs p) {
   __shared__ int32_t sid[kFrontMaxT * 8];
   __shared__ float sw[kFrontMaxT * 8];
   __shared__ int32_t base[1024];  // per expert: count, then first sorted row
-  __shared__ int32_t wsum[4][2];
+  __shared__ int32_t wsum[BS / 64][2];
   const int wave = tid >> 6, lane = tid & 63;
   const int T = p.T, E = p.E, k = p.top_k, N = T * k;
-  for (int i = tid; i < p.nsync; i += 256) p.sync[i] = 0;
-  for (int e = tid; e < E; e += 256) base[e] = 0;
-  // wave w routes tokens w, w + 4, ...
-  for (int t = wave; t < T; t += 4) {
+  for (int i = tid; i < p.nsync; i += BS) p.sync[i] = 0;
+  for (int e = tid; e < E; e += BS) base[e] = 0;
+  // wave w routes tokens w, w + BS / 64, ...
+  for (int t = wave; t < T; t += BS / 64) {
     float v[NV];
     load_logits<NV>(p.logits + (long)t * E, E, lane, v);
     route_values<NV>(v, E, k, lane, sid + t * k, sw + t * k);
   }
   __syncthreads();
-  for (int a = tid; a < N; a += 256) {
+  for (int a = tid; a < N; a += BS) {
     p.ids[a] = sid[a];
     p.wts[a] = sw[a];
     atomicAdd(&base[sid[a]], 1);
   }
   __syncthreads();
-  // exclusive prefix sums of the counts and of the m-blocks per expert
+  // exclusive prefix sums of the counts and of the m-blocks per expert (the
+  // first 256 threads own four experts each, E <= 1024; the others scan zeros)
   int c[4], m[4], lc = 0, lm = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -594,7 +595,7 @@ __global__ __launch_bounds__(256) void front_small_kernel(FrontArgs p) {
   __syncthreads();
   // assignment a's row: its expert's first row plus the number of lower
   // assignments of the same expert (ascending a within an expert)
-  for (int a = tid; a < N; a += 256) {
+  for (int a = tid; a < N; a += BS) {
     const int e = sid[a];
     int r = 0;
     for (int b = 0; b < a; ++b) r += sid[b] == e;
@@ -609,11 +610,15 @@ hipError_t launch_front(const FrontArgs &a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (a.T > kSortBlock || a.E > 1024 || a.top_k > 8) return hipErrorInvalidValue;
   if (a.logits && a.T <= kFrontMaxT) {
-    const long nq = a.x ? ((long)a.T * (a.H / 32) + 255) / 256 : 0;
-    const dim3 grid((unsigned)(1 + nq)), block(256);
-#define FRONT_SMALL_CASE(NV_)                                 \
-  case NV_:                                                   \
-    front_small_kernel<NV_><<<grid, block, 0, s>>>(a);        \
+    // one wave routes each token: 16 waves above 4 tokens (T = 16 with four:
+    // each wave routed four tokens in turn, 12.8 us of routing)
+    const int bs = a.T > 4 ? 1024 : 256;
+    const long nq = a.x ? ((long)a.T * (a.H / 32) + bs - 1) / bs : 0;
+    const dim3 grid((unsigned)(1 + nq)), block(bs);
+#define FRONT_SMALL_CASE(NV_)                                                   \
+  case NV_:                                                                     \
+    if (bs == 1024) front_small_kernel<NV_, 1024><<<grid, block, 0, s>>>(a);    \
+    else front_small_kernel<NV_, 256><<<grid, block, 0, s>>>(a);                \
     break;
     switch (ceil_div(a.E, 64)) {
       FRONT_SMALL_CASE(1) FRONT_SMALL_CASE(2) FRONT_SMALL_CASE(3) FRONT_SMALL_CASE(4)
