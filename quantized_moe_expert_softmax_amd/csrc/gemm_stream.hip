@@ -216,10 +216,14 @@ __global__ __launch_bounds__(64 * NW) void gemm2_kernel(KArgs p) {
 // ranges over the NW waves; a wave loads the weight fragments and A2 operands
 // of four pairs at a time (they may span two slots) and accumulates per slot
 // (all 16 rows of the MFMA tile carry the token's A2 row; row 0 is kept).  The
-// per-(wave, slot) partial sums meet in LDS; wave 0 adds them per slot, scales
-// each slot's row by its routing weight, stores it to the assignment's
-// staging row (the layout the combine kernel reads) and writes
-// y[t] = bf16 of the FP32 sum of the weighted rows in slot order: the
+// token's per-slot expert, sorted row and routing weight are loaded once per
+// item into lanes 0 .. top_k - 1 and read with readlane, so the operand loads
+// of a group never wait on another load (loaded per pair, they cost 21.2 ->
+// 18.4 us per GEMM2 at T = 1 and 33.4 -> 30.4 at T = 2 on the 7168 x 3072
+// layer).  The per-(wave, slot) partial sums meet in LDS; wave j < top_k adds
+// slot j's, scales them by its routing weight and stores the row to the
+// assignment's staging row (the layout the combine kernel reads); wave 0 then
+// writes y[t] = bf16 of the FP32 sum of the weighted rows in slot order: the
 // combine kernel's result, without its launch or its reads of the staging.
 // With eight waves per item it measured on the 7168 x 3072, 384 x 6 layer
 // (us per call, eager, one box) T = 1: 58.5 against 55.0 for the stream plan
@@ -241,6 +245,8 @@ struct TmGroup {
 template <int FMT, int NW, int TPI>
 __global__ __launch_bounds__(64 * NW) void gemm2_tm_kernel(KArgs p) {
   __shared__ float part[NW][8][TPI][16];  // [wave][slot][tile][column]: row 0 of each tile
+  __shared__ float wrow[8][TPI][16];      // [slot][tile][column]: weighted rows
+  static_assert(NW >= 8, "one wave per slot in the epilogue (top_k <= 8)");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4;
   const int NB = p.H / (16 * TPI), k = p.top_k, S = p.I / 128, P = k * S;
   const int i0 = wave * P / NW, i1 = (wave + 1) * P / NW;
@@ -251,6 +257,14 @@ __global__ __launch_bounds__(64 * NW) void gemm2_tm_kernel(KArgs p) {
     const int t = (int)(w / NB), nb = (int)(w % NB);
     // the first tile of the item: tile u of quad qd is tile 4 qd + u
     const size_t tile0 = (size_t)nb * TPI;
+    // lane j < top_k holds slot j's expert, sorted row and routing weight:
+    // one load each per item, so no load below waits on another
+    int slot_e = 0, slot_r = 0, slot_w = 0;
+    if (lane < k) {
+      slot_e = p.ids[t * k + lane];
+      slot_r = p.inv[t * k + lane];
+      slot_w = __builtin_bit_cast(int, p.wts_a[t * k + lane]);
+    }
     // slots this wave's range does not reach keep zero partial sums
     for (int x = lane; x < 8 * TPI * 16; x += 64) (&part[wave][0][0][0])[x] = 0.0f;
     v4f acc[TPI];
@@ -268,9 +282,8 @@ __global__ __launch_bounds__(64 * NW) void gemm2_tm_kernel(KArgs p) {
         const int i = i4 + u;
         if (i < i1) {
           const int j = i / S, st = i - j * S;
-          const int asg = t * k + j;
-          const size_t e = (size_t)uniform(p.ids[asg]);
-          const size_t pr = (size_t)uniform(p.inv[asg]);
+          const size_t e = (size_t)__builtin_amdgcn_readlane(slot_e, j);
+          const size_t pr = (size_t)__builtin_amdgcn_readlane(slot_r, j);
           G.a[u] = load_a<FMT>(p.a2c + a2c_at<FMT>(pr, st, N), g);
           G.sa[u] = p.a2s[a2s_at(pr, st, N) + g];
           const size_t qb = e * (ntiles / 4) + tile0 / 4;  // the item's tiles share a quad
@@ -310,32 +323,31 @@ __global__ __launch_bounds__(64 * NW) void gemm2_tm_kernel(KArgs p) {
 #pragma unroll
       for (int q = 0; q < TPI; ++q) part[wave][cj][q][lane] = acc[q][0];
     __syncthreads();
-    if (wave == 0 && lane < 16) {
+    {
       // each weighted row is rounded on its own before it joins the sum (no
       // fused multiply-add), so y is exactly the slot-order sum of the rows
-      // stored for the combine
+      // stored for the combine.  Wave j < top_k adds the waves' partial sums
+      // of slot j (lane 16 q + c: tile q, column c) and stores the weighted
+      // row; then wave 0 adds each column over the slots in slot order.
 #pragma clang fp contract(off)
-      float sum[TPI];
+      if (wave < k && lane < 16 * TPI) {
+        const int q = lane / 16, c = lane % 16;
+        const float wj =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(slot_w, wave));
+        const int rj = __builtin_amdgcn_readlane(slot_r, wave);
+        float o = 0.f;
 #pragma unroll
-      for (int q = 0; q < TPI; ++q) sum[q] = 0.f;
-      const size_t col = (size_t)16 * tile0 + lane;
-      for (int j = 0; j < k; ++j) {
-        const int asg = t * k + j;
-        const float wj = p.wts_a[asg];
-        float *row = p.rows + (size_t)p.inv[asg] * p.H + col;
-#pragma unroll
-        for (int q = 0; q < TPI; ++q) {
-          float o = 0.f;
-#pragma unroll
-          for (int v = 0; v < NW; ++v) o += part[v][j][q][lane];
-          const float tj = wj * o;
-          row[16 * q] = tj;
-          sum[q] += tj;
-        }
+        for (int v = 0; v < NW; ++v) o += part[v][wave][q][c];
+        const float tj = wj * o;
+        p.rows[(size_t)rj * p.H + 16 * tile0 + lane] = tj;
+        wrow[wave][q][c] = tj;
       }
-      uint16_t *yr = p.y + (size_t)t * p.H + col;
-#pragma unroll
-      for (int q = 0; q < TPI; ++q) yr[16 * q] = f32_to_bf16(sum[q]);
+      __syncthreads();
+      if (wave == 0 && lane < 16 * TPI) {
+        float sum = 0.f;
+        for (int j = 0; j < k; ++j) sum += wrow[j][lane / 16][lane % 16];
+        p.y[(size_t)t * p.H + 16 * tile0 + lane] = f32_to_bf16(sum);
+      }
     }
     __syncthreads();  // part is free again
   }
