@@ -200,11 +200,27 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restric
   for (int e = threadIdx.x; e < E; e += 256) hist[(long)blockIdx.x * E + e] = lhist[e];
 }
 
+// The m-blocks of an expert with c rows from sorted row r0: m-block i (table
+// entry mb0 + i) holds rows [r0 + bm i, + min(bm, c - bm i)).  Writes the
+// expert of each and, when mbrows is not null, its first row and row count
+// (one load gives a GEMM item both; from offsets they are a second
+// dependent load).
+__device__ __forceinline__ void write_mblocks(int32_t *__restrict__ mbexp,
+                                              int32_t *__restrict__ mbrows, int e, int mb0,
+                                              int m, int r0, int c, int bm) {
+  for (int i = 0; i < m; ++i) {
+    mbexp[mb0 + i] = e;
+    if (mbrows)
+      reinterpret_cast<int2 *>(mbrows)[mb0 + i] = make_int2(r0 + bm * i, min(bm, c - bm * i));
+  }
+}
+
 __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ hist, int nb, int E,
                                                          int32_t *__restrict__ counts,
                                                          int32_t *__restrict__ offsets,
                                                          int32_t *__restrict__ mtoff,
-                                                         int32_t *__restrict__ mbexp, int bm,
+                                                         int32_t *__restrict__ mbexp,
+                                                         int32_t *__restrict__ mbrows, int bm,
                                                          int32_t *__restrict__ sync, int nsync) {
   __shared__ int32_t sc[1024];
   __shared__ int32_t sm[1024];
@@ -254,8 +270,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ h
       offsets[E] = sc[e];
       mtoff[E] = sm[e];
     }
-    const int mb0 = sm[e] - m;
-    for (int i = 0; i < m; ++i) mbexp[mb0 + i] = e;
+    write_mblocks(mbexp, mbrows, e, sm[e] - m, m, base, c, bm);
   }
 }
 
@@ -301,10 +316,10 @@ hipError_t launch_sort_hist(const int32_t *ids, int T, int E, int top_k, int32_t
 }
 
 hipError_t launch_sort_scan(int32_t *hist, int nb, int E, int32_t *counts, int32_t *offsets,
-                            int32_t *mtoff, int32_t *mbexp, int bm, int32_t *sync, int nsync,
-                            hipStream_t s) {
-  sort_scan_kernel<<<1, 1024, 0, s>>>(hist, nb, E, counts, offsets, mtoff, mbexp, bm, sync,
-                                      nsync);
+                            int32_t *mtoff, int32_t *mbexp, int32_t *mbrows, int bm,
+                            int32_t *sync, int nsync, hipStream_t s) {
+  sort_scan_kernel<<<1, 1024, 0, s>>>(hist, nb, E, counts, offsets, mtoff, mbexp, mbrows, bm,
+                                      sync, nsync);
   return hipGetLastError();
 }
 
@@ -482,7 +497,7 @@ __global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
       p.offsets[E] = sc[tid];
       p.mtoff[E] = sm[tid];
     }
-    for (int i = 0; i < m; ++i) p.mbexp[sm[tid] - m + i] = tid;
+    write_mblocks(p.mbexp, p.mbrows, tid, sm[tid] - m, m, sc[tid] - c, c, p.bm);
   }
   const unsigned long long bit = 1ull << lane;
   if (tid < T)
@@ -582,7 +597,7 @@ __global__ __launch_bounds__(BS) void front_small_kernel(FrontArgs p) {
       p.counts[e] = c[i];
       p.offsets[e] = oc;
       p.mtoff[e] = om;
-      for (int j = 0; j < m[i]; ++j) p.mbexp[om + j] = e;
+      write_mblocks(p.mbexp, p.mbrows, e, om, m[i], oc, c[i], p.bm);
       base[e] = oc;
     }
     oc += c[i];

@@ -48,6 +48,7 @@ struct KArgs {
   const uint8_t *a1c, *a1s;
   uint8_t *a2c, *a2s;
   const int32_t *perm, *offsets, *mtoff, *mbexp;
+  const int2 *mbrows;  // m-block mt's first sorted row and row count
   const float *wts;  // [N] routing weight of sorted row p
   const uint8_t *wp;
   const uint32_t *wsp;
@@ -220,6 +221,7 @@ inline KArgs make_args(const GemmArgs &a, bool second) {
   k.T = a.T; k.top_k = a.top_k; k.E = a.E; k.H = a.H; k.I = a.I;
   k.a1c = a.a1c; k.a1s = a.a1s; k.a2c = a.a2c; k.a2s = a.a2s;
   k.perm = a.perm; k.offsets = a.offsets; k.mtoff = a.mtoff; k.mbexp = a.mbexp; k.wts = a.wts;
+  k.mbrows = reinterpret_cast<const int2 *>(a.mbrows);
   k.wp = second ? a.w2p : a.w13p;
   k.wsp = reinterpret_cast<const uint32_t *>(second ? a.w2sp : a.w13sp);
   k.rows = a.rows;

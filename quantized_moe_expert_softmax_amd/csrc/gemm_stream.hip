@@ -109,8 +109,8 @@ __global__ __launch_bounds__(64 * NW) void gemm1_kernel(KArgs p) {
   for (long w = blockIdx.x; w < total; w += gridDim.x) {
     const int mt = (int)(w / NU), j = (int)(w % NU);
     const int e = uniform(p.mbexp[mt]);
-    const int row0 = uniform(p.offsets[e]) + kMTile * (mt - uniform(p.mtoff[e]));
-    const int nrows = min(kMTile, uniform(p.offsets[e + 1]) - row0);
+    const int2 mr = p.mbrows[mt];  // loaded beside e, not after it
+    const int row0 = uniform(mr.x), nrows = uniform(mr.y);
     const int pr = row0 + min(lane & 15, nrows - 1);
     const int tok = p.perm[pr] / p.top_k;
     const uint8_t *arow = p.a1c + (size_t)tok * a1row;
@@ -165,8 +165,8 @@ __global__ __launch_bounds__(64 * NW) void gemm2_kernel(KArgs p) {
   for (long w = blockIdx.x; w < total; w += gridDim.x) {  // m-tile major, as in GEMM1
     const int mt = (int)(w / NB), nb = (int)(w % NB);
     const int e = uniform(p.mbexp[mt]);
-    const int row0 = uniform(p.offsets[e]) + kMTile * (mt - uniform(p.mtoff[e]));
-    const int nrows = min(kMTile, uniform(p.offsets[e + 1]) - row0);
+    const int2 mr = p.mbrows[mt];  // loaded beside e, not after it
+    const int row0 = uniform(mr.x), nrows = uniform(mr.y);
     const size_t pr = (size_t)(row0 + min(lane & 15, nrows - 1));
     const uint8_t *arow = p.a2c + a2c_at<FMT>(pr, 0, N);
     const uint8_t *asrow = p.a2s + a2s_at(pr, 0, N);
@@ -396,8 +396,8 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(KArgs p) {
       const int j = (int)(w / n_mt), mt = (int)(w % n_mt);
       const int s0 = wave * S1 / NW, s1 = (wave + 1) * S1 / NW;
       const int e = uniform(p.mbexp[mt]);
-      const int row0 = uniform(p.offsets[e]) + kMTile * (mt - uniform(p.mtoff[e]));
-      const int nrows = min(kMTile, uniform(p.offsets[e + 1]) - row0);
+      const int2 mr = p.mbrows[mt];  // loaded beside e, not after it
+      const int row0 = uniform(mr.x), nrows = uniform(mr.y);
       const int tok = p.perm[row0 + min(lane & 15, nrows - 1)] / p.top_k;
       const uint8_t *wt = p.wp + ((size_t)e * nq1 + j) * (size_t)S1 * 4096;
       const uint32_t *wsq = p.wsp + ((size_t)e * nq1 + j) * (size_t)S1 * 64;
@@ -439,8 +439,8 @@ __global__ __launch_bounds__(64 * NW) void fused_kernel(KArgs p) {
       const int nb = (int)(w2 / n_mt), mt = (int)(w2 % n_mt);
       const int s0 = wave * S2 / NW, s1 = (wave + 1) * S2 / NW;
       const int e = uniform(p.mbexp[mt]);
-      const int row0 = uniform(p.offsets[e]) + kMTile * (mt - uniform(p.mtoff[e]));
-      const int nrows = min(kMTile, uniform(p.offsets[e + 1]) - row0);
+      const int2 mr = p.mbrows[mt];  // loaded beside e, not after it
+      const int row0 = uniform(mr.x), nrows = uniform(mr.y);
       const uint8_t *wt = p.w2p + ((size_t)e * nq2 + nb) * (size_t)S2 * 4096;
       const uint32_t *wsq = p.w2sp + ((size_t)e * nq2 + nb) * (size_t)S2 * 64;
       if (tid == 0) {

@@ -45,6 +45,7 @@ struct WsLayout {
   size_t hist;    // [nb][E] int32 per-sort-block histograms, then bases within the expert
   size_t mtoff;   // [E+1] int32 prefix sum of m-blocks per expert
   size_t mbexp;   // [N/16 + E] int32 expert of each m-block
+  size_t mbrows;  // [N/16 + E] int32 pairs: first sorted row and row count of each m-block
   size_t wsorted; // [N] fp32 routing weight of sorted row p (assignment perm[p])
   size_t sync;    // [kSyncHead + N/16 + E + 1] int32: item counters, fused-launch sync (zeroed per call)
   size_t total;
@@ -65,6 +66,7 @@ inline WsLayout ws_layout(int T, int top_k, int E, int H, int I, int act) {
   L.off[MOE_WS_OFFSETS] = take((size_t)(E + 1) * 4);
   L.mtoff = take((size_t)(E + 1) * 4);
   L.mbexp = take((N / kMTile + E + 1) * 4);
+  L.mbrows = take((N / kMTile + E + 1) * 8);
   L.hist = take((size_t)L.nb * E * 4);
   L.wsorted = take(N * 4);
   L.sync = take((kSyncHead + N / kMTile + E + 1) * 4);
@@ -102,9 +104,10 @@ hipError_t launch_route(const float *logits, int T, int E, int top_k, int32_t *i
                         hipStream_t s);
 hipError_t launch_sort_hist(const int32_t *ids, int T, int E, int top_k, int32_t *hist, int nb,
                             hipStream_t s);
+// mbrows may be null (no m-block row table)
 hipError_t launch_sort_scan(int32_t *hist, int nb, int E, int32_t *counts, int32_t *offsets,
-                            int32_t *mtoff, int32_t *mbexp, int bm, int32_t *sync, int nsync,
-                            hipStream_t s);
+                            int32_t *mtoff, int32_t *mbexp, int32_t *mbrows, int bm,
+                            int32_t *sync, int nsync, hipStream_t s);
 hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, const int32_t *hist,
                                const int32_t *offsets, int32_t *perm, int32_t *inv,
                                const float *w, float *wsorted, hipStream_t s);
@@ -118,7 +121,7 @@ struct FrontArgs {
   int T, E, top_k, H, act, bm;
   int32_t *ids;
   float *wts;
-  int32_t *counts, *offsets, *mtoff, *mbexp, *perm, *inv;
+  int32_t *counts, *offsets, *mtoff, *mbexp, *mbrows, *perm, *inv;
   float *wsorted;
   uint8_t *codes, *scales;
 };
@@ -160,6 +163,7 @@ struct GemmArgs {
   const uint8_t *a1c, *a1s;
   uint8_t *a2c, *a2s;
   const int32_t *perm, *offsets, *mtoff, *mbexp;
+  const int32_t *mbrows;  // [m-block][2]: first sorted row, rows (stream and fused plans)
   const float *wts;  // [N] routing weight of sorted row p
   const uint8_t *w13p, *w13sp, *w2p, *w2sp;
   float *rows;  // [N][H] weighted GEMM2 rows (layout by combine)

@@ -335,6 +335,7 @@ static moe_status forward_impl(moe_layer_t L, bool prequant, const void *x, cons
   int32_t *offsets = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_OFFSETS]);
   int32_t *mtoff = reinterpret_cast<int32_t *>(base + W.mtoff);
   int32_t *mbexp = reinterpret_cast<int32_t *>(base + W.mbexp);
+  int32_t *mbrows = reinterpret_cast<int32_t *>(base + W.mbrows);
   int32_t *hist = reinterpret_cast<int32_t *>(base + W.hist);
   int32_t *perm = reinterpret_cast<int32_t *>(base + W.off[MOE_WS_PERM]);
   uint8_t *a1c = base + W.off[MOE_WS_A1_CODES];
@@ -357,6 +358,7 @@ static moe_status forward_impl(moe_layer_t L, bool prequant, const void *x, cons
   g.num_cus = L->num_cus;
   g.a1c = g1c; g.a1s = g1s; g.a2c = a2c; g.a2s = a2s;
   g.perm = perm; g.offsets = offsets; g.mtoff = mtoff; g.mbexp = mbexp; g.wts = wsorted;
+  g.mbrows = mbrows;
   g.w13p = L->w13p; g.w13sp = L->w13sp; g.w2p = L->w2p; g.w2sp = L->w2sp;
   g.rows = rows;
   g.combine = (int)flags;
@@ -383,7 +385,7 @@ static moe_status forward_impl(moe_layer_t L, bool prequant, const void *x, cons
     f.logits = routed_logits; f.x = static_cast<const uint16_t *>(x);
     f.T = T; f.E = L->E; f.top_k = top_k; f.H = L->H; f.act = act; f.bm = g.plan.bm();
     f.ids = ids; f.wts = wts; f.counts = counts; f.offsets = offsets; f.mtoff = mtoff;
-    f.mbexp = mbexp; f.perm = perm; f.inv = inv; f.wsorted = wsorted; f.codes = a1c;
+    f.mbexp = mbexp; f.mbrows = mbrows; f.perm = perm; f.inv = inv; f.wsorted = wsorted; f.codes = a1c;
     f.scales = a1s;
     f.sync = g.sync;
     f.nsync = nsync;
@@ -410,8 +412,8 @@ static moe_status forward_impl(moe_layer_t L, bool prequant, const void *x, cons
     if (e == hipSuccess) e = launch_sort_hist(ids, T, L->E, top_k, hist, W.nb, s);
     mark();
     if (e == hipSuccess)
-      e = launch_sort_scan(hist, W.nb, L->E, counts, offsets, mtoff, mbexp, g.plan.bm(), g.sync,
-                           nsync, s);
+      e = launch_sort_scan(hist, W.nb, L->E, counts, offsets, mtoff, mbexp, mbrows, g.plan.bm(),
+                           g.sync, nsync, s);
     mark();
     if (e == hipSuccess)
       e = launch_sort_scatter(ids, T, L->E, top_k, hist, offsets, perm, inv, wts, wsorted, s);
@@ -522,7 +524,8 @@ moe_status moe_sort(const int32_t *ids, int T, int E, int top_k, int32_t *counts
   hipError_t e = hipSuccess;
   if (nb > 0) e = launch_sort_hist(ids, T, E, top_k, hist, nb, s);
   if (e == hipSuccess)
-    e = launch_sort_scan(hist, nb, E, counts, offsets, mtoff, mbexp, kMTile, nullptr, 0, s);
+    e = launch_sort_scan(hist, nb, E, counts, offsets, mtoff, mbexp, nullptr, kMTile, nullptr, 0,
+                         s);
   if (e == hipSuccess && nb > 0)
     e = launch_sort_scatter(ids, T, E, top_k, hist, offsets, perm, inv, nullptr, nullptr, s);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "sort launch");
