@@ -525,6 +525,22 @@ __global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
 // compares); workgroups 1.. quantise the token rows.  The same outputs as the
 // separate kernels (and front_kernel), with far fewer block-wide steps than
 // front_kernel's 1024-wide scans, which the decode sizes do not need.
+// Inclusive prefix sum of x over the wave's 64 lanes with VALU moves only:
+// DPP row_shr 1, 2, 4, 8 within each 16-lane row (a lane with no source lane
+// in its row adds 0), then each row adds the totals of the rows before it
+// (lanes 15, 31, 47 read with readlane).  (The __shfl_up ladder it replaces
+// is six dependent ds_bpermute round trips per value.)
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 template <int NV, int BS>
 __global__ __launch_bounds__(BS) void front_small_kernel(FrontArgs p) {
   const int tid = threadIdx.x;
@@ -571,15 +587,7 @@ __global__ __launch_bounds__(BS) void front_small_kernel(FrontArgs p) {
     lc += c[i];
     lm += m[i];
   }
-  int ic = lc, im = lm;  // inclusive scan over the wave
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int oc = __shfl_up(ic, d), om = __shfl_up(im, d);
-    if (lane >= d) {
-      ic += oc;
-      im += om;
-    }
-  }
+  const int ic = wave_inclusive_scan(lc, lane), im = wave_inclusive_scan(lm, lane);
   if (lane == 63) {
     wsum[wave][0] = ic;
     wsum[wave][1] = im;
