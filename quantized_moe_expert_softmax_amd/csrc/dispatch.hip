@@ -200,6 +200,22 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restric
   for (int e = threadIdx.x; e < E; e += 256) hist[(long)blockIdx.x * E + e] = lhist[e];
 }
 
+// Inclusive prefix sum of x over the wave's 64 lanes with VALU moves only:
+// DPP row_shr 1, 2, 4, 8 within each 16-lane row (a lane with no source lane
+// in its row adds 0), then each row adds the totals of the rows before it
+// (lanes 15, 31, 47 read with readlane).  (The __shfl_up ladder it replaces
+// is six dependent ds_bpermute round trips per value.)
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 // The m-blocks of an expert with c rows from sorted row r0: m-block i (table
 // entry mb0 + i) holds rows [r0 + bm i, + min(bm, c - bm i)).  Writes the
 // expert of each and, when mbrows is not null, its first row and row count
@@ -224,6 +240,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ h
                                                          int32_t *__restrict__ sync, int nsync) {
   __shared__ int32_t sc[1024];
   __shared__ int32_t sm[1024];
+  __shared__ int32_t wtot[16][2];
   const int e = threadIdx.x;
   for (int i = e; i < nsync; i += 1024) sync[i] = 0;
   int run = 0;
@@ -251,17 +268,21 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ h
   }
   const int c = e < E ? run : 0;
   const int m = e < E ? (run + bm - 1) / bm : 0;
-  sc[e] = c;
-  sm[e] = m;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int ac = e >= d ? sc[e - d] : 0;
-    const int am = e >= d ? sm[e - d] : 0;
-    __syncthreads();
-    sc[e] += ac;
-    sm[e] += am;
-    __syncthreads();
+  // inclusive prefix sums over the experts: within each wave, then plus the
+  // totals of the lower waves
+  const int wave = e >> 6, lane = e & 63;
+  int ic = wave_inclusive_scan(c, lane), im = wave_inclusive_scan(m, lane);
+  if (lane == 63) {
+    wtot[wave][0] = ic;
+    wtot[wave][1] = im;
   }
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) {
+    ic += wtot[w][0];
+    im += wtot[w][1];
+  }
+  sc[e] = ic;
+  sm[e] = im;
   if (e < E) {
     const int base = sc[e] - c;
     offsets[e] = base;
@@ -438,6 +459,7 @@ __global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
   __shared__ int32_t sid[kSortBlock * 8];
   __shared__ float sw[kSortBlock * 8];
   __shared__ int32_t cnt[1024], sc[1024], sm[1024];
+  __shared__ int32_t wtot[16][2];
   __shared__ unsigned long long masks[4][1024];
   const int wave = tid >> 6, lane = tid & 63;
   const int T = p.T, E = p.E, k = p.top_k, N = T * k;
@@ -478,17 +500,20 @@ __global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
   __syncthreads();
   const int c = tid < E ? cnt[tid] : 0;
   const int m = (c + p.bm - 1) / p.bm;
-  sc[tid] = c;
-  sm[tid] = m;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int ac = tid >= d ? sc[tid - d] : 0;
-    const int am = tid >= d ? sm[tid - d] : 0;
-    __syncthreads();
-    sc[tid] += ac;
-    sm[tid] += am;
-    __syncthreads();
+  // inclusive prefix sums over the experts: within each wave, then plus the
+  // totals of the lower waves
+  int ic = wave_inclusive_scan(c, lane), im = wave_inclusive_scan(m, lane);
+  if (lane == 63) {
+    wtot[wave][0] = ic;
+    wtot[wave][1] = im;
   }
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) {
+    ic += wtot[w][0];
+    im += wtot[w][1];
+  }
+  sc[tid] = ic;
+  sm[tid] = im;
   if (tid < E) {
     p.counts[tid] = c;
     p.offsets[tid] = sc[tid] - c;
@@ -525,22 +550,6 @@ __global__ __launch_bounds__(1024) void front_kernel(FrontArgs p) {
 // compares); workgroups 1.. quantise the token rows.  The same outputs as the
 // separate kernels (and front_kernel), with far fewer block-wide steps than
 // front_kernel's 1024-wide scans, which the decode sizes do not need.
-// Inclusive prefix sum of x over the wave's 64 lanes with VALU moves only:
-// DPP row_shr 1, 2, 4, 8 within each 16-lane row (a lane with no source lane
-// in its row adds 0), then each row adds the totals of the rows before it
-// (lanes 15, 31, 47 read with readlane).  (The __shfl_up ladder it replaces
-// is six dependent ds_bpermute round trips per value.)
-__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
-  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
-            r2 = __builtin_amdgcn_readlane(x, 47);
-  const int row = lane >> 4;
-  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
-}
-
 template <int NV, int BS>
 __global__ __launch_bounds__(BS) void front_small_kernel(FrontArgs p) {
   const int tid = threadIdx.x;
