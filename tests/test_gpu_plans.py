@@ -206,3 +206,23 @@ def test_tiled_many_items_per_workgroup(act, rows, T, H, I, E, k):
     what = "tiled rows=%d T=%d H=%d I=%d act=%d" % (rows, T, H, I, act)
     _, _, st = forward_and_check(layer, x, lg, k, act, host_weights(w), what=what)
     print(what, st)
+
+
+# Plan DECODE (token-major GEMM2 with the combine folded in) at its limits:
+# eight waves per item when the items outnumber the CUs (T * H / 32 > CUs)
+# with top_k = 8 (one epilogue wave per slot, all eight busy), and sixteen
+# waves at one token with top_k = 8; both formats; ragged: experts shared by
+# the two tokens.
+DECODE_TM_CASES = [(2, 5120, 256, 16, 8), (1, 2048, 384, 8, 8), (2, 7168, 128, 12, 5)]
+
+
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("T,H,I,E,k", DECODE_TM_CASES)
+def test_decode_plan_limits(T, H, I, E, k, act):
+    w, x, lg = _small(T, H, I, E, k, seed=T * 13 + H + k)
+    layer = _layer(*w)
+    moe.moe_set_plans(layer, [dict(act=act, top_k=k, t_max=T, variant=moe.MOE_PLAN_DECODE,
+                                   rows=16)])
+    forward_and_check(layer, x, lg, k, act, host_weights(w),
+                      what="decode limits T=%d H=%d I=%d E=%d k=%d act=%d" % (T, H, I, E, k, act))
+    layer.close()
