@@ -172,8 +172,7 @@ __device__ __forceinline__ void swiglu_codes_n(const float (&glo)[NR], const flo
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
     X[i] = block_exponent<F>(am[i]);
-    clo[i] = encode_element<F>(f32_bits(hlo[i]), X[i]);
-    chi[i] = encode_element<F>(f32_bits(hhi[i]), X[i]);
+    encode_pair<F>(hlo[i], hhi[i], X[i], clo[i], chi[i]);
   }
 }
 
