@@ -278,8 +278,10 @@ __device__ __forceinline__ void stage_store_n(const KArgs &p, const size_t (&pro
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int X = block_exponent<E4M3>(am[2 * i + b]);
-        d[32 * b] = (uint8_t)encode_element<E4M3>(f32_bits(t[i][2 * b]), X);
-        d[32 * b + 16] = (uint8_t)encode_element<E4M3>(f32_bits(t[i][2 * b + 1]), X);
+        uint32_t c0, c1;
+        encode_pair<E4M3>(t[i][2 * b], t[i][2 * b + 1], X, c0, c1);
+        d[32 * b] = (uint8_t)c0;
+        d[32 * b + 16] = (uint8_t)c1;
         sc[b] = (uint8_t)(X + 127);  // every lane writes the same byte
       }
     }
