@@ -359,7 +359,8 @@ hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, cons
 // E8M0 scales, once per token before dispatch).  One thread per 32-element
 // block: amax over the bit patterns, block exponent, RNE encode.
 // ---------------------------------------------------------------------------
-// 1x32 block b of the row-major bf16 matrix x.
+// 1x32 block b of the row-major bf16 matrix x (the element codes by the
+// scaled conversion instructions, encode_pair).
 template <class F>
 __device__ __forceinline__ void quant_block(const uint16_t *__restrict__ x, long b,
                                             uint8_t *__restrict__ codes,
@@ -385,10 +386,11 @@ __device__ __forceinline__ void quant_block(const uint16_t *__restrict__ x, long
     uint32_t out[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t c0 = encode_element<F>(w[2 * i] << 16, X);
-      const uint32_t c1 = encode_element<F>(w[2 * i] & 0xffff0000u, X);
-      const uint32_t c2 = encode_element<F>(w[2 * i + 1] << 16, X);
-      const uint32_t c3 = encode_element<F>(w[2 * i + 1] & 0xffff0000u, X);
+      uint32_t c0, c1, c2, c3;
+      encode_pair<F>(__uint_as_float(w[2 * i] << 16), __uint_as_float(w[2 * i] & 0xffff0000u), X,
+                     c0, c1);
+      encode_pair<F>(__uint_as_float(w[2 * i + 1] << 16),
+                     __uint_as_float(w[2 * i + 1] & 0xffff0000u), X, c2, c3);
       out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
     }
     uint4 *dst = reinterpret_cast<uint4 *>(codes + b * 32);
@@ -402,8 +404,8 @@ __device__ __forceinline__ void quant_block(const uint16_t *__restrict__ x, long
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         const uint32_t word = w[4 * i + h];
-        const uint32_t c0 = encode_element<F>(word << 16, X);
-        const uint32_t c1 = encode_element<F>(word & 0xffff0000u, X);
+        uint32_t c0, c1;
+        encode_pair<F>(__uint_as_float(word << 16), __uint_as_float(word & 0xffff0000u), X, c0, c1);
         d |= (c0 | (c1 << 4)) << (8 * h);
       }
       out[i] = d;
