@@ -695,44 +695,71 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return (c & 0x80u) ? -v : v;
 }
 
-template <int MODE>
+// Every slot's row piece is requested before the first is summed (the slot
+// count is a template argument, so the loads are straight-line code and all
+// of a thread's rows are in flight at once).
+template <int MODE, int K>
 __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ rows,
                                                       const int32_t *__restrict__ inv, long n8,
-                                                      int H, int top_k, long N,
-                                                      uint16_t *__restrict__ y) {
+                                                      int H, long N, uint16_t *__restrict__ y) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
   const long t = i / (H / 8);
   const int h = (int)(i % (H / 8)) * 8;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < top_k; ++j) {
-    const size_t p = (size_t)inv[t * top_k + j];
-    float v[8];
-    if (MODE == MOE_COMBINE_FP32) {
+  size_t p[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) p[j] = (size_t)inv[t * K + j];
+  float v[K][8];
+  if (MODE == MOE_COMBINE_FP32) {
+    float4 a[K], b[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
       const float4 *r = reinterpret_cast<const float4 *>(static_cast<const float *>(rows) +
-                                                         p * H + h);
-      const float4 a = r[0], b = r[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else if (MODE == MOE_COMBINE_BF16) {
-      const uint4 a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(rows) +
-                                                       p * H + h);
-      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[2 * k] = __uint_as_float(w[k] << 16);
-        v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-      }
-    } else {
-      const uint8_t *base = static_cast<const uint8_t *>(rows);
-      const uint2 a = *reinterpret_cast<const uint2 *>(base + p * H + h);
-      const int X = (int)base[(size_t)N * H + p * (H / 32) + h / 32] - 127;
-      const uint32_t w[2] = {a.x, a.y};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = ldexpf(e4m3_value((w[k / 4] >> (8 * (k % 4))) & 0xffu), X);
+                                                         p[j] * H + h);
+      a[j] = r[0];
+      b[j] = r[1];
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] += v[k];
+    for (int j = 0; j < K; ++j) {
+      v[j][0] = a[j].x; v[j][1] = a[j].y; v[j][2] = a[j].z; v[j][3] = a[j].w;
+      v[j][4] = b[j].x; v[j][5] = b[j].y; v[j][6] = b[j].z; v[j][7] = b[j].w;
+    }
+  } else if (MODE == MOE_COMBINE_BF16) {
+    uint4 a[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      a[j] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(rows) + p[j] * H + h);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const uint32_t w[4] = {a[j].x, a[j].y, a[j].z, a[j].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[j][2 * k] = __uint_as_float(w[k] << 16);
+        v[j][2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      }
+    }
+  } else {
+    const uint8_t *base = static_cast<const uint8_t *>(rows);
+    uint2 a[K];
+    int sx[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      a[j] = *reinterpret_cast<const uint2 *>(base + p[j] * H + h);
+      sx[j] = base[(size_t)N * H + p[j] * (H / 32) + h / 32];
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const uint32_t w[2] = {a[j].x, a[j].y};
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[j][k] = ldexpf(e4m3_value((w[k / 4] >> (8 * (k % 4))) & 0xffu), sx[j] - 127);
+    }
   }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += v[j][k];
   uint4 o;
   o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
   o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
@@ -741,26 +768,37 @@ __global__ __launch_bounds__(256) void combine_kernel(const void *__restrict__ r
   reinterpret_cast<uint4 *>(y)[i] = o;
 }
 
-hipError_t launch_combine(const void *rows, const int32_t *inv, int T, int H, int top_k,
-                          int combine, uint16_t *y, hipStream_t s) {
-  const long n8 = (long)T * H / 8;
-  if (n8 == 0) return hipSuccess;
+template <int MODE>
+hipError_t launch_combine_k(const void *rows, const int32_t *inv, long n8, int H, int top_k,
+                            long N, uint16_t *y, hipStream_t s) {
   const unsigned grid = (unsigned)((n8 + 255) / 256);
-  const long N = (long)T * top_k;
-  switch (combine) {
-    case MOE_COMBINE_FP32:
-      combine_kernel<MOE_COMBINE_FP32><<<grid, 256, 0, s>>>(rows, inv, n8, H, top_k, N, y);
-      break;
-    case MOE_COMBINE_BF16:
-      combine_kernel<MOE_COMBINE_BF16><<<grid, 256, 0, s>>>(rows, inv, n8, H, top_k, N, y);
-      break;
-    case MOE_COMBINE_FP8:
-      combine_kernel<MOE_COMBINE_FP8><<<grid, 256, 0, s>>>(rows, inv, n8, H, top_k, N, y);
-      break;
+  switch (top_k) {
+#define COMBINE_CASE(K) \
+    case K: combine_kernel<MODE, K><<<grid, 256, 0, s>>>(rows, inv, n8, H, N, y); break;
+    COMBINE_CASE(1) COMBINE_CASE(2) COMBINE_CASE(3) COMBINE_CASE(4)
+    COMBINE_CASE(5) COMBINE_CASE(6) COMBINE_CASE(7) COMBINE_CASE(8)
+#undef COMBINE_CASE
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const void *rows, const int32_t *inv, int T, int H, int top_k,
+                          int combine, uint16_t *y, hipStream_t s) {
+  const long n8 = (long)T * H / 8;
+  if (n8 == 0) return hipSuccess;
+  const long N = (long)T * top_k;
+  switch (combine) {
+    case MOE_COMBINE_FP32:
+      return launch_combine_k<MOE_COMBINE_FP32>(rows, inv, n8, H, top_k, N, y, s);
+    case MOE_COMBINE_BF16:
+      return launch_combine_k<MOE_COMBINE_BF16>(rows, inv, n8, H, top_k, N, y, s);
+    case MOE_COMBINE_FP8:
+      return launch_combine_k<MOE_COMBINE_FP8>(rows, inv, n8, H, top_k, N, y, s);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace moe
