@@ -266,7 +266,9 @@ moe_status moe_workspace_offsets(moe_layer_t layer, int T, int top_k, moe_act_dt
 /* Step 1 (aiter #6125 Changes: the top-k softmax kernel).  For each token the
  * top_k largest logits are taken, larger first, equal logits by lower expert
  * index; w[t][j] = exp(l_j - m) / sum over the picks of exp(l - m), which is
- * the softmax over all E renormalised over the picks.
+ * the softmax over all E renormalised over the picks.  Logits are finite or
+ * infinite; with a NaN logit in a row the picks of that row are unspecified
+ * (they are still distinct experts below E).
  *   logits [T][E] fp32 -> ids [T][top_k] int32, w [T][top_k] fp32. */
 moe_status moe_route(const float *logits, int T, int E, int top_k, int32_t *ids, float *w,
                      hipStream_t s);

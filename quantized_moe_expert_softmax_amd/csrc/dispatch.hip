@@ -19,29 +19,28 @@ namespace moe {
 // which equals the full softmax renormalised over the picks (the softmax
 // denominator over all E cancels).
 // ---------------------------------------------------------------------------
-// Lane l of a wave holds logits l, l + 64, ... of one token row.
+// Lane l of a wave holds logits l, l + 64, ... of one token row.  Positions
+// past E load logit E - 1 (route_values ignores them): every load is
+// unconditional, so all NV are in flight at once (a load under a per-lane
+// branch was waited for before the next one issued).
 template <int NV>
 __device__ __forceinline__ void load_logits(const float *__restrict__ row, int E, int lane,
                                             float v[NV]) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : 0.0f;
-  }
+  for (int i = 0; i < NV; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
 }
 
-// Selection key of logit v of expert e: the larger logit, then the lower
-// index, is the larger key.  The float's bits are mapped to an unsigned
-// order (negative values flipped whole, positive ones above them), -0 is
-// taken as +0 (a strict logit compare treats them as equal), and the index
-// is stored inverted below them.
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
+// Selection key of a logit: its float bits mapped to an unsigned order
+// (negative values flipped whole, positive ones above them), with -0 taken
+// as +0 (a strict logit compare treats them as equal).  Keys of real logits
+// are at least 1 (only one NaN pattern maps to 0, raised to 1), so 0 marks
+// an expert that is taken or past E.
+__device__ __forceinline__ uint32_t route_key(float v) {
   const uint32_t u = __float_as_uint(v + 0.0f);  // -0 + 0 = +0
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
+  return o > 1u ? o : 1u;
 }
-__device__ __forceinline__ float route_key_value(uint64_t k) {
-  const uint32_t o = (uint32_t)(k >> 32);
+__device__ __forceinline__ float route_key_value(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
@@ -49,18 +48,12 @@ __device__ __forceinline__ float route_key_value(uint64_t k) {
 // DPP within each 16-lane row (quad_perm [1,0,3,2], [2,3,0,1],
 // row_half_mirror, row_mirror: every lane then holds its row's largest
 // key), then v_permlane16_swap (rows 0 with 1, 2 with 3) and
-// v_permlane32_swap (the two halves).  The __shfl_xor butterfly this
-// replaces was a chain of dependent ds_bpermute round trips through LDS,
-// about 0.6 us per pick: 3.7 of the 5 us a one-token route took.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
-  auto pack = [](uint32_t hi, uint32_t lo) __attribute__((always_inline)) {
-    return ((uint64_t)hi << 32) | lo;
-  };
+// v_permlane32_swap (the two halves).  (A __shfl_xor butterfly is a chain of
+// dependent ds_bpermute round trips through LDS, about 0.6 us per pick.)
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t key) {
   auto dpp_step = [&](auto ctrl) __attribute__((always_inline)) {
     constexpr int C = decltype(ctrl)::value;
-    const uint64_t o =
-        pack((uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(key >> 32), C, 0xF, 0xF, false),
-             (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)key, C, 0xF, 0xF, false));
+    const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)key, C, 0xF, 0xF, false);
     key = o > key ? o : key;
   };
   dpp_step(std::integral_constant<int, 0xB1>{});
@@ -68,49 +61,53 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
   dpp_step(std::integral_constant<int, 0x141>{});
   dpp_step(std::integral_constant<int, 0x140>{});
   {
-    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)key, (uint32_t)key, false, false);
-    const auto hi =
-        __builtin_amdgcn_permlane16_swap((uint32_t)(key >> 32), (uint32_t)(key >> 32), false, false);
-    const uint64_t a = pack(hi[0], lo[0]), b = pack(hi[1], lo[1]);
-    key = a > b ? a : b;
+    const auto r = __builtin_amdgcn_permlane16_swap(key, key, false, false);
+    key = r[0] > r[1] ? r[0] : r[1];
   }
   {
-    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)key, (uint32_t)key, false, false);
-    const auto hi =
-        __builtin_amdgcn_permlane32_swap((uint32_t)(key >> 32), (uint32_t)(key >> 32), false, false);
-    const uint64_t a = pack(hi[0], lo[0]), b = pack(hi[1], lo[1]);
-    key = a > b ? a : b;
+    const auto r = __builtin_amdgcn_permlane32_swap(key, key, false, false);
+    key = r[0] > r[1] ? r[0] : r[1];
   }
   return key;
 }
 
 // One wave routes the token whose logits it holds (load_logits); lanes <
-// top_k write ids[j], w[j].  The whole wave must be active.
+// top_k write ids[j], w[j].  The whole wave must be active.  A pick is the
+// wave's largest 32-bit key M; of the experts holding M the lowest index
+// wins: the first register position i (ascending) at which any lane holds
+// M, then the lowest such lane (expert lane + 64 i), both read from ballots.
 template <int NV>
 __device__ __forceinline__ void route_values(const float v[NV], int E, int top_k, int lane,
                                              int32_t *__restrict__ ids, float *__restrict__ wts) {
-  uint32_t taken = 0;
+  uint32_t key[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) key[i] = lane + 64 * i < E ? route_key(v[i]) : 0u;
   float sel0 = 0.0f, mine = 0.0f;  // the largest logit; lane j: pick j's logit
   int myid = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j < top_k) {
-      uint64_t best = 0;  // below every valid key
+      uint32_t m = key[0];
+#pragma unroll
+      for (int i = 1; i < NV; ++i) m = key[i] > m ? key[i] : m;
+      const uint32_t M = __builtin_amdgcn_readfirstlane(wave_max_key(m));
+      int wl = -1, wi = 0;  // winning lane and register position
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && !((taken >> i) & 1u)) {
-          const uint64_t k = route_key(v[i], e);
-          best = k > best ? k : best;
+        const uint64_t b = __ballot(key[i] == M);
+        if (wl < 0 && b != 0) {
+          wl = __builtin_ctzll(b);
+          wi = i;
         }
       }
-      best = wave_max_key(best);
-      const int bi = (int)~(uint32_t)best;
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (j == 0) sel0 = route_key_value(best);
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (i == wi && lane == wl) key[i] = 0u;
+      const float val = route_key_value(M);
+      if (j == 0) sel0 = val;
       if (j == lane) {
-        mine = route_key_value(best);
-        myid = bi;
+        mine = val;
+        myid = wl + 64 * wi;
       }
     }
   }
