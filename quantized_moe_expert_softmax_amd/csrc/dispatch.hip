@@ -180,18 +180,24 @@ hipError_t launch_route(const float *logits, int T, int E, int top_k, int32_t *i
 //            so the order within an expert is ascending token, i.e.
 //            ascending a (a token's top_k experts are distinct).
 // ---------------------------------------------------------------------------
+// The slot count K is a template argument: a token's K ids are loaded
+// together (from a clamped token row, so the loads are unconditional) before
+// the first is used.
+template <int K>
 __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t *__restrict__ ids, int T,
-                                                        int E, int top_k,
-                                                        int32_t *__restrict__ hist) {
+                                                        int E, int32_t *__restrict__ hist) {
   extern __shared__ int32_t lhist[];
   for (int e = threadIdx.x; e < E; e += 256) lhist[e] = 0;
-  __syncthreads();
   const long t = (long)blockIdx.x * kSortBlock + threadIdx.x;
+  const long tc = t < T ? t : (long)T - 1;
+  uint32_t id[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) id[j] = (uint32_t)ids[tc * K + j];
+  __syncthreads();
   if (t < T) {
-    for (int j = 0; j < top_k; ++j) {
-      const uint32_t e = (uint32_t)ids[t * top_k + j];
-      if (e < (uint32_t)E) atomicAdd(&lhist[e], 1);
-    }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (id[j] < (uint32_t)E) atomicAdd(&lhist[id[j]], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) hist[(long)blockIdx.x * E + e] = lhist[e];
@@ -292,8 +298,9 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t *__restrict__ h
   }
 }
 
+template <int K>
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__restrict__ ids, int T,
-                                                           int E, int top_k,
+                                                           int E,
                                                            const int32_t *__restrict__ base,
                                                            const int32_t *__restrict__ offsets,
                                                            int32_t *__restrict__ perm,
@@ -302,34 +309,58 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t *__rest
                                                            float *__restrict__ wsorted) {
   extern __shared__ unsigned long long masks[];  // [4 waves][E]
   for (int i = threadIdx.x; i < 4 * E; i += 256) masks[i] = 0ull;
-  __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long t = (long)blockIdx.x * kSortBlock + threadIdx.x;
+  const long tc = t < T ? t : (long)T - 1;
   const unsigned long long bit = 1ull << lane;
-  if (t < T) {
-    for (int j = 0; j < top_k; ++j) {
-      const uint32_t e = (uint32_t)ids[t * top_k + j];
-      if (e < (uint32_t)E) atomicOr(&masks[wave * E + e], bit);
-    }
+  uint32_t id[K];
+  float wt[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    id[j] = (uint32_t)ids[tc * K + j];
+    wt[j] = wsorted ? w[tc * K + j] : 0.0f;
   }
   __syncthreads();
   if (t < T) {
-    for (int j = 0; j < top_k; ++j) {
-      const uint32_t e = (uint32_t)ids[t * top_k + j];
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (id[j] < (uint32_t)E) atomicOr(&masks[wave * E + id[j]], bit);
+  }
+  // each slot's expert start row (all loads issued before the first use;
+  // ids past E read expert 0's and are skipped below)
+  int32_t start[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const uint32_t e = id[j] < (uint32_t)E ? id[j] : 0u;
+    start[j] = offsets[e] + base[(long)blockIdx.x * E + e];
+  }
+  __syncthreads();
+  if (t < T) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const uint32_t e = id[j];
       if (e >= (uint32_t)E) continue;
       int r = __popcll(masks[wave * E + e] & (bit - 1ull));
-      for (int w = 0; w < wave; ++w) r += __popcll(masks[w * E + e]);
-      const int32_t pos = offsets[e] + base[(long)blockIdx.x * E + e] + r;
-      perm[pos] = (int32_t)(t * top_k + j);
-      inv[t * top_k + j] = pos;
-      if (wsorted) wsorted[pos] = w[t * top_k + j];
+      for (int v = 0; v < wave; ++v) r += __popcll(masks[v * E + e]);
+      const int32_t pos = start[j] + r;
+      perm[pos] = (int32_t)(t * K + j);
+      inv[t * K + j] = pos;
+      if (wsorted) wsorted[pos] = wt[j];
     }
   }
 }
 
 hipError_t launch_sort_hist(const int32_t *ids, int T, int E, int top_k, int32_t *hist, int nb,
                             hipStream_t s) {
-  sort_hist_kernel<<<nb, 256, (size_t)E * 4, s>>>(ids, T, E, top_k, hist);
+  switch (top_k) {
+#define HIST_CASE(K) \
+    case K: sort_hist_kernel<K><<<nb, 256, (size_t)E * 4, s>>>(ids, T, E, hist); break;
+    HIST_CASE(1) HIST_CASE(2) HIST_CASE(3) HIST_CASE(4)
+    HIST_CASE(5) HIST_CASE(6) HIST_CASE(7) HIST_CASE(8)
+#undef HIST_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -345,8 +376,18 @@ hipError_t launch_sort_scatter(const int32_t *ids, int T, int E, int top_k, cons
                                const int32_t *offsets, int32_t *perm, int32_t *inv,
                                const float *w, float *wsorted, hipStream_t s) {
   const int nb = ceil_div(T, kSortBlock);
-  sort_scatter_kernel<<<nb, 256, (size_t)E * 4 * 8, s>>>(ids, T, E, top_k, hist, offsets, perm,
-                                                         inv, w, wsorted);
+  switch (top_k) {
+#define SCATTER_CASE(K)                                                                  \
+    case K:                                                                              \
+      sort_scatter_kernel<K><<<nb, 256, (size_t)E * 4 * 8, s>>>(ids, T, E, hist, offsets, \
+                                                                perm, inv, w, wsorted);  \
+      break;
+    SCATTER_CASE(1) SCATTER_CASE(2) SCATTER_CASE(3) SCATTER_CASE(4)
+    SCATTER_CASE(5) SCATTER_CASE(6) SCATTER_CASE(7) SCATTER_CASE(8)
+#undef SCATTER_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
