@@ -42,6 +42,37 @@ def test_route_ties(moe):
     assert ulp_diff(host(w), rw).max() <= ROUTE_ULP_TOL
 
 
+def test_route_signed_zero_ties(moe):
+    # -0 and +0 compare equal: equal logits go by the lower expert index
+    lg = np.full((2, 130), -1.0, np.float32)
+    lg[0, [5, 3, 1]] = [-0.0, 0.0, -0.0]
+    lg[1, [129, 64, 0]] = [0.0, -0.0, 0.0]
+    ids, w = moe.moe_route(dev(lg), 3)
+    rid, rw = oracle.route(lg, 3)
+    assert np.array_equal(host(ids), rid)
+    assert host(ids)[0].tolist() == [1, 3, 5] and host(ids)[1].tolist() == [0, 64, 129]
+    assert ulp_diff(host(w), rw).max() <= ROUTE_ULP_TOL
+
+
+def test_route_nan_rows_pick_valid_experts(moe):
+    # NaN logits are outside the contract (the picks of such a row are
+    # unspecified), but the ids stay distinct experts below E
+    E, k = 200, 8
+    lg = np.random.default_rng(11).standard_normal((6, E)).astype(np.float32)
+    bits = lg.view(np.uint32)
+    bits[0, :] = 0xFFFFFFFF
+    bits[1, ::3] = 0x7FC00000
+    bits[2, 190:] = 0xFFFFFFFF
+    bits[3, :8] = 0xFFC00001
+    bits[4, 100] = 0x7F800001
+    ids = host(moe.moe_route(dev(lg), k)[0])
+    assert ids.min() >= 0 and ids.max() < E
+    assert all(len(set(r.tolist())) == k for r in ids)
+    # the rows without NaN still match the oracle
+    rid, _ = oracle.route(lg[5:], k)
+    assert np.array_equal(ids[5:], rid)
+
+
 SORT_CASES = [(1, 8, 2), (16, 8, 2), (255, 384, 6), (256, 384, 6), (257, 384, 6), (4096, 384, 6),
               (8192, 128, 3), (32768, 384, 6), (100, 1024, 8), (3, 1, 1)]
 
