@@ -191,7 +191,8 @@ struct PcShape {
   // that four weight stages still fit
   static constexpr int NA = A_BYTES > 20 * 1024 ? 3 : kPcActStages;
   static constexpr int GRP_BASE = NA * A_STAGE;
-  static constexpr int NB_FIT = (160 * 1024 - NA * A_STAGE - NGRP * GRP) / B_STAGE;
+  // (the 16 bytes after the rings hold the work-distribution slots)
+  static constexpr int NB_FIT = (160 * 1024 - 16 - NA * A_STAGE - NGRP * GRP) / B_STAGE;
   static constexpr int NB = NB_FIT < kPcWStages ? NB_FIT : kPcWStages;
   static constexpr int B_BASE = GRP_BASE + NGRP * GRP;
   static constexpr int LDS = B_BASE + NB * B_STAGE;
